@@ -1,0 +1,13 @@
+"""fp64 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.  The HIP product path never imports, links or
+runs anything here, and nothing here imports the HIP path.
+"""
+from .babai_oracle import (babai_bound, babai_gram_schmidt, certificate,
+                           cholesky_lower, colspacing_steps,
+                           column_entropy_bits, cvp_box, cvp_enumerate,
+                           expand_group_steps, fix_dead_and_damp,
+                           gamma_ratio, gptq_obs_sweep, grid_steps, hessian,
+                           nearest_plane_sweep, nearest_plane_sweep_blocked,
+                           order_permutation, proxy_loss, quant_layer)
