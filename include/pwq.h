@@ -1,0 +1,219 @@
+/*
+ * pwq.h -- C ABI of libpwq: Hessian-weighted sequential quantization of one
+ * linear layer on an MI355X (gfx950), read as Babai's nearest-plane algorithm.
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [GEOM] "The Geometry of LLM Quantization: GPTQ as Babai's Nearest Plane
+ *          Algorithm", technical summary 1 (problem), 2.1 (closest-vector
+ *          form, basis X diag(s), Theorem 1), 2.2 (back-to-front GPTQ =
+ *          Babai, Theorem 4), 2.3 (no clipping, Theorem 5, pivot order).
+ *   [WSIC] "WaterSIC: information-theoretically (near) optimal linear layer
+ *          quantization", technical summary 1 (objective) and 2 (Cholesky
+ *          Sigma = L L^T, last column first with interference cancellation,
+ *          spacing alpha_i = c/|l_ii|, dead-feature erasure).
+ *   [OAEM] "Initialisation Determines the Basin: Efficient Codebook
+ *          Optimisation for Extreme LLM Quantization", section 3 (damped
+ *          Hessian X^T X + lambda I).
+ *
+ * Conventions for every entry point
+ *   - Matrices are row-major.  W is m x n (d_out x d_in), row stride ldw
+ *     elements.  X is n x ntok (channels x tokens, tokens contiguous), row
+ *     stride ldx elements.  H and L are n x n with row stride n.
+ *   - Every pointer except `grid` and the returned strings is a DEVICE
+ *     pointer owned by the caller.  The library allocates nothing: scratch
+ *     memory is the caller's workspace `ws` of `ws_bytes` bytes (ask the
+ *     matching *_workspace_size function), 256-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.
+ *   - Argument errors are reported synchronously, before anything is
+ *     enqueued, as a pwq_status (details: pwq_last_error()).  A numerical
+ *     failure on the device (Cholesky of a matrix that is not positive
+ *     definite) is written to result->info, LAPACK-potrf style: 0 = success,
+ *     k > 0 = the leading minor of order k is not positive definite; the
+ *     codes, steps and losses are then undefined.  NaN/Inf pivots also
+ *     report info = k.
+ *   - Same inputs and arguments give bitwise-identical outputs (no float
+ *     atomics; every reduction has a fixed order).
+ *   - Calls with distinct workspaces may run concurrently on distinct streams.
+ */
+#ifndef PWQ_H
+#define PWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PWQ_OK = 0,
+  PWQ_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum or combination      */
+  PWQ_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  PWQ_ERR_WORKSPACE = 3,     /* ws NULL, misaligned or smaller than needed  */
+  PWQ_ERR_HIP = 4            /* a HIP runtime call failed                   */
+} pwq_status;
+
+/* Element types of W and X (PWQ_F32/PWQ_BF16) and the precision of the
+ * factor / running target / sweep (PWQ_F32 or PWQ_F64). */
+typedef enum { PWQ_F32 = 0, PWQ_BF16 = 1, PWQ_F64 = 2 } pwq_dtype;
+
+/* Quantization grid.  The lattice of one row is s * Z per column (no
+ * clipping: codes are any int32) [GEOM 2.1, 2.3].
+ *   SYM        : s = max|w| / (2^(bits-1) - 1) over each group of
+ *                `group_size` consecutive columns of a row (0 = whole row);
+ *                stored code = lattice integer.
+ *   ASYM       : lo = min(min w, 0), hi = max(max w, 0),
+ *                s = (hi - lo) / (2^bits - 1), zero point z0 = rint(-lo/s);
+ *                stored code = lattice integer + z0.
+ *   COLSPACING : one spacing per column, alpha_k = c / l_kk of the Cholesky
+ *                factor [WSIC 2]; stored code = lattice integer.
+ * Steps are taken from W (after dead-feature erasure) before the sweep; a
+ * zero step becomes 1.  bits in [2, 16] for SYM/ASYM; c > 0 for COLSPACING. */
+typedef enum { PWQ_GRID_SYM = 0, PWQ_GRID_ASYM = 1, PWQ_GRID_COLSPACING = 2 } pwq_grid_kind;
+typedef struct {
+  int32_t kind;        /* pwq_grid_kind                                  */
+  int32_t bits;
+  int32_t group_size;  /* 0 = one step per row; must divide n otherwise  */
+  int32_t reserved;
+  double c;            /* COLSPACING constant                            */
+} pwq_grid;
+
+/* Processing order.  Position k of the permuted problem holds original
+ * column perm[k]; positions are processed from n-1 down to 0 [GEOM 2.2].
+ *   BACK_TO_FRONT : perm = identity (Babai's natural order)
+ *   FRONT_TO_BACK : perm = reversal (standard GPTQ order)
+ *   PERM          : caller's device int32 permutation of 0..n-1
+ *   ACT_ORDER     : largest diag(H) processed first, ties by lower index
+ *                   [GEOM 2.3] */
+typedef enum {
+  PWQ_ORDER_BACK_TO_FRONT = 0,
+  PWQ_ORDER_FRONT_TO_BACK = 1,
+  PWQ_ORDER_PERM = 2,
+  PWQ_ORDER_ACT = 3
+} pwq_order_kind;
+
+/* Device-resident result record (read after a stream synchronisation).
+ *   loss        = tr((W - W^) H (W - W^)^T), undamped H [WSIC 1]
+ *   loss_damped = the same with H + lambda I; equals sum rho^2 s^2 l_kk^2
+ *   bound       = (1/4) sum s^2 l_kk^2, Theorem 5 of [GEOM 2.3]
+ *   delta_sq    = ||W - W^||_F^2
+ *   lambda      = damp * mean(diag H) after dead-feature erasure [OAEM 3]
+ *   info        = 0, or the order of the failing leading minor
+ *   ndead       = number of zero-variance inputs erased [WSIC 2]        */
+typedef struct {
+  double loss;
+  double loss_damped;
+  double bound;
+  double delta_sq;
+  double lambda;
+  int32_t info;
+  int32_t ndead;
+  int32_t reserved[2];
+} pwq_result;
+
+/* Human-readable name of a status. Never NULL. */
+const char* pwq_status_string(pwq_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* pwq_last_error(void);
+
+/* ---------------------------------------------------------------------- *
+ * Stage 1: H (+)= 2 X X^T  [GEOM 2.1: the lattice comes from the
+ * calibration inputs; WSIC 1: output error of Y = W X].
+ *   H        : n x n float32, full symmetric result (both triangles
+ *              written; with accumulate != 0 the previous H is added).
+ *   X        : n x ntok, xdtype PWQ_BF16 or PWQ_F32, row stride ldx >= ntok.
+ *   Products are exact in fp32 for bf16 inputs; accumulation is fp32 in a
+ *   fixed order.  Calling it once per calibration chunk with accumulate = 1
+ *   streams the Hessian over any number of tokens.
+ * ---------------------------------------------------------------------- */
+size_t pwq_hessian_workspace_size(int64_t n, int64_t ntok);
+pwq_status pwq_hessian_accum(float* H, int64_t n, const void* X, int32_t xdtype,
+                             int64_t ntok, int64_t ldx, int32_t accumulate,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- *
+ * Stage 2+3: dead features, damping, Cholesky [WSIC 2; OAEM 3; GEOM 2.1].
+ *   H      : n x n float32 (lower triangle read).
+ *   L      : n x n output in precision `prec` (PWQ_F32 -> float,
+ *            PWQ_F64 -> double): lower factor of H_d = H' + lambda I where
+ *            H' is H with H_kk = 1 for every k with H_kk == 0; the strict
+ *            upper triangle is written with zeros.
+ *   dead   : optional int32 [n] output, 1 where H_kk == 0 (erased input).
+ *   result : lambda, ndead and info are written (losses are not).
+ * ---------------------------------------------------------------------- */
+size_t pwq_cholesky_workspace_size(int64_t n, int32_t prec);
+pwq_status pwq_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec,
+                             void* L, int32_t* dead, pwq_result* result,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- *
+ * Steps for SYM / ASYM grids from W [GEOM 2.1: fixed basis X diag(s)].
+ *   scales : m x (n / G) float32 (G = group_size, or n when 0)
+ *   zeros  : m x (n / G) int32 for ASYM, ignored (may be NULL) otherwise.
+ *   dead   : optional int32 [n]; flagged columns count as zero weights.
+ * ---------------------------------------------------------------------- */
+pwq_status pwq_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                          int64_t ldw, const int32_t* dead, const pwq_grid* grid,
+                          float* scales, int32_t* zeros, void* stream);
+
+/* ---------------------------------------------------------------------- *
+ * Stage 4: the back-to-front nearest-plane sweep with lazy block updates,
+ * given a factor [GEOM 2.2, Theorem 4; WSIC 2].  Columns are processed in
+ * natural order (n-1 first).  For column k, with running target
+ * w~_k = w_k + sum_{j>k} (l_jk / l_kk) e_j:
+ *     z = rint(w~_k / s)  (half to even),  e_k = w_k - s z,
+ * where e is the ORIGINAL weight minus the dequantized weight.
+ *   W      : m x n (wdtype), L : n x n lower in `prec` (as written by
+ *            pwq_damp_cholesky).  dead: optional int32 [n] flags; columns
+ *            flagged non-zero are treated as zero weights.
+ *   scales : SYM/ASYM: input, as written by pwq_grid_steps.
+ *            COLSPACING: output, float32 [n], alpha_k = c / l_kk.
+ *   zeros  : ASYM input zero points (added to the stored codes).
+ *   codes  : m x n int32 output (row stride n).
+ *   result : loss_damped, bound, delta_sq written; loss = loss_damped -
+ *            lambda * delta_sq uses result->lambda as found on entry.
+ *   block  : lazy-update block size, one of 32, 64, 128, 256.
+ * ---------------------------------------------------------------------- */
+size_t pwq_sweep_workspace_size(int64_t m, int64_t n, int32_t block, int32_t prec);
+pwq_status pwq_babai_sweep(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                           int64_t ldw, const void* L, int32_t prec,
+                           const int32_t* dead, const pwq_grid* grid,
+                           float* scales, const int32_t* zeros, int32_t block,
+                           int32_t* codes, pwq_result* result,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- *
+ * The whole layer: quant_layer(W, X or H, grid, order, damp) ->
+ * codes + steps + proxy loss [GEOM 1, 2.1-2.3; WSIC 1-2; OAEM 3].
+ *   Exactly one of X (n x ntok, xdtype) and H (n x n float32) is non-NULL.
+ *   order_kind : pwq_order_kind; perm (device int32 [n]) only for PERM.
+ *   damp       : lambda = damp * mean(diag H) (0 for none).
+ *   block      : 32, 64, 128 or 256.   prec : PWQ_F32 or PWQ_F64.
+ *   codes      : m x n int32 in ORIGINAL column order (row stride n).
+ *   scales     : SYM/ASYM m x (n/G) float32; COLSPACING [n] float32 per
+ *                original column.
+ *   zeros      : m x (n/G) int32 for ASYM, else ignored.
+ *   result     : every field written.
+ *   H_out      : optional n x n float32 copy of H = 2 X X^T (X given only).
+ *   L_out      : optional n x n factor (precision prec) of the PERMUTED
+ *                damped Hessian.
+ * ---------------------------------------------------------------------- */
+size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok,
+                                      int32_t has_x, int32_t order_kind,
+                                      int32_t block, int32_t prec);
+pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                           int64_t ldw, const void* X, int32_t xdtype,
+                           int64_t ntok, int64_t ldx, const float* H,
+                           const pwq_grid* grid, int32_t order_kind,
+                           const int32_t* perm, float damp, int32_t block,
+                           int32_t prec, int32_t* codes, float* scales,
+                           int32_t* zeros, pwq_result* result, float* H_out,
+                           void* L_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PWQ_H */

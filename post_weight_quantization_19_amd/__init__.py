@@ -1,0 +1,197 @@
+"""MI355X-native Hessian-weighted sequential layer quantization.
+
+GPTQ read as Babai's nearest-plane algorithm ("The Geometry of LLM
+Quantization: GPTQ as Babai's Nearest Plane Algorithm", technical summary
+2.1-2.3) and its successive-interference-cancellation form with per-column
+spacing ("WaterSIC: information-theoretically (near) optimal linear layer
+quantization", technical summary 2), behind the C ABI of ``libpwq.so``
+(``include/pwq.h``).  These wrappers only marshal torch tensors (device
+memory) and the current stream into that ABI; the HIP kernels do all the
+work and there is no CPU fallback.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PwqError, check, lib, make_grid, parse_result
+
+__all__ = ["Grid", "hessian_accum", "damp_cholesky", "grid_steps", "babai_sweep",
+           "quant_layer", "read_result", "PwqError"]
+
+
+@dataclass(frozen=True)
+class Grid:
+    kind: str = "sym"       # "sym" | "asym" | "colspacing"
+    bits: int = 4
+    group: int = 0          # 0 = one step per row
+    c: float = 0.0          # colspacing constant (alpha_k = c / l_kk)
+
+    def c_struct(self):
+        return make_grid(self.kind, self.bits, self.group, self.c)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream or None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.PWQ_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.PWQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _prec(prec: str) -> int:
+    return {"f32": _lib.PWQ_F32, "f64": _lib.PWQ_F64}[prec]
+
+
+def _tdt(prec: str):
+    return torch.float64 if prec == "f64" else torch.float32
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def _row_major(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def new_result(device) -> torch.Tensor:
+    return torch.zeros(_lib.RESULT_BYTES, dtype=torch.uint8, device=device)
+
+
+def read_result(res: torch.Tensor) -> dict:
+    """Synchronising read of a device result record."""
+    return parse_result(bytes(res.cpu().numpy().tobytes()))
+
+
+def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None,
+                  accumulate: bool = False) -> torch.Tensor:
+    """H (+)= 2 X X^T for X [n, ntok] (bf16 or fp32)."""
+    _require_cuda(X, H)
+    n, ntok = X.shape
+    ldx = _row_major(X)
+    if H is None:
+        H = torch.empty((n, n), dtype=torch.float32, device=X.device)
+    L = lib()
+    wsb = L.pwq_hessian_workspace_size(n, ntok)
+    ws = _workspace(wsb, X.device)
+    check(L.pwq_hessian_accum(H.data_ptr(), n, X.data_ptr(), _dtype_code(X), ntok, ldx,
+                              int(accumulate), ws.data_ptr(), ws.numel(), _stream()))
+    return H
+
+
+def damp_cholesky(H: torch.Tensor, damp: float = 0.01, prec: str = "f32"):
+    """(L, dead, result) for H_d = H' + lambda I (lower factor)."""
+    _require_cuda(H)
+    n = H.shape[0]
+    L_ = lib()
+    Lt = torch.empty((n, n), dtype=_tdt(prec), device=H.device)
+    dead = torch.empty(n, dtype=torch.int32, device=H.device)
+    res = new_result(H.device)
+    ws = _workspace(L_.pwq_cholesky_workspace_size(n, _prec(prec)), H.device)
+    check(L_.pwq_damp_cholesky(H.data_ptr(), n, float(damp), _prec(prec), Lt.data_ptr(),
+                               dead.data_ptr(), res.data_ptr(), ws.data_ptr(), ws.numel(),
+                               _stream()))
+    return Lt, dead, res
+
+
+def grid_steps(W: torch.Tensor, grid: Grid, dead: Optional[torch.Tensor] = None):
+    """(scales [m, n/G], zeros [m, n/G] or None) for SYM / ASYM grids."""
+    _require_cuda(W, dead)
+    m, n = W.shape
+    G = grid.group or n
+    scales = torch.empty((m, n // G), dtype=torch.float32, device=W.device)
+    zeros = (torch.empty((m, n // G), dtype=torch.int32, device=W.device)
+             if grid.kind == "asym" else None)
+    g = grid.c_struct()
+    check(lib().pwq_grid_steps(W.data_ptr(), _dtype_code(W), m, n, _row_major(W), _ptr(dead),
+                               g, scales.data_ptr(), _ptr(zeros), _stream()))
+    return scales, zeros
+
+
+def babai_sweep(W: torch.Tensor, L: torch.Tensor, grid: Grid, scales=None, zeros=None,
+                dead=None, block: int = 128, result: Optional[torch.Tensor] = None):
+    """Nearest-plane sweep given a factor L (natural order).  Returns
+    (codes, scales, result)."""
+    _require_cuda(W, L)
+    m, n = W.shape
+    prec = "f64" if L.dtype == torch.float64 else "f32"
+    if grid.kind == "colspacing":
+        scales = torch.empty(n, dtype=torch.float32, device=W.device)
+    elif scales is None:
+        raise ValueError("SYM/ASYM sweeps need scales (see grid_steps)")
+    codes = torch.empty((m, n), dtype=torch.int32, device=W.device)
+    res = new_result(W.device) if result is None else result
+    L_ = lib()
+    ws = _workspace(L_.pwq_sweep_workspace_size(m, n, block, _prec(prec)), W.device)
+    g = grid.c_struct()
+    check(L_.pwq_babai_sweep(W.data_ptr(), _dtype_code(W), m, n, _row_major(W), L.data_ptr(),
+                             _prec(prec), _ptr(dead), g, scales.data_ptr(), _ptr(zeros),
+                             block, codes.data_ptr(), res.data_ptr(), ws.data_ptr(),
+                             ws.numel(), _stream()))
+    return codes, scales, res
+
+
+def workspace_for_layer(m, n, ntok, has_x, order, block, prec, device) -> torch.Tensor:
+    nb = lib().pwq_quant_layer_workspace_size(m, n, ntok, int(has_x), _lib.ORDERS[order],
+                                             block, _prec(prec))
+    return _workspace(nb, device)
+
+
+def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
+                H: Optional[torch.Tensor] = None, grid: Grid = Grid(),
+                order: str = "back_to_front", perm: Optional[torch.Tensor] = None,
+                damp: float = 0.01, block: int = 128, prec: str = "f32",
+                want_H: bool = False, want_L: bool = False,
+                workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+    """quant_layer(W, X or H, grid, order, damp) -> dict(codes, scales, zeros,
+    result[, H, L]).  ``out`` may pass preallocated outputs (same keys)."""
+    _require_cuda(W, X, H, perm)
+    m, n = W.shape
+    dev = W.device
+    ntok, ldx = (X.shape[1], _row_major(X)) if X is not None else (0, 0)
+    G = n if grid.kind == "colspacing" else (grid.group or n)
+    o = dict(out or {})
+    if "codes" not in o:
+        o["codes"] = torch.empty((m, n), dtype=torch.int32, device=dev)
+    if "scales" not in o:
+        o["scales"] = (torch.empty(n, dtype=torch.float32, device=dev)
+                       if grid.kind == "colspacing"
+                       else torch.empty((m, n // G), dtype=torch.float32, device=dev))
+    if "zeros" not in o:
+        o["zeros"] = (torch.empty((m, n // G), dtype=torch.int32, device=dev)
+                      if grid.kind == "asym" else None)
+    if "result" not in o:
+        o["result"] = new_result(dev)
+    if want_H and X is not None and o.get("H") is None:
+        o["H"] = torch.empty((n, n), dtype=torch.float32, device=dev)
+    if want_L and o.get("L") is None:
+        o["L"] = torch.empty((n, n), dtype=_tdt(prec), device=dev)
+    ws = workspace if workspace is not None else workspace_for_layer(
+        m, n, ntok, X is not None, order, block, prec, dev)
+    g = grid.c_struct()
+    check(lib().pwq_quant_layer(
+        W.data_ptr(), _dtype_code(W), m, n, _row_major(W),
+        _ptr(X), _dtype_code(X) if X is not None else 0, ntok, ldx, _ptr(H), g,
+        _lib.ORDERS[order], _ptr(perm), float(damp), int(block), _prec(prec),
+        o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o["zeros"]),
+        o["result"].data_ptr(), _ptr(o.get("H")), _ptr(o.get("L")), ws.data_ptr(),
+        ws.numel(), _stream()))
+    return o

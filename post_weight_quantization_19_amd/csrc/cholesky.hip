@@ -1,0 +1,301 @@
+// Dead features, damping and the Cholesky factor of the damped Hessian.
+//
+// "WaterSIC: ...", technical summary 2: factor Sigma = L L^T (L lower) and
+// erase inputs of (near) zero variance; "Initialisation Determines the
+// Basin ...", section 3: the damped Hessian H + lambda I; "The Geometry of
+// LLM Quantization ...", technical summary 2.1, Theorem 1: any factor of the
+// Hessian gives the same closest-vector instance, so the square Cholesky
+// factor replaces the tall input matrix.
+//
+// Design (gfx950): right-looking blocked Cholesky with 64-column panels, in
+// place on an n x n working copy (float or double).  Per panel:
+//   chol_diag     one workgroup factors the 64x64 diagonal block in LDS
+//   chol_panel    one thread per row solves L_ik = A_ik L_kk^-T by forward
+//                 substitution (L_kk broadcast from LDS)
+//   chol_trailing the trailing lower triangle A_ij -= L_ik L_jk^T as 128x128
+//                 MFMA tiles (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64);
+//                 both operands are panel rows, contiguous along K.
+// A non-positive or non-finite pivot stops the factorization and records the
+// LAPACK-style order of the failing minor; every later kernel sees the flag
+// and returns at once.
+#include "pwq_device.h"
+#include "pwq_internal.h"
+
+namespace pwq {
+
+namespace {
+
+constexpr int NB = 64;   // panel width
+
+// lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;
+// fixed-order fp64 reduction.
+__global__ __launch_bounds__(256) void damp_prep(const float* __restrict__ H,
+                                                 int n, float damp,
+                                                 int32_t* __restrict__ dead,
+                                                 pwq_result* __restrict__ res,
+                                                 DevFlags* flags,
+                                                 double* __restrict__ lam_out) {
+  __shared__ double ssum[256];
+  __shared__ int scnt[256];
+  double s = 0.0;
+  int cnt = 0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float h = H[(int64_t)i * n + i];
+    const int d = h == 0.0f;
+    if (dead) dead[i] = d;
+    cnt += d;
+    s += d ? 1.0 : (double)h;
+  }
+  ssum[threadIdx.x] = s;
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + o];
+      scnt[threadIdx.x] += scnt[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double lam = (double)damp * (ssum[0] / (double)n);
+    *lam_out = lam;
+    res->lambda = lam;
+    res->ndead = scnt[0];
+  }
+}
+
+// A[i][j] = H'[p_i][p_j] (+ lambda on the diagonal) for j <= i, 0 above.
+template <typename T>
+__global__ __launch_bounds__(256) void copy_damped(const float* __restrict__ H,
+                                                   int n, const int32_t* __restrict__ perm,
+                                                   const double* __restrict__ lam_p,
+                                                   T* __restrict__ A, const DevFlags* flags) {
+  if (flags->info != 0) return;
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  const double lam = *lam_p;
+  T v = (T)0;
+  if (j <= i) {
+    const int pi = perm ? perm[i] : i, pj = perm ? perm[j] : j;
+    const int a = pi > pj ? pi : pj, b = pi > pj ? pj : pi;
+    const float h = H[(int64_t)a * n + b];
+    if (i == j)
+      v = (T)((h == 0.0f ? 1.0 : (double)h) + lam);
+    else
+      v = (T)h;
+  }
+  A[(int64_t)i * n + j] = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void chol_diag(T* __restrict__ A, int n, int k0,
+                                                 DevFlags* flags,
+                                                 pwq_result* __restrict__ res) {
+  __shared__ T a[NB][NB + 1];
+  if (flags->info != 0) return;
+  const int nb = min(NB, n - k0);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    a[r][c] = (r < nb && c <= r) ? A[(int64_t)(k0 + r) * n + k0 + c] : (T)0;
+  }
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    const T piv = a[j][j];
+    // every thread reads the same pivot: uniform decision
+    if (!(piv > (T)0) || !(piv < (T)INFINITY)) {
+      if (tid == 0) {
+        flags->info = k0 + j + 1;
+        res->info = k0 + j + 1;
+      }
+      return;
+    }
+    const T d = sqrt(piv);
+    const T inv = (T)1 / d;
+    __syncthreads();
+    if (tid < nb) {
+      if (tid == j) a[j][j] = d;
+      else if (tid > j) a[tid][j] *= inv;
+    }
+    __syncthreads();
+    // rank-1 update of the trailing lower part: a[r][c] -= a[r][j] a[c][j]
+    const int m = nb - j - 1;
+    for (int e = tid; e < m * m; e += 256) {
+      const int r = j + 1 + e / m, c = j + 1 + e % m;
+      if (c <= r) a[r][c] -= a[r][j] * a[c][j];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < nb * nb; e += 256) {
+    const int r = e / nb, c = e % nb;
+    if (c <= r) A[(int64_t)(k0 + r) * n + k0 + c] = a[r][c];
+  }
+}
+
+// Rows below the diagonal block: x = a L_kk^-T by forward substitution,
+// column-oriented (x_j /= l_jj, then x_p -= x_j l_pj for p > j).  Only
+// launched while a full 64-column panel has rows below it.
+template <typename T>
+__global__ __launch_bounds__(256) void chol_panel(T* __restrict__ A, int n, int k0,
+                                                  const DevFlags* flags) {
+  __shared__ T l[NB][NB + 1];
+  __shared__ T linv[NB];
+  if (flags->info != 0) return;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    l[r][c] = A[(int64_t)(k0 + r) * n + k0 + c];
+  }
+  __syncthreads();
+  if (tid < NB) linv[tid] = (T)1 / l[tid][tid];
+  __syncthreads();
+  const int i = k0 + NB + blockIdx.x * 256 + tid;
+  if (i >= n) return;
+  T* row = A + (int64_t)i * n + k0;
+  T x[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) x[j] = row[j];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    x[j] *= linv[j];
+#pragma unroll
+    for (int p = j + 1; p < NB; ++p) x[p] -= x[j] * l[p][j];
+    // keep each column's LDS reads next to their use (bounded live ranges)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) row[j] = x[j];
+}
+
+// Trailing update of the lower triangle: A_ij -= P_i P_j^T, P = the panel
+// (columns k0..k0+nb of the rows below the diagonal block).
+template <typename T>
+__global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, int k0,
+                                                     const DevFlags* flags) {
+  constexpr int TB = 128, LD = NB + 1;
+  __shared__ T As[TB * LD];
+  __shared__ T Bs[TB * LD];
+  if (flags->info != 0) return;
+  const int base = k0 + NB;
+  int ti, tj;
+  {
+    const int t = blockIdx.x;
+    int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    while (r * (r + 1) / 2 > t) --r;
+    ti = r;
+    tj = t - r * (r + 1) / 2;
+  }
+  const int r0 = base + ti * TB, c0 = base + tj * TB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  for (int e = tid; e < TB * NB; e += 256) {
+    const int r = e / NB, k = e % NB;
+    As[r * LD + k] = (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
+    Bs[r * LD + k] = (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
+  }
+  __syncthreads();
+  if constexpr (sizeof(T) == 4) {
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < NB; k += 2) {
+      const int ko = k + (lane >> 5);
+      const float a0 = As[(wm * 64 + (lane & 31)) * LD + ko];
+      const float a1 = As[(wm * 64 + 32 + (lane & 31)) * LD + ko];
+      const float b0 = Bs[(wn * 64 + (lane & 31)) * LD + ko];
+      const float b1 = Bs[(wn * 64 + 32 + (lane & 31)) * LD + ko];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] -= acc[i][j][r];
+        }
+  } else {
+    f64x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0;
+#pragma unroll 4
+    for (int k = 0; k < NB; k += 4) {
+      const int ko = k + (lane >> 4);
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[(wm * 64 + i * 16 + (lane & 15)) * LD + ko];
+        b[i] = Bs[(wn * 64 + i * 16 + (lane & 15)) * LD + ko];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gr = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] -= acc[i][j][r];
+        }
+  }
+}
+
+template <typename T>
+hipError_t factor_impl(T* A, int n, DevFlags* flags, pwq_result* res, hipStream_t st) {
+  for (int k0 = 0; k0 < n; k0 += NB) {
+    chol_diag<T><<<1, 256, 0, st>>>(A, n, k0, flags, res);
+    const int below = n - k0 - NB;
+    if (below > 0) {
+      chol_panel<T><<<(below + 255) / 256, 256, 0, st>>>(A, n, k0, flags);
+      const int nt = (below + 127) / 128;
+      chol_trailing<T><<<nt * (nt + 1) / 2, 256, 0, st>>>(A, n, k0, flags);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec,
+                                const int32_t* perm, void* L, int32_t* dead,
+                                pwq_result* res, DevFlags* flags, double* lam,
+                                hipStream_t st) {
+  damp_prep<<<1, 256, 0, st>>>(H, (int)n, damp, dead, res, flags, lam);
+  dim3 g((unsigned)((n + 255) / 256), (unsigned)n);
+  if (prec == PWQ_F64) {
+    copy_damped<double><<<g, 256, 0, st>>>(H, (int)n, perm, lam, (double*)L, flags);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return factor_impl<double>((double*)L, (int)n, flags, res, st);
+  }
+  copy_damped<float><<<g, 256, 0, st>>>(H, (int)n, perm, lam, (float*)L, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return factor_impl<float>((float*)L, (int)n, flags, res, st);
+}
+
+}  // namespace pwq

@@ -1,0 +1,396 @@
+// extern "C" entry points of libpwq: argument validation, workspace carving
+// and stage orchestration.  Every argument check runs before any HIP call,
+// so invalid requests return without touching the device.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "pwq_internal.h"
+
+using namespace pwq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pwq_status fail(pwq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pwq_status ok() {
+  g_last_error.clear();
+  return PWQ_OK;
+}
+
+pwq_status hip_fail(hipError_t e, const char* where) {
+  return fail(PWQ_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures, so sizing and carving share one code path.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+  size_t size() const { return (off + kAlign - 1) / kAlign * kAlign; }
+};
+
+size_t elem(int32_t prec) { return prec == PWQ_F64 ? 8 : 4; }
+
+bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128 || b == 256; }
+
+pwq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return PWQ_OK;
+  if (!ws) return fail(PWQ_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws % kAlign)
+    return fail(PWQ_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(PWQ_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return PWQ_OK;
+}
+
+pwq_status check_grid(const pwq_grid* g, int64_t n, bool allow_colspacing) {
+  if (!g) return fail(PWQ_ERR_INVALID_ARG, "grid is NULL");
+  if (g->kind == PWQ_GRID_SYM || g->kind == PWQ_GRID_ASYM) {
+    if (g->bits < 2 || g->bits > 16)
+      return fail(PWQ_ERR_INVALID_ARG, "bits must be in [2, 16] (got %d)", g->bits);
+    if (g->group_size < 0) return fail(PWQ_ERR_INVALID_ARG, "group_size must be >= 0");
+    if (g->group_size > 0 && n % g->group_size)
+      return fail(PWQ_ERR_INVALID_ARG, "group_size %d does not divide n = %lld", g->group_size,
+                  (long long)n);
+    return PWQ_OK;
+  }
+  if (g->kind == PWQ_GRID_COLSPACING) {
+    if (!allow_colspacing) return fail(PWQ_ERR_INVALID_ARG, "COLSPACING steps need the factor");
+    if (!(g->c > 0.0) || !(g->c < 1e300))
+      return fail(PWQ_ERR_INVALID_ARG, "COLSPACING needs a finite c > 0");
+    return PWQ_OK;
+  }
+  return fail(PWQ_ERR_INVALID_ARG, "unknown grid kind %d", g->kind);
+}
+
+int group_of(const pwq_grid* g, int64_t n) { return g->group_size > 0 ? g->group_size : (int)n; }
+
+// ---- workspace layouts (shared by sizing and carving)
+
+struct SweepWs {
+  DevFlags* flags;
+  void *invd, *dg, *alpha, *acc, *E;
+  double* partials;
+};
+
+void carve_sweep(Carver& c, int64_t m, int64_t n, int32_t block, int32_t prec, SweepWs* w) {
+  w->invd = c.take((size_t)n * elem(prec));
+  w->dg = c.take((size_t)n * elem(prec));
+  w->alpha = c.take((size_t)n * elem(prec));
+  w->acc = c.take((size_t)m * n * elem(prec));
+  w->E = c.take((size_t)m * block * elem(prec));
+  w->partials = (double*)c.take(sweep_partials_bytes(m, n, block));
+}
+
+struct LayerWs {
+  DevFlags* flags;
+  double* lam;
+  int32_t* perm;
+  int32_t* seen;
+  int32_t* dead;
+  float* H;
+  void* partial;
+  void* L;
+  SweepWs sw;
+};
+
+void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool need_h,
+                 bool need_l, int32_t xdtype, int32_t block, int32_t prec, LayerWs* w) {
+  w->flags = (DevFlags*)c.take(sizeof(DevFlags));
+  w->lam = (double*)c.take(sizeof(double));
+  w->perm = (int32_t*)c.take((size_t)n * 4);
+  w->seen = (int32_t*)c.take((size_t)n * 4);
+  w->dead = (int32_t*)c.take((size_t)n * 4);
+  w->H = need_h ? (float*)c.take((size_t)n * n * 4) : nullptr;
+  w->partial = nullptr;
+  if (has_x) {
+    SyrkPlan p;
+    syrk_plan(n, ntok, xdtype, &p);
+    w->partial = p.partial_bytes ? c.take(p.partial_bytes) : nullptr;
+  }
+  w->L = need_l ? c.take((size_t)n * n * elem(prec)) : nullptr;
+  carve_sweep(c, m, n, block, prec, &w->sw);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pwq_status_string(pwq_status s) {
+  switch (s) {
+    case PWQ_OK: return "PWQ_OK";
+    case PWQ_ERR_INVALID_ARG: return "PWQ_ERR_INVALID_ARG";
+    case PWQ_ERR_UNSUPPORTED: return "PWQ_ERR_UNSUPPORTED";
+    case PWQ_ERR_WORKSPACE: return "PWQ_ERR_WORKSPACE";
+    case PWQ_ERR_HIP: return "PWQ_ERR_HIP";
+  }
+  return "PWQ_ERR_UNKNOWN";
+}
+
+const char* pwq_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------ Hessian
+
+size_t pwq_hessian_workspace_size(int64_t n, int64_t ntok) {
+  if (n <= 0 || ntok < 0) return 0;
+  SyrkPlan a, b;
+  syrk_plan(n, ntok, PWQ_BF16, &a);
+  syrk_plan(n, ntok, PWQ_F32, &b);
+  size_t need = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
+  return (need + kAlign - 1) / kAlign * kAlign;
+}
+
+pwq_status pwq_hessian_accum(float* H, int64_t n, const void* X, int32_t xdtype, int64_t ntok,
+                             int64_t ldx, int32_t accumulate, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!H) return fail(PWQ_ERR_INVALID_ARG, "H is NULL");
+  if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
+  if (ntok < 0) return fail(PWQ_ERR_INVALID_ARG, "ntok must be >= 0");
+  if (ntok > 0 && !X) return fail(PWQ_ERR_INVALID_ARG, "X is NULL");
+  if (xdtype != PWQ_BF16 && xdtype != PWQ_F32)
+    return fail(PWQ_ERR_INVALID_ARG, "X dtype must be PWQ_BF16 or PWQ_F32");
+  if (ldx < ntok) return fail(PWQ_ERR_INVALID_ARG, "ldx < ntok");
+  SyrkPlan p;
+  syrk_plan(n, ntok, xdtype, &p);
+  pwq_status s = check_ws(ws, ws_bytes, p.partial_bytes);
+  if (s != PWQ_OK) return s;
+  hipError_t e = launch_hessian(H, n, X, xdtype, ntok, ldx, accumulate, p, ws,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hessian_accum launch");
+  return ok();
+}
+
+// ----------------------------------------------------------------- Cholesky
+
+size_t pwq_cholesky_workspace_size(int64_t n, int32_t prec) {
+  (void)n;
+  (void)prec;
+  Carver c(nullptr);
+  c.take(sizeof(DevFlags));
+  c.take(sizeof(double));
+  return c.size();
+}
+
+pwq_status pwq_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec, void* L,
+                             int32_t* dead, pwq_result* result, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!H || !L || !result) return fail(PWQ_ERR_INVALID_ARG, "H, L and result must be non-NULL");
+  if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
+  if (prec != PWQ_F32 && prec != PWQ_F64)
+    return fail(PWQ_ERR_INVALID_ARG, "prec must be PWQ_F32 or PWQ_F64");
+  if (!(damp >= 0.0f) || !(damp < 1e30f)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
+  pwq_status s = check_ws(ws, ws_bytes, pwq_cholesky_workspace_size(n, prec));
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  DevFlags* flags = (DevFlags*)c.take(sizeof(DevFlags));
+  double* lam = (double*)c.take(sizeof(double));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_init_flags(flags, result, 1, st);
+  if (e == hipSuccess)
+    e = launch_damp_cholesky(H, n, damp, prec, nullptr, L, dead, result, flags, lam, st);
+  if (e != hipSuccess) return hip_fail(e, "damp_cholesky launch");
+  return ok();
+}
+
+// -------------------------------------------------------------------- steps
+
+pwq_status pwq_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
+                          const int32_t* dead, const pwq_grid* grid, float* scales,
+                          int32_t* zeros, void* stream) {
+  if (!W || !scales) return fail(PWQ_ERR_INVALID_ARG, "W and scales must be non-NULL");
+  if (m <= 0 || n <= 0) return fail(PWQ_ERR_INVALID_ARG, "m and n must be positive");
+  if (wdtype != PWQ_BF16 && wdtype != PWQ_F32)
+    return fail(PWQ_ERR_INVALID_ARG, "W dtype must be PWQ_BF16 or PWQ_F32");
+  if (ldw < n) return fail(PWQ_ERR_INVALID_ARG, "ldw < n");
+  pwq_status s = check_grid(grid, n, false);
+  if (s != PWQ_OK) return s;
+  if (grid->kind == PWQ_GRID_ASYM && !zeros)
+    return fail(PWQ_ERR_INVALID_ARG, "ASYM grid needs zeros");
+  hipError_t e = launch_grid_steps(W, wdtype, m, n, ldw, dead, grid->kind, grid->bits,
+                                   group_of(grid, n), scales, zeros, nullptr,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "grid_steps launch");
+  return ok();
+}
+
+// -------------------------------------------------------------------- sweep
+
+size_t pwq_sweep_workspace_size(int64_t m, int64_t n, int32_t block, int32_t prec) {
+  if (m < 0 || n <= 0 || !valid_block(block)) return 0;
+  Carver c(nullptr);
+  c.take(sizeof(DevFlags));
+  SweepWs w;
+  carve_sweep(c, m, n, block, prec, &w);
+  return c.size();
+}
+
+static pwq_status check_sweep_common(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                                     int64_t ldw, int32_t prec, const pwq_grid* grid,
+                                     float* scales, const int32_t* zeros, int32_t block,
+                                     int32_t* codes, pwq_result* result) {
+  if (!W && m > 0) return fail(PWQ_ERR_INVALID_ARG, "W is NULL");
+  if (!codes && m > 0) return fail(PWQ_ERR_INVALID_ARG, "codes is NULL");
+  if (!result) return fail(PWQ_ERR_INVALID_ARG, "result is NULL");
+  if (m < 0 || m > (1 << 30)) return fail(PWQ_ERR_INVALID_ARG, "m out of range");
+  if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
+  if (wdtype != PWQ_BF16 && wdtype != PWQ_F32)
+    return fail(PWQ_ERR_INVALID_ARG, "W dtype must be PWQ_BF16 or PWQ_F32");
+  if (ldw < n) return fail(PWQ_ERR_INVALID_ARG, "ldw < n");
+  if (prec != PWQ_F32 && prec != PWQ_F64)
+    return fail(PWQ_ERR_INVALID_ARG, "prec must be PWQ_F32 or PWQ_F64");
+  if (!valid_block(block))
+    return fail(PWQ_ERR_UNSUPPORTED, "block must be 32, 64, 128 or 256 (got %d)", block);
+  pwq_status s = check_grid(grid, n, true);
+  if (s != PWQ_OK) return s;
+  if (!scales) return fail(PWQ_ERR_INVALID_ARG, "scales is NULL");
+  if (grid->kind == PWQ_GRID_ASYM && !zeros)
+    return fail(PWQ_ERR_INVALID_ARG, "ASYM grid needs zeros");
+  return PWQ_OK;
+}
+
+pwq_status pwq_babai_sweep(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
+                           const void* L, int32_t prec, const int32_t* dead,
+                           const pwq_grid* grid, float* scales, const int32_t* zeros,
+                           int32_t block, int32_t* codes, pwq_result* result, void* ws,
+                           size_t ws_bytes, void* stream) {
+  pwq_status s = check_sweep_common(W, wdtype, m, n, ldw, prec, grid, scales, zeros, block,
+                                    codes, result);
+  if (s != PWQ_OK) return s;
+  if (!L) return fail(PWQ_ERR_INVALID_ARG, "L is NULL");
+  s = check_ws(ws, ws_bytes, pwq_sweep_workspace_size(m, n, block, prec));
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  DevFlags* flags = (DevFlags*)c.take(sizeof(DevFlags));
+  SweepWs w;
+  carve_sweep(c, m, n, block, prec, &w);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_init_flags(flags, result, 1, st);
+  if (e != hipSuccess) return hip_fail(e, "babai_sweep launch");
+  SweepLaunch sl{};
+  sl.W = W; sl.wdtype = wdtype; sl.ldw = ldw; sl.m = m; sl.n = n; sl.prec = prec;
+  sl.block = block; sl.L = L; sl.invd = w.invd; sl.dg = w.dg; sl.alpha = w.alpha;
+  sl.colspacing = grid->kind == PWQ_GRID_COLSPACING; sl.c = grid->c;
+  sl.scales = scales; sl.scales_out = scales;
+  sl.zeros = grid->kind == PWQ_GRID_ASYM ? zeros : nullptr;
+  const int G = sl.colspacing ? 1 : group_of(grid, n);
+  sl.G = G; sl.ng = (int)(n / G);
+  sl.colmap = nullptr; sl.dead = dead; sl.acc = w.acc; sl.E = w.E; sl.codes = codes;
+  sl.partials = w.partials; sl.result = result; sl.flags = flags;
+  e = launch_sweep(sl, st);
+  if (e != hipSuccess) return hip_fail(e, "babai_sweep launch");
+  return ok();
+}
+
+// -------------------------------------------------------------- whole layer
+
+size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_t has_x,
+                                      int32_t order_kind, int32_t block, int32_t prec) {
+  (void)order_kind;
+  if (m < 0 || n <= 0 || !valid_block(block)) return 0;
+  Carver c(nullptr);
+  LayerWs w;
+  // size for the worst case: H and L kept in the workspace, bf16 or fp32 X
+  size_t a, b;
+  carve_layer(c, m, n, ntok, has_x != 0, has_x != 0, true, PWQ_BF16, block, prec, &w);
+  a = c.size();
+  Carver c2(nullptr);
+  carve_layer(c2, m, n, ntok, has_x != 0, has_x != 0, true, PWQ_F32, block, prec, &w);
+  b = c2.size();
+  return a > b ? a : b;
+}
+
+pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
+                           const void* X, int32_t xdtype, int64_t ntok, int64_t ldx,
+                           const float* H, const pwq_grid* grid, int32_t order_kind,
+                           const int32_t* perm, float damp, int32_t block, int32_t prec,
+                           int32_t* codes, float* scales, int32_t* zeros, pwq_result* result,
+                           float* H_out, void* L_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  pwq_status s = check_sweep_common(W, wdtype, m, n, ldw, prec, grid, scales, zeros, block,
+                                    codes, result);
+  if (s != PWQ_OK) return s;
+  const bool has_x = X != nullptr;
+  if (has_x == (H != nullptr)) return fail(PWQ_ERR_INVALID_ARG, "give exactly one of X and H");
+  if (has_x) {
+    if (xdtype != PWQ_BF16 && xdtype != PWQ_F32)
+      return fail(PWQ_ERR_INVALID_ARG, "X dtype must be PWQ_BF16 or PWQ_F32");
+    if (ntok < 0 || ldx < ntok) return fail(PWQ_ERR_INVALID_ARG, "bad ntok / ldx");
+  } else if (H_out) {
+    return fail(PWQ_ERR_INVALID_ARG, "H_out is only produced when X is given");
+  }
+  if (order_kind < PWQ_ORDER_BACK_TO_FRONT || order_kind > PWQ_ORDER_ACT)
+    return fail(PWQ_ERR_INVALID_ARG, "unknown order %d", order_kind);
+  if (order_kind == PWQ_ORDER_PERM && !perm)
+    return fail(PWQ_ERR_INVALID_ARG, "PERM order needs perm");
+  if (!(damp >= 0.0f) || !(damp < 1e30f)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
+
+  const bool need_h = has_x && !H_out;
+  const bool need_l = !L_out;
+  Carver measure(nullptr);
+  LayerWs w;
+  carve_layer(measure, m, n, ntok, has_x, need_h, need_l, xdtype, block, prec, &w);
+  s = check_ws(ws, ws_bytes, measure.size());
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  carve_layer(c, m, n, ntok, has_x, need_h, need_l, xdtype, block, prec, &w);
+  hipStream_t st = (hipStream_t)stream;
+  float* Hm = has_x ? (H_out ? H_out : w.H) : (float*)H;
+  void* Lm = L_out ? L_out : w.L;
+
+  hipError_t e = launch_init_flags(w.flags, result, 1, st);
+  if (e == hipSuccess && has_x) {
+    SyrkPlan p;
+    syrk_plan(n, ntok, xdtype, &p);
+    e = launch_hessian(Hm, n, X, xdtype, ntok, ldx, 0, p, w.partial, st);
+  }
+  const int32_t* colmap = nullptr;
+  if (e == hipSuccess && order_kind != PWQ_ORDER_BACK_TO_FRONT) {
+    e = launch_order(order_kind, Hm, n, perm, w.perm, w.seen, result, w.flags, st);
+    colmap = order_kind == PWQ_ORDER_PERM ? perm : w.perm;
+  }
+  if (e == hipSuccess)
+    e = launch_damp_cholesky(Hm, n, damp, prec, colmap, Lm, w.dead, result, w.flags, w.lam,
+                             st);
+  const bool colsp = grid->kind == PWQ_GRID_COLSPACING;
+  const int G = colsp ? 1 : group_of(grid, n);
+  if (e == hipSuccess && !colsp && m > 0)
+    e = launch_grid_steps(W, wdtype, m, n, ldw, w.dead, grid->kind, grid->bits, G, scales,
+                          zeros, w.flags, st);
+  if (e == hipSuccess) {
+    SweepLaunch sl{};
+    sl.W = W; sl.wdtype = wdtype; sl.ldw = ldw; sl.m = m; sl.n = n; sl.prec = prec;
+    sl.block = block; sl.L = Lm; sl.invd = w.sw.invd; sl.dg = w.sw.dg; sl.alpha = w.sw.alpha;
+    sl.colspacing = colsp; sl.c = grid->c;
+    sl.scales = scales; sl.scales_out = scales;
+    sl.zeros = grid->kind == PWQ_GRID_ASYM ? zeros : nullptr;
+    sl.G = G; sl.ng = (int)(n / G);
+    sl.colmap = colmap; sl.dead = w.dead; sl.acc = w.sw.acc; sl.E = w.sw.E; sl.codes = codes;
+    sl.partials = w.sw.partials; sl.result = result; sl.flags = w.flags;
+    e = launch_sweep(sl, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "quant_layer launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Host-side declarations shared by the libpwq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pwq.h"
+#include "pwq_device.h"
+
+namespace pwq {
+
+struct SyrkPlan {
+  int64_t ntiles;
+  int64_t nsplit;
+  int64_t kps;           // tokens per split (multiple of the LDS stage)
+  size_t partial_bytes;  // 0 when a single split writes H directly
+};
+
+void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, SyrkPlan* p);
+hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype, int64_t ntok,
+                          int64_t ldx, int32_t accumulate, const SyrkPlan& p, void* partial,
+                          hipStream_t st);
+
+hipError_t launch_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec,
+                                const int32_t* perm, void* L, int32_t* dead, pwq_result* res,
+                                DevFlags* flags, double* lam, hipStream_t st);
+
+hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
+                             const int32_t* dead, int kind, int bits, int G, float* scales,
+                             int32_t* zeros, const DevFlags* flags, hipStream_t st);
+
+struct SweepLaunch {
+  const void* W;
+  int32_t wdtype;
+  int64_t ldw, m, n;
+  int32_t prec, block;
+  const void* L;
+  void* invd;
+  void* dg;
+  void* alpha;
+  int colspacing;
+  double c;
+  float* scales;       // SYM/ASYM input
+  float* scales_out;   // COLSPACING output (per original column)
+  const int32_t* zeros;
+  int ng, G;
+  const int32_t* colmap;
+  const int32_t* dead;
+  void* acc;
+  void* E;
+  int32_t* codes;
+  double* partials;
+  pwq_result* result;
+  const DevFlags* flags;
+};
+
+size_t sweep_partials_bytes(int64_t m, int64_t n, int32_t block);
+hipError_t launch_sweep(const SweepLaunch& sl, hipStream_t st);
+
+hipError_t launch_order(int32_t order_kind, const float* H, int64_t n, const int32_t* perm_in,
+                        int32_t* perm_out, int32_t* seen, pwq_result* res, DevFlags* flags,
+                        hipStream_t st);
+hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, hipStream_t st);
+
+}  // namespace pwq

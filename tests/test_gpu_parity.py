@@ -1,0 +1,256 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, at sizes
+the oracle finishes in seconds that still span several tiles, panels and
+blocks plus ragged tails.
+
+Codes are judged stage-fed: the oracle is run on the GPU's own fp32 Hessian
+(widened to fp64), so the comparison isolates the factor and the sweep; the
+Hessian itself is compared with the oracle's fp64 Hessian of the same X.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_19_amd as P
+import synth
+from _gpu import to_np, upload
+from _parity import (TOL_H, TOL_L, TOL_STEP, check_codes, check_loss, rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": (synth.config(1), "f32", None),
+    "qproj_small": (synth.config(2).resized(m=80, n=384, ntok=4096), "f32", None),
+    "upproj_small_ragged": (synth.config(3).resized(m=100, n=256, ntok=3000), "f32", None),
+    "downproj_small_ragged": (synth.config(4).resized(m=64, n=576, ntok=2048), "f32", None),
+    "zsic_small": (synth.config(5).resized(m=48, n=512), "f64", 0.001),
+}
+
+
+def _grid(cfg, c=None):
+    if cfg.grid_kind == "colspacing":
+        return P.Grid("colspacing", 0, 0, c if c is not None else cfg.colspacing_c)
+    return P.Grid(cfg.grid_kind, cfg.bits, cfg.group)
+
+
+def _oracle_args(cfg, c=None):
+    return dict(grid_kind=cfg.grid_kind, bits=cfg.bits, group=cfg.group,
+                c=(c if c is not None else cfg.colspacing_c), damp=cfg.damp)
+
+
+@pytest.fixture(scope="module")
+def layers():
+    return {k: synth.make_layer(v[0]) for k, v in CASES.items()}
+
+
+def _run(layer, prec, c, order="back_to_front", perm=None, block=None):
+    cfg = layer.cfg
+    W, X, H = upload(layer)
+    out = P.quant_layer(W, X=X, H=H, grid=_grid(cfg, c), order=order, perm=perm,
+                        damp=cfg.damp, block=block or cfg.block, prec=prec,
+                        want_H=X is not None, want_L=True)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", [k for k, v in CASES.items() if v[0].ntok > 0])
+def test_hessian_stage(layers, case):
+    lay = layers[case]
+    _, X, _ = upload(lay)
+    H = P.hessian_accum(X)
+    torch.cuda.synchronize()
+    Hg = to_np(H)
+    assert np.array_equal(Hg, Hg.T)
+    err = rel_fro(Hg, O.hessian(lay.X64()))
+    assert err <= TOL_H, err
+
+
+def test_hessian_accumulate_and_empty(layers):
+    lay = layers["qproj_small"]
+    _, X, _ = upload(lay)
+    H1 = P.hessian_accum(X)
+    H2 = P.hessian_accum(X, H=H1.clone(), accumulate=True)
+    torch.cuda.synchronize()
+    assert rel_fro(to_np(H2), 2 * to_np(H1)) <= 1e-6
+    Xe = torch.empty((40, 0), dtype=torch.bfloat16, device="cuda")
+    He = P.hessian_accum(Xe)
+    torch.cuda.synchronize()
+    assert np.all(to_np(He) == 0)
+
+
+@pytest.mark.parametrize("prec,tol", [("f32", TOL_L), ("f64", 1e-10)])
+def test_cholesky_stage(layers, prec, tol):
+    lay = layers["qproj_small"]
+    H64 = O.hessian(lay.X64())
+    Ht = torch.from_numpy(H64.astype(np.float32)).cuda()
+    L, dead, res = P.damp_cholesky(Ht, damp=0.01, prec=prec)
+    torch.cuda.synchronize()
+    r = P.read_result(res)
+    Hd, _, lam, _ = O.fix_dead_and_damp(H64.astype(np.float32).astype(np.float64),
+                                       np.zeros((1, H64.shape[0])), 0.01)
+    Lo, info = O.cholesky_lower(Hd)
+    assert info == 0 and r["info"] == 0 and r["ndead"] == 0
+    assert r["lambda"] == pytest.approx(lam, rel=1e-12)
+    Lg = to_np(L)
+    assert np.all(np.triu(Lg, 1) == 0)
+    assert rel_fro(Lg, Lo) <= tol
+
+
+def test_cholesky_reports_failing_minor():
+    n = 200
+    d = np.ones(n, np.float32)
+    d[70] = -1.0
+    H = torch.from_numpy(np.diag(d)).cuda()
+    for prec in ("f32", "f64"):
+        _, _, res = P.damp_cholesky(H, damp=0.0, prec=prec)
+        torch.cuda.synchronize()
+        assert P.read_result(res)["info"] == 71
+    Hn = np.eye(n, dtype=np.float32)
+    Hn[130, 130] = np.nan
+    _, _, res = P.damp_cholesky(torch.from_numpy(Hn).cuda(), damp=0.0)
+    torch.cuda.synchronize()
+    assert P.read_result(res)["info"] == 131
+    # the whole layer reports it too, and skips the sweep
+    W = torch.zeros((16, n), dtype=torch.float32, device="cuda")
+    out = P.quant_layer(W, H=H, grid=P.Grid("sym", 4, 0), damp=0.0, block=64)
+    torch.cuda.synchronize()
+    assert P.read_result(out["result"])["info"] == 71
+
+
+@pytest.mark.parametrize("kind,bits,group", [("sym", 4, 0), ("sym", 3, 128), ("asym", 4, 128),
+                                             ("asym", 2, 64), ("sym", 2, 64)])
+def test_grid_steps(layers, kind, bits, group):
+    lay = layers["qproj_small"]
+    W, _, _ = upload(lay)
+    s, z = P.grid_steps(W, P.Grid(kind, bits, group))
+    torch.cuda.synchronize()
+    so, zo = O.grid_steps(lay.W64(), kind, bits, group)
+    np.testing.assert_allclose(to_np(s), so, rtol=TOL_STEP)
+    if kind == "asym":
+        np.testing.assert_array_equal(to_np(z), zo)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_quant_layer(layers, case):
+    cfg, prec, c = CASES[case]
+    lay = layers[case]
+    out = _run(lay, prec, c)
+    r = P.read_result(out["result"])
+    assert r["info"] == 0
+    if lay.X is not None:
+        H64 = O.hessian(lay.X64())
+        Hg = to_np(out["H"]).astype(np.float64)
+        assert rel_fro(Hg, H64) <= TOL_H
+    else:
+        Hg = lay.H.astype(np.float64)
+    ref = O.quant_layer(lay.W64(), H=Hg, **_oracle_args(cfg, c))
+    assert rel_fro(to_np(out["L"]), ref["L"]) <= (TOL_L if prec == "f32" else 1e-9)
+    assert r["lambda"] == pytest.approx(ref["lam"], rel=1e-9)
+    scales = to_np(out["scales"])
+    np.testing.assert_allclose(scales, ref["scales"], rtol=TOL_STEP)
+    zeros = to_np(out["zeros"]) if out["zeros"] is not None else None
+    if zeros is not None:
+        np.testing.assert_array_equal(zeros, ref["zeros"])
+    stats = check_codes(to_np(out["codes"]), ref, zeros, label=case)
+    check_loss(r["loss"], ref["loss"], case + " loss")
+    check_loss(r["loss_damped"], ref["loss_damped"], case + " loss_damped")
+    check_loss(r["bound"], ref["bound"], case + " bound")
+    assert r["loss_damped"] <= r["bound"]
+    print(case, stats, flush=True)
+
+
+def test_deterministic(layers):
+    lay = layers["qproj_small"]
+    a = _run(lay, "f32", None)
+    b = _run(lay, "f32", None)
+    assert torch.equal(a["codes"], b["codes"])
+    assert torch.equal(a["result"], b["result"])
+    assert torch.equal(a["H"], b["H"])
+
+
+@pytest.mark.parametrize("order", ["front_to_back", "act_order", "perm"])
+def test_orders(layers, order):
+    lay = layers["qproj_small"]
+    cfg = lay.cfg
+    perm = None
+    perm_np = None
+    if order == "perm":
+        perm_np = np.random.default_rng(5).permutation(cfg.n)
+        perm = torch.from_numpy(perm_np.astype(np.int32)).cuda()
+    out = _run(lay, "f32", None, order=order, perm=perm)
+    r = P.read_result(out["result"])
+    assert r["info"] == 0
+    Hg = to_np(out["H"]).astype(np.float64)
+    ref = O.quant_layer(lay.W64(), H=Hg, order=order, perm=perm_np, **_oracle_args(cfg))
+    zeros = to_np(out["zeros"])
+    check_codes(to_np(out["codes"]), ref, zeros, label=order)
+    check_loss(r["loss"], ref["loss"], order)
+
+
+def test_invalid_perm_reports_minus_one(layers):
+    lay = layers["qproj_small"]
+    perm = torch.zeros(lay.cfg.n, dtype=torch.int32, device="cuda")
+    out = _run(lay, "f32", None, order="perm", perm=perm)
+    assert P.read_result(out["result"])["info"] == -1
+
+
+def test_dead_feature(layers):
+    cfg = synth.config(2).resized(m=40, n=256, ntok=2048)
+    lay = synth.make_layer(cfg)
+    lay.X[37] = 0.0
+    lay.X_bits[37] = 0
+    out = _run(lay, "f32", None)
+    r = P.read_result(out["result"])
+    assert r["ndead"] == 1
+    Hg = to_np(out["H"]).astype(np.float64)
+    ref = O.quant_layer(lay.W64(), H=Hg, **_oracle_args(cfg))
+    codes = to_np(out["codes"])
+    zeros = to_np(out["zeros"])
+    Z = codes - np.repeat(zeros, cfg.group, axis=1)
+    assert np.all(Z[:, 37] == 0)
+    check_codes(codes, ref, zeros, label="dead")
+
+
+@pytest.mark.parametrize("block", [32, 64, 128, 256])
+def test_block_sizes(layers, block):
+    lay = layers["downproj_small_ragged"]
+    out = _run(lay, "f32", None, block=block)
+    Hg = to_np(out["H"]).astype(np.float64)
+    ref = O.quant_layer(lay.W64(), H=Hg, **_oracle_args(lay.cfg))
+    check_codes(to_np(out["codes"]), ref, None, label=f"block{block}")
+
+
+@pytest.mark.parametrize("prec", ["f32", "f64"])
+def test_sweep_stage_given_factor(layers, prec):
+    """The sweep alone, fed the oracle's own factor (rounded to the kernel's
+    precision)."""
+    lay = layers["qproj_small"]
+    cfg = lay.cfg
+    H64 = O.hessian(lay.X64())
+    Hd, W0, lam, _ = O.fix_dead_and_damp(H64, lay.W64(), cfg.damp)
+    L64, _ = O.cholesky_lower(Hd)
+    Lk = L64.astype(np.float32).astype(np.float64) if prec == "f32" else L64
+    W, _, _ = upload(lay)
+    grid = _grid(cfg)
+    s, z = P.grid_steps(W, grid)
+    Lt = torch.from_numpy(Lk.astype(np.float32 if prec == "f32" else np.float64)).cuda()
+    codes, _, res = P.babai_sweep(W, Lt, grid, scales=s, zeros=z, block=cfg.block)
+    torch.cuda.synchronize()
+    S = O.expand_group_steps(to_np(s).astype(np.float64), cfg.n)
+    Zo, rho = O.nearest_plane_sweep(W0, Lk, S)
+    ref = {"codes": Zo.astype(np.int64) + np.repeat(to_np(z), cfg.group, axis=1),
+           "pi": np.arange(cfg.n), "Sp": S, "W0": W0, "L": Lk}
+    check_codes(to_np(codes), ref, to_np(z), label="sweep " + prec)
+    r = P.read_result(res)
+    ident = float(np.sum(rho ** 2 * S ** 2 * np.diag(Lk)[None, :] ** 2))
+    check_loss(r["loss_damped"], ident, "sweep loss_damped")
+
+
+def test_empty_rows():
+    n = 128
+    H = torch.eye(n, dtype=torch.float32, device="cuda")
+    W = torch.zeros((0, n), dtype=torch.float32, device="cuda")
+    out = P.quant_layer(W, H=H, grid=P.Grid("sym", 4, 0), damp=0.0, block=32)
+    torch.cuda.synchronize()
+    r = P.read_result(out["result"])
+    assert r["info"] == 0 and r["loss"] == 0.0 and r["bound"] == 0.0
