@@ -75,16 +75,20 @@ def test_golden_asym_tie_rounds_to_even():
 def test_step_closed_forms_per_group():
     W = np.array([[0.1, -0.7, 0.3, 0.2],
                   [0.0, 0.0, -0.5, 0.25]])
+    # steps are stored (and computed) in float32: compare at that precision
+    f32 = dict(rtol=2 ** -23)
     s, z = O.grid_steps(W, "sym", 4, 2)
-    np.testing.assert_allclose(s, [[0.7 / 7, 0.3 / 7], [1.0, 0.5 / 7]])
+    np.testing.assert_allclose(s, [[0.7 / 7, 0.3 / 7], [1.0, 0.5 / 7]], **f32)
     assert z is None
     s, z = O.grid_steps(W, "asym", 3, 2)
     # row0 g0: lo=-0.7 hi=0.1; g1: lo=0 hi=0.3; row1 g0 all zero; g1 lo=-.5 hi=.25
-    np.testing.assert_allclose(s, [[0.8 / 7, 0.3 / 7], [1.0, 0.75 / 7]])
+    np.testing.assert_allclose(s, [[0.8 / 7, 0.3 / 7], [1.0, 0.75 / 7]], **f32)
     np.testing.assert_array_equal(z, [[np.rint(0.7 / (0.8 / 7)), 0],
                                       [0, np.rint(0.5 / (0.75 / 7))]])
     s, _ = O.grid_steps(W, "sym", 2, 0)
-    np.testing.assert_allclose(s, [[0.7], [0.5]])
+    np.testing.assert_allclose(s, [[0.7], [0.5]], **f32)
+    # the stored value is exactly the float32 quotient
+    assert s[0, 0] == float(np.float32(np.float32(0.7) / np.float32(1)))
 
 
 # ----------------------------------------------- three forms of one method
@@ -186,7 +190,9 @@ def test_lattice_points_are_fixed_points():
     m, n = 6, 16
     Z = rng.integers(-7, 8, (m, n)).astype(float)
     Z[:, 0] = 7.0  # max |z| = 7 in each row: the symmetric 4-bit step is s
-    s = rng.uniform(0.01, 0.1, (m, 1))
+    # dyadic steps: 7 s and 7 s / 7 are exact in float32, so the float32 step
+    # recovered from W is s itself
+    s = rng.integers(2 ** 12, 2 ** 16, (m, 1)) * 2.0 ** -20
     W = Z * s
     _, X = _rand_problem(rng, 1, n, 60)
     res = O.quant_layer(W, X=X, grid_kind="sym", bits=4, group=0, damp=0.01)
@@ -274,6 +280,11 @@ def test_cholesky_failure_reports_minor():
     res = O.quant_layer(np.ones((2, 4)), H=np.zeros((4, 4)) - np.eye(4),
                         damp=0.0)
     assert res["info"] == 1
+    # a NaN pivot is a failure at its column (reading; pages are silent)
+    C = np.eye(6)
+    C[4, 1] = C[1, 4] = np.nan
+    _, info = O.cholesky_lower(C)
+    assert info == 5
 
 
 def test_spectral_hessian_closed_form_factor():
