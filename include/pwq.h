@@ -144,7 +144,7 @@ pwq_status pwq_hessian_accum(float* H, int64_t n, const void* X, int32_t xdtype,
  *   result : lambda, ndead and info are written (losses are not).
  * ---------------------------------------------------------------------- */
 size_t pwq_cholesky_workspace_size(int64_t n, int32_t prec);
-pwq_status pwq_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec,
+pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                              void* L, int32_t* dead, pwq_result* result,
                              void* ws, size_t ws_bytes, void* stream);
 
@@ -207,7 +207,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
                            int64_t ldw, const void* X, int32_t xdtype,
                            int64_t ntok, int64_t ldx, const float* H,
                            const pwq_grid* grid, int32_t order_kind,
-                           const int32_t* perm, float damp, int32_t block,
+                           const int32_t* perm, double damp, int32_t block,
                            int32_t prec, int32_t* codes, float* scales,
                            int32_t* zeros, pwq_result* result, float* H_out,
                            void* L_out, void* ws, size_t ws_bytes, void* stream);

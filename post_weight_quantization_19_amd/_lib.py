@@ -45,15 +45,15 @@ class PwqError(RuntimeError):
 
 _lib = None
 
-_vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
-                              ctypes.c_float, ctypes.c_size_t)
+_vp, _i32, _i64, _f64, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                              ctypes.c_double, ctypes.c_size_t)
 _SIGS = {
     "pwq_status_string": (ctypes.c_char_p, [_i32]),
     "pwq_last_error": (ctypes.c_char_p, []),
     "pwq_hessian_workspace_size": (_sz, [_i64, _i64]),
     "pwq_hessian_accum": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _i32, _vp, _sz, _vp]),
     "pwq_cholesky_workspace_size": (_sz, [_i64, _i32]),
-    "pwq_damp_cholesky": (_i32, [_vp, _i64, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_damp_cholesky": (_i32, [_vp, _i64, _f64, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_grid_steps": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, ctypes.POINTER(PwqGrid),
                               _vp, _vp, _vp]),
     "pwq_sweep_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
@@ -62,7 +62,7 @@ _SIGS = {
                                _vp]),
     "pwq_quant_layer_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
     "pwq_quant_layer": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _i64, _i64, _vp,
-                               ctypes.POINTER(PwqGrid), _i32, _vp, _f32, _i32, _i32, _vp,
+                               ctypes.POINTER(PwqGrid), _i32, _vp, _f64, _i32, _i32, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 

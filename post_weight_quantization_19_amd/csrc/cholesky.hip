@@ -30,7 +30,7 @@ constexpr int NB = 64;   // panel width
 // lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;
 // fixed-order fp64 reduction.
 __global__ __launch_bounds__(256) void damp_prep(const float* __restrict__ H,
-                                                 int n, float damp,
+                                                 int n, double damp,
                                                  int32_t* __restrict__ dead,
                                                  pwq_result* __restrict__ res,
                                                  DevFlags* flags,
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void damp_prep(const float* __restrict__ H,
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double lam = (double)damp * (ssum[0] / (double)n);
+    const double lam = damp * (ssum[0] / (double)n);
     *lam_out = lam;
     res->lambda = lam;
     res->ndead = scnt[0];
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, i
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int gr = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
           if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] -= acc[i][j][r];
         }
@@ -280,7 +280,7 @@ hipError_t factor_impl(T* A, int n, DevFlags* flags, pwq_result* res, hipStream_
 
 }  // namespace
 
-hipError_t launch_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec,
+hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                                 const int32_t* perm, void* L, int32_t* dead,
                                 pwq_result* res, DevFlags* flags, double* lam,
                                 hipStream_t st) {

@@ -192,14 +192,14 @@ size_t pwq_cholesky_workspace_size(int64_t n, int32_t prec) {
   return c.size();
 }
 
-pwq_status pwq_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec, void* L,
+pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec, void* L,
                              int32_t* dead, pwq_result* result, void* ws, size_t ws_bytes,
                              void* stream) {
   if (!H || !L || !result) return fail(PWQ_ERR_INVALID_ARG, "H, L and result must be non-NULL");
   if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
   if (prec != PWQ_F32 && prec != PWQ_F64)
     return fail(PWQ_ERR_INVALID_ARG, "prec must be PWQ_F32 or PWQ_F64");
-  if (!(damp >= 0.0f) || !(damp < 1e30f)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
+  if (!(damp >= 0.0) || !(damp < 1e30)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
   pwq_status s = check_ws(ws, ws_bytes, pwq_cholesky_workspace_size(n, prec));
   if (s != PWQ_OK) return s;
   Carver c(ws);
@@ -263,7 +263,8 @@ static pwq_status check_sweep_common(const void* W, int32_t wdtype, int64_t m, i
     return fail(PWQ_ERR_UNSUPPORTED, "block must be 32, 64, 128 or 256 (got %d)", block);
   pwq_status s = check_grid(grid, n, true);
   if (s != PWQ_OK) return s;
-  if (!scales) return fail(PWQ_ERR_INVALID_ARG, "scales is NULL");
+  if (!scales && (m > 0 || grid->kind == PWQ_GRID_COLSPACING))
+    return fail(PWQ_ERR_INVALID_ARG, "scales is NULL");
   if (grid->kind == PWQ_GRID_ASYM && !zeros)
     return fail(PWQ_ERR_INVALID_ARG, "ASYM grid needs zeros");
   return PWQ_OK;
@@ -323,7 +324,7 @@ size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_
 pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
                            const void* X, int32_t xdtype, int64_t ntok, int64_t ldx,
                            const float* H, const pwq_grid* grid, int32_t order_kind,
-                           const int32_t* perm, float damp, int32_t block, int32_t prec,
+                           const int32_t* perm, double damp, int32_t block, int32_t prec,
                            int32_t* codes, float* scales, int32_t* zeros, pwq_result* result,
                            float* H_out, void* L_out, void* ws, size_t ws_bytes,
                            void* stream) {
@@ -343,7 +344,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
     return fail(PWQ_ERR_INVALID_ARG, "unknown order %d", order_kind);
   if (order_kind == PWQ_ORDER_PERM && !perm)
     return fail(PWQ_ERR_INVALID_ARG, "PERM order needs perm");
-  if (!(damp >= 0.0f) || !(damp < 1e30f)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
+  if (!(damp >= 0.0) || !(damp < 1e30)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
 
   const bool need_h = has_x && !H_out;
   const bool need_l = !L_out;

@@ -6,7 +6,8 @@
 //   v_mfma_f32_32x32x2f32    : A lane l holds A[l%32][l/32]; B [l/32][l%32].
 //   v_mfma_f64_16x16x4f64    : A lane l holds A[l%16][l/16]; B [l/16][l%16].
 //   32x32 results: lane l, register r -> C[8*(r/4) + 4*(l/32) + r%4][l%32].
-//   16x16 results: lane l, register r -> C[4*(l/16) + r][l%16].
+//   16x16 f32 results: lane l, register r -> C[4*(l/16) + r][l%16].
+//   16x16 f64 results: lane l, register r -> C[4*r + l/16][l%16].
 #pragma once
 
 #include <hip/hip_runtime.h>

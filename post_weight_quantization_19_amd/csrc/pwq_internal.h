@@ -22,7 +22,7 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype, in
                           int64_t ldx, int32_t accumulate, const SyrkPlan& p, void* partial,
                           hipStream_t st);
 
-hipError_t launch_damp_cholesky(const float* H, int64_t n, float damp, int32_t prec,
+hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                                 const int32_t* perm, void* L, int32_t* dead, pwq_result* res,
                                 DevFlags* flags, double* lam, hipStream_t st);
 

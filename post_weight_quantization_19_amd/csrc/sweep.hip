@@ -166,10 +166,11 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int blk, int 
       il = a.invd[col];
       if (!first) ac = a.acc[(int64_t)row * n + col];
     }
-    const T is = (T)1 / s;
+    // true (correctly rounded) quotients: with no feedback yet the coordinate
+    // is exactly w / s, so an exact tie is rounded to even as on paper
     acc[t] = ac;
-    av[t] = il * is;
-    bv[t] = w * is;
+    av[t] = il / s;
+    bv[t] = w / s;
     sv[t] = s;
     wv[t] = w;
   }
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int gr = r0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
           if (gr < m && gc < j0) {
             T* p = acc + (int64_t)gr * n + gc;

@@ -105,11 +105,16 @@ def test_cholesky_reports_failing_minor():
         _, _, res = P.damp_cholesky(H, damp=0.0, prec=prec)
         torch.cuda.synchronize()
         assert P.read_result(res)["info"] == 71
+    # a NaN below the diagonal reaches pivot 130 through the trailing update
     Hn = np.eye(n, dtype=np.float32)
-    Hn[130, 130] = np.nan
-    _, _, res = P.damp_cholesky(torch.from_numpy(Hn).cuda(), damp=0.0)
-    torch.cuda.synchronize()
-    assert P.read_result(res)["info"] == 131
+    Hn[130, 5] = Hn[5, 130] = np.nan
+    Hd, _, _, _ = O.fix_dead_and_damp(Hn.astype(np.float64), np.zeros((1, n)), 0.0)
+    _, info = O.cholesky_lower(Hd)
+    assert info == 131
+    for prec in ("f32", "f64"):
+        _, _, res = P.damp_cholesky(torch.from_numpy(Hn).cuda(), damp=0.0, prec=prec)
+        torch.cuda.synchronize()
+        assert P.read_result(res)["info"] == info
     # the whole layer reports it too, and skips the sweep
     W = torch.zeros((16, n), dtype=torch.float32, device="cuda")
     out = P.quant_layer(W, H=H, grid=P.Grid("sym", 4, 0), damp=0.0, block=64)
