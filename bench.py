@@ -1,0 +1,185 @@
+"""Benchmark: quantize one q_proj-shaped layer end to end on one MI355X.
+
+A step is one whole quant_layer call on device-resident inputs: H = 2 X X^T
+(bf16 MFMA SYRK), dead features + damping, blocked Cholesky, grid steps,
+the back-to-front nearest-plane sweep with lazy MFMA block updates, and the
+loss/bound reduction.  Workload: W 4096 x 4096 bf16, X 4096 x 131072 bf16
+(Student-t, 8 outlier channels x20), asymmetric 4-bit, group 128, block 128,
+damp 0.01 -- synthetic, seeded.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the Hessian
+SYRK): algorithmic flops n(n+1)N per launch over its average duration,
+measured here with HIP events on the stream the library launches on.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3          # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "layer quantize time (s) & weights quantized/s; MFMA util of SYRK+update"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload table entry")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-token-fraction", type=int, default=8,
+                    help="oracle Hessian is timed on 1/k of the tokens, scaled by k")
+    return ap.parse_args()
+
+
+def cpu_baseline(lay, cfg, frac):
+    """Time the fp64 oracle on a bounded sample and project the whole layer."""
+    import numpy as np
+
+    import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    ntok_s = cfg.ntok // frac
+    t0 = time.perf_counter()
+    Xs = lay.X[:, :ntok_s]
+    H_s = O.hessian(Xs)
+    t_h = (time.perf_counter() - t0) * frac
+    H = H_s * frac  # stand-in Hessian of the right scale for timing the rest
+    t0 = time.perf_counter()
+    Hd, W0, lam, _ = O.fix_dead_and_damp(H, lay.W64(), cfg.damp)
+    L, info = O.cholesky_lower(Hd)
+    t_c = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    s_grp, z = O.grid_steps(W0, cfg.grid_kind, cfg.bits, cfg.group)
+    S = O.expand_group_steps(s_grp, cfg.n)
+    O.nearest_plane_sweep_blocked(W0, L, S, cfg.block)
+    t_s = time.perf_counter() - t0
+    total = t_h + t_c + t_s
+    return {
+        "value": cfg.m * cfg.n / total, "unit": "weights/s", "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy/OpenBLAS oracle: Hessian on the first {ntok_s} of {cfg.ntok} "
+                   f"tokens, time x{frac}; full Cholesky and blocked sweep "
+                   f"({cfg.m}x{cfg.n}); projected whole-layer time {total:.2f} s "
+                   f"(H {t_h:.2f} s, chol {t_c:.2f} s, sweep {t_s:.2f} s)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the "
+              "quantizer's rows are independent, and a multi-GPU run would shard them "
+              "with one all-reduce of H, which this build does not implement.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_19_amd as P
+    import synth
+
+    cfg = synth.config(args.config)
+    m, n, N = cfg.m, cfg.n, cfg.ntok
+    print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
+          flush=True)
+    lay = synth.make_layer(cfg, keep_x_f32=not args.no_cpu_baseline)
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    grid = P.Grid(cfg.grid_kind, cfg.bits, cfg.group)
+    ws = P.workspace_for_layer(m, n, N, True, "back_to_front", cfg.block, "f32", dev)
+    out = P.quant_layer(W, X=X, grid=grid, damp=cfg.damp, block=cfg.block, workspace=ws)
+    torch.cuda.synchronize()
+    res0 = P.read_result(out["result"])
+    if res0["info"] != 0:
+        raise RuntimeError(f"Cholesky failed: {res0}")
+
+    def step():
+        P.quant_layer(W, X=X, grid=grid, damp=cfg.damp, block=cfg.block, workspace=ws,
+                      out=out)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+
+    # dominant kernel: the Hessian SYRK, timed with events on the library's stream
+    stream = torch.cuda.current_stream()
+    H = torch.empty((n, n), dtype=torch.float32, device=dev)
+    reps = max(3, args.steps)
+    P.hessian_accum(X, H=H)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        P.hessian_accum(X, H=H)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_h = ev0.elapsed_time(ev1) / 1e3 / reps
+    flops_h = float(n) * (n + 1) * N
+    achieved = flops_h / t_h / 1e12
+
+    # stage breakdown (same library calls, separately)
+    def timed(fn, r=3):
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(r):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / r
+    Lf, dead, _ = P.damp_cholesky(H, damp=cfg.damp)
+    s, z = P.grid_steps(W, grid)
+    t_chol = timed(lambda: P.damp_cholesky(H, damp=cfg.damp))
+    t_sweep = timed(lambda: P.babai_sweep(W, Lf, grid, scales=s, zeros=z, block=cfg.block))
+    flops_upd = float(m) * n * (n - cfg.block)
+
+    line = {
+        "metric": METRIC,
+        "value": m * n / dt,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 products, f32 accumulate/factor/sweep",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{cfg.name}: W {m}x{n} bf16, X {n}x{N} bf16 Student-t(4) "
+                               f"with {cfg.outliers} outlier channels x20; "
+                               f"{cfg.grid_kind} {cfg.bits}-bit group {cfg.group}, "
+                               f"block {cfg.block}, damp {cfg.damp}",
+                   "m": m, "n": n, "ntok": N, "layer_quantize_time_s": dt},
+        "roofline": {"bound": "mfma", "kernel": "hessian_accum (bf16 SYRK)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "stages_ms": {"hessian": t_h * 1e3, "damp_cholesky": t_chol, "sweep_and_update": t_sweep},
+        "update_mfma_util_upper": (flops_upd / (t_sweep / 1e3) / 1e12) / PEAK_F32_TFLOPS,
+        "loss": res0["loss"], "bound": res0["bound"],
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(lay, cfg, args.cpu_token_fraction)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,10 +9,11 @@
 //
 // Design (gfx950): right-looking blocked Cholesky with 64-column panels, in
 // place on an n x n working copy (float or double).  Per panel:
-//   chol_diag     one workgroup factors the 64x64 diagonal block in LDS
-//   chol_panel    one thread per row solves L_ik = A_ik L_kk^-T by forward
-//                 substitution (L_kk broadcast from LDS)
-//   chol_trailing the trailing lower triangle A_ij -= L_ik L_jk^T as 128x128
+//   chol_panel_step  every workgroup factors the 64x64 diagonal block in
+//                    registers (one wave, lane = row, readlane broadcasts);
+//                    workgroup 0 stores it, the others solve 64 panel rows
+//                    L_ik = A_ik L_kk^-T by forward substitution
+//   chol_trailing    the trailing lower triangle A_ij -= L_ik L_jk^T as 128x128
 //                 MFMA tiles (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64);
 //                 both operands are panel rows, contiguous along K.
 // A non-positive or non-finite pivot stops the factorization and records the
@@ -88,69 +89,74 @@ __global__ __launch_bounds__(256) void copy_damped(const float* __restrict__ H,
   A[(int64_t)i * n + j] = v;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void chol_diag(T* __restrict__ A, int n, int k0,
-                                                 DevFlags* flags,
-                                                 pwq_result* __restrict__ res) {
-  __shared__ T a[NB][NB + 1];
-  if (flags->info != 0) return;
-  const int nb = min(NB, n - k0);
-  const int tid = threadIdx.x;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    a[r][c] = (r < nb && c <= r) ? A[(int64_t)(k0 + r) * n + k0 + c] : (T)0;
-  }
-  __syncthreads();
-  for (int j = 0; j < nb; ++j) {
-    const T piv = a[j][j];
-    // every thread reads the same pivot: uniform decision
-    if (!(piv > (T)0) || !(piv < (T)INFINITY)) {
-      if (tid == 0) {
-        flags->info = k0 + j + 1;
-        res->info = k0 + j + 1;
-      }
-      return;
-    }
-    const T d = sqrt(piv);
-    const T inv = (T)1 / d;
-    __syncthreads();
-    if (tid < nb) {
-      if (tid == j) a[j][j] = d;
-      else if (tid > j) a[tid][j] *= inv;
-    }
-    __syncthreads();
-    // rank-1 update of the trailing lower part: a[r][c] -= a[r][j] a[c][j]
-    const int m = nb - j - 1;
-    for (int e = tid; e < m * m; e += 256) {
-      const int r = j + 1 + e / m, c = j + 1 + e % m;
-      if (c <= r) a[r][c] -= a[r][j] * a[c][j];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < nb * nb; e += 256) {
-    const int r = e / nb, c = e % nb;
-    if (c <= r) A[(int64_t)(k0 + r) * n + k0 + c] = a[r][c];
-  }
+__device__ __forceinline__ float readlane_t(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_t(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
+                                          (unsigned long long)(unsigned)lo));
 }
 
-// Rows below the diagonal block: x = a L_kk^-T by forward substitution,
-// column-oriented (x_j /= l_jj, then x_p -= x_j l_pj for p > j).  Only
-// launched while a full 64-column panel has rows below it.
+// One panel step.  Workgroup b (one wave) owns rows k0 + 64 b .. + 64; b = 0
+// is the diagonal block.  Every workgroup factors the 64 x 64 diagonal block
+// itself, in registers (lane = row, pivot column broadcast with readlane),
+// so no second launch or inter-workgroup wait is needed; the factors are
+// bitwise identical.  Workgroup 0 stores L_kk; the others solve their rows
+// x = a L_kk^-T by forward substitution (L_kk broadcast from LDS).
 template <typename T>
-__global__ __launch_bounds__(256) void chol_panel(T* __restrict__ A, int n, int k0,
-                                                  const DevFlags* flags) {
-  __shared__ T l[NB][NB + 1];
-  __shared__ T linv[NB];
+__global__ __launch_bounds__(64) void chol_panel_step(T* __restrict__ A, int n, int k0,
+                                                      DevFlags* flags,
+                                                      pwq_result* __restrict__ res) {
+  __shared__ T Ls[NB][NB + 1];
   if (flags->info != 0) return;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    l[r][c] = A[(int64_t)(k0 + r) * n + k0 + c];
+  const int lane = threadIdx.x;
+  const int nb = min(NB, n - k0);
+  T a[NB];
+  {
+    const T* src = A + (int64_t)(k0 + lane) * n + k0;
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+      a[c] = (lane < nb && c <= lane) ? src[c] : (c == lane ? (T)1 : (T)0);
   }
+  int fail_col = -1;
+  static_for_up<NB>([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    const T piv = readlane_t(a[j], j);
+    const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
+    if (bad && fail_col < 0) fail_col = j;
+    const T d = sqrt(piv);
+    const T inv = (T)1 / d;
+    a[j] = (lane == j) ? d : a[j] * inv;
+    static_for_up<NB - j - 1>([&](auto K) {
+      constexpr int k = j + 1 + decltype(K)::value;
+      const T lkj = readlane_t(a[j], k);
+      a[k] -= a[j] * lkj;
+    });
+  });
+  if (fail_col >= 0 && fail_col < nb) {
+    if (blockIdx.x == 0 && lane == 0) {
+      flags->info = k0 + fail_col + 1;
+      res->info = k0 + fail_col + 1;
+    }
+    return;
+  }
+  if (blockIdx.x == 0) {
+    if (lane < nb) {
+      T* dst = A + (int64_t)(k0 + lane) * n + k0;
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+        if (c <= lane && c < nb) dst[c] = a[c];
+    }
+    return;
+  }
+  // rows below: only reached while a full panel has rows below it (nb == NB)
+#pragma unroll
+  for (int c = 0; c < NB; ++c) Ls[lane][c] = a[c];
   __syncthreads();
-  if (tid < NB) linv[tid] = (T)1 / l[tid][tid];
-  __syncthreads();
-  const int i = k0 + NB + blockIdx.x * 256 + tid;
+  const int i = k0 + NB * blockIdx.x + lane;
   if (i >= n) return;
   T* row = A + (int64_t)i * n + k0;
   T x[NB];
@@ -158,9 +164,9 @@ __global__ __launch_bounds__(256) void chol_panel(T* __restrict__ A, int n, int 
   for (int j = 0; j < NB; ++j) x[j] = row[j];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    x[j] *= linv[j];
+    x[j] /= Ls[j][j];
 #pragma unroll
-    for (int p = j + 1; p < NB; ++p) x[p] -= x[j] * l[p][j];
+    for (int p = j + 1; p < NB; ++p) x[p] -= x[j] * Ls[p][j];
     // keep each column's LDS reads next to their use (bounded live ranges)
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(256) void chol_panel(T* __restrict__ A, int n, int 
 }
 
 // Trailing update of the lower triangle: A_ij -= P_i P_j^T, P = the panel
-// (columns k0..k0+nb of the rows below the diagonal block).
+// (columns k0..k0+64 of the rows below the diagonal block), 128x128 tiles.
 template <typename T>
 __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, int k0,
                                                      const DevFlags* flags) {
@@ -187,15 +193,19 @@ __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, i
     ti = r;
     tj = t - r * (r + 1) / 2;
   }
+  const bool diag = ti == tj;
   const int r0 = base + ti * TB, c0 = base + tj * TB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  for (int e = tid; e < TB * NB; e += 256) {
-    const int r = e / NB, k = e % NB;
-    As[r * LD + k] = (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
-    Bs[r * LD + k] = (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
-  }
+  tile_to_lds<T, TB, NB, 256, LD>(As, tid, [&](int r, int k) {
+    return (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
+  });
+  if (!diag)
+    tile_to_lds<T, TB, NB, 256, LD>(Bs, tid, [&](int r, int k) {
+      return (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
+    });
   __syncthreads();
+  const T* Bp = diag ? As : Bs;
   if constexpr (sizeof(T) == 4) {
     f32x16_t acc[2][2];
 #pragma unroll
@@ -209,13 +219,15 @@ __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, i
       const int ko = k + (lane >> 5);
       const float a0 = As[(wm * 64 + (lane & 31)) * LD + ko];
       const float a1 = As[(wm * 64 + 32 + (lane & 31)) * LD + ko];
-      const float b0 = Bs[(wn * 64 + (lane & 31)) * LD + ko];
-      const float b1 = Bs[(wn * 64 + 32 + (lane & 31)) * LD + ko];
+      const float b0 = Bp[(wn * 64 + (lane & 31)) * LD + ko];
+      const float b1 = Bp[(wn * 64 + 32 + (lane & 31)) * LD + ko];
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
+    // epilogue: all loads first, then the stores
+    float old[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -224,7 +236,17 @@ __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, i
         for (int r = 0; r < 16; ++r) {
           const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] -= acc[i][j][r];
+          old[i][j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0f;
+        }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = old[i][j][r] - acc[i][j][r];
         }
   } else {
     f64x4_t acc[4][4];
@@ -237,38 +259,48 @@ __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, i
 #pragma unroll 4
     for (int k = 0; k < NB; k += 4) {
       const int ko = k + (lane >> 4);
-      double a[4], b[4];
+      double av[4], bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = As[(wm * 64 + i * 16 + (lane & 15)) * LD + ko];
-        b[i] = Bs[(wn * 64 + i * 16 + (lane & 15)) * LD + ko];
+        av[i] = As[(wm * 64 + i * 16 + (lane & 15)) * LD + ko];
+        bv[i] = Bp[(wn * 64 + i * 16 + (lane & 15)) * LD + ko];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      double old[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] -= acc[i][j][r];
+          old[j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0;
         }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = old[j][r] - acc[i][j][r];
+        }
+    }
   }
 }
 
 template <typename T>
 hipError_t factor_impl(T* A, int n, DevFlags* flags, pwq_result* res, hipStream_t st) {
   for (int k0 = 0; k0 < n; k0 += NB) {
-    chol_diag<T><<<1, 256, 0, st>>>(A, n, k0, flags, res);
+    const int rows = n - k0;
+    chol_panel_step<T><<<(rows + NB - 1) / NB, 64, 0, st>>>(A, n, k0, flags, res);
     const int below = n - k0 - NB;
     if (below > 0) {
-      chol_panel<T><<<(below + 255) / 256, 256, 0, st>>>(A, n, k0, flags);
       const int nt = (below + 127) / 128;
       chol_trailing<T><<<nt * (nt + 1) / 2, 256, 0, st>>>(A, n, k0, flags);
     }

@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void syrk_reduce(
     const int lr = e >> 6, lc = e & 63;
     const int64_t off = (int64_t)(qr + lr) * BM + qc + lc;
     float s = 0.0f;
+#pragma unroll 8
     for (int sp = 0; sp < nsplit; ++sp) s += partial[((int64_t)sp * ntiles + tile) * (BM * BM) + off];
     const int gr = r0 + lr, gc = c0 + lc;
     float v = 2.0f * s;

@@ -100,7 +100,7 @@ void carve_sweep(Carver& c, int64_t m, int64_t n, int32_t block, int32_t prec, S
   w->alpha = c.take((size_t)n * elem(prec));
   w->acc = c.take((size_t)m * n * elem(prec));
   w->E = c.take((size_t)m * block * elem(prec));
-  w->partials = (double*)c.take(sweep_partials_bytes(m, n, block));
+  w->partials = (double*)c.take(sweep_partials_bytes(m, n, block, prec));
 }
 
 struct LayerWs {

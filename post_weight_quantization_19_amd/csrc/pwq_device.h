@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pwq {
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
@@ -45,6 +47,48 @@ __device__ __forceinline__ double row_bcast(double v) {
   int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), 0x150 + Q, 0xF, 0xF, false);
   return __builtin_bit_cast(double, (long long)(((unsigned long long)(unsigned)hi << 32) |
                                                 (unsigned long long)(unsigned)lo));
+}
+
+// Straight-line "loop" I = N-1, N-2, ..., 0 with I a compile-time constant in
+// the body (register arrays stay registers; DPP controls stay immediates).
+template <int I, typename F>
+__device__ __forceinline__ void static_for_down(F&& f) {
+  if constexpr (I >= 0) {
+    f(std::integral_constant<int, I>{});
+    static_for_down<I - 1>(f);
+  }
+}
+
+// Global -> LDS copy of a ROWS x COLS tile by NT threads: every load is issued
+// before the first LDS store, so the tile costs one memory latency, not one
+// per loop iteration.  get(r, c) returns the (masked) source element.
+template <typename T, int ROWS, int COLS, int NT, int LDD, typename Get>
+__device__ __forceinline__ void tile_to_lds(T* __restrict__ dst, int tid, Get&& get) {
+  constexpr int PER = (ROWS * COLS + NT - 1) / NT;
+  T v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + NT * i;
+    v[i] = (e < ROWS * COLS) ? get(e / COLS, e % COLS) : (T)0;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + NT * i;
+    if (e < ROWS * COLS) dst[(e / COLS) * LDD + e % COLS] = v[i];
+  }
+}
+
+// Empty register constraint: the value must exist in a VGPR at this point.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(double& v) { asm volatile("" : "+v"(v)); }
+
+// Straight-line "loop" I = 0 .. N-1 with I a compile-time constant.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for_up(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_up<N, I + 1>(f);
+  }
 }
 
 __device__ __forceinline__ float rint_t(float x) { return __builtin_rintf(x); }

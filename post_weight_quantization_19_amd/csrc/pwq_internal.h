@@ -55,7 +55,7 @@ struct SweepLaunch {
   const DevFlags* flags;
 };
 
-size_t sweep_partials_bytes(int64_t m, int64_t n, int32_t block);
+size_t sweep_partials_bytes(int64_t m, int64_t n, int32_t block, int32_t prec);
 hipError_t launch_sweep(const SweepLaunch& sl, hipStream_t st);
 
 hipError_t launch_order(int32_t order_kind, const float* H, int64_t n, const int32_t* perm_in,

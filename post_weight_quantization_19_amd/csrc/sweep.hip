@@ -118,52 +118,41 @@ struct SweepArgs {
   const DevFlags* flags;
 };
 
-template <int Q, typename T>
-__device__ __forceinline__ T bcast_q(T v) { return row_bcast<Q>(v); }
-
-template <typename T>
-__device__ __forceinline__ T bcast(T v, int q) {
-  switch (q) {
-    case 0: return bcast_q<0>(v);   case 1: return bcast_q<1>(v);
-    case 2: return bcast_q<2>(v);   case 3: return bcast_q<3>(v);
-    case 4: return bcast_q<4>(v);   case 5: return bcast_q<5>(v);
-    case 6: return bcast_q<6>(v);   case 7: return bcast_q<7>(v);
-    case 8: return bcast_q<8>(v);   case 9: return bcast_q<9>(v);
-    case 10: return bcast_q<10>(v); case 11: return bcast_q<11>(v);
-    case 12: return bcast_q<12>(v); case 13: return bcast_q<13>(v);
-    case 14: return bcast_q<14>(v); default: return bcast_q<15>(v);
-  }
-}
-
+// One sub-block of Bi columns [j0, j0 + Bi) of every row.  E (leading
+// dimension ldE) receives the sub-block's errors at column offset e_off.
 template <typename T, int B>
-__global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int blk, int first) {
+__global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int ldE, int e_off,
+                                                  int first, int part) {
   constexpr int P = 16, S = B / P;
-  constexpr int CH0 = 16384 / (B * (int)sizeof(T));
-  constexpr int CH = CH0 < 8 ? 8 : (CH0 > 32 ? 32 : CH0);
+  // rows of L staged per LDS pass (64 KB of the CU's 160 KB)
+  constexpr int CH0 = 65536 / (B * (int)sizeof(T));
+  constexpr int CH = CH0 < 8 ? 8 : (CH0 > B ? B : CH0);
   static_assert(B % CH == 0, "chunk must divide block");
   __shared__ T Ls[CH * B];
   __shared__ double red[4][4];
-  if (a.flags->info != 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 15;
   const int row = blockIdx.x * 16 + wave * 4 + (lane >> 4);
   const bool rok = row < a.m;
   const int n = a.n;
-  const int j0 = blk * B;
 
-  T acc[S], av[S], bv[S], sv[S], wv[S];
+  T acc[S], av[S], bv[S], sv[S], wv[S], dv[S];
+  int ocv[S], zpv[S];
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const int col = j0 + q + P * t;
     const bool ok = rok && col < n;
-    T w = (T)0, s = (T)1, il = (T)0, ac = (T)0;
+    T w = (T)0, s = (T)1, il = (T)0, ac = (T)0, d = (T)0;
+    int oc = -1, zp = 0;
     if (ok) {
-      const int oc = a.colmap ? a.colmap[col] : col;
+      oc = a.colmap ? a.colmap[col] : col;
       w = load_w<T>(a.W, a.wdtype, (int64_t)row * a.ldw + oc);
       if (a.dead && a.dead[oc]) w = (T)0;
       s = a.alpha ? a.alpha[col] : (T)a.scales[(int64_t)row * a.ng + oc / a.G];
+      if (a.zeros) zp = a.zeros[(int64_t)row * a.ng + oc / a.G];
       il = a.invd[col];
+      d = a.dg[col];
       if (!first) ac = a.acc[(int64_t)row * n + col];
     }
     // true (correctly rounded) quotients: with no feedback yet the coordinate
@@ -173,55 +162,72 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int blk, int 
     bv[t] = w / s;
     sv[t] = s;
     wv[t] = w;
+    dv[t] = d;
+    ocv[t] = oc;
+    zpv[t] = zp;
   }
+  int32_t* codes_row = a.codes + (int64_t)(rok ? row : 0) * n;
+  T* e_row = a.E + (int64_t)(rok ? row : 0) * ldE + e_off;
 
   double loss_d = 0.0, bound = 0.0, dsq = 0.0;
-
+  T lc[S], ln[S];  // coefficients l_kj of the current / next column
 #pragma unroll
-  for (int kk = B - 1; kk >= 0; --kk) {
-    if (kk % CH == CH - 1) {
+  for (int t = 0; t < S; ++t) lc[t] = ln[t] = (T)0;
+
+  static_for_down<B - 1>([&](auto KK) {
+    constexpr int kk = decltype(KK)::value;
+    constexpr int t = kk / P, qk = kk % P;
+    if constexpr (kk % CH == CH - 1) {
       // stage rows j0+kk-CH+1 .. j0+kk of L (strictly-lower part of the block)
-      const int cb = kk - CH + 1;
+      constexpr int cb = kk - CH + 1;
       __syncthreads();
-      for (int e = tid; e < CH * B; e += 256) {
-        const int rr = e / B, i = e % B;
+      tile_to_lds<T, CH, B, 256, B>(Ls, tid, [&](int rr, int i) {
         const int kr = cb + rr;
-        T v = (T)0;
-        if (i < kr && j0 + kr < n) v = a.L[(int64_t)(j0 + kr) * n + j0 + i];
-        Ls[e] = v;
-      }
+        return (i < kr && j0 + kr < n) ? a.L[(int64_t)(j0 + kr) * n + j0 + i] : (T)0;
+      });
       __syncthreads();
+#pragma unroll
+      for (int t2 = 0; t2 <= t; ++t2) lc[t2] = Ls[(kk % CH) * B + q + P * t2];
     }
-    const int t = kk / P, qk = kk % P;
+    // prefetch the next column's coefficients when they are already staged
+    if constexpr (kk > 0 && (kk - 1) % CH != CH - 1) {
+      constexpr int tn = (kk - 1) / P;
+#pragma unroll
+      for (int t2 = 0; t2 <= tn; ++t2) ln[t2] = Ls[((kk - 1) % CH) * B + q + P * t2];
+    }
     const T c = acc[t] * av[t] + bv[t];
     const T z = rint_t(c);
     const T e = wv[t] - sv[t] * z;
-    const T eb = bcast(e, qk);
-    const T* lrow = &Ls[(kk % CH) * B + q];
+    const T eb = row_bcast<qk>(e);
 #pragma unroll
-    for (int t2 = 0; t2 <= t; ++t2) acc[t2] += eb * lrow[P * t2];
-    if (qk == 0) {
+    for (int t2 = 0; t2 <= t; ++t2) {
+      acc[t2] += eb * lc[t2];
+      // materialise the update here: without this the compiler sinks the
+      // updates toward their distant use and keeps every broadcast alive
+      pin(acc[t2]);
+    }
+    if constexpr (qk == 0) {
       // every lane's slot t is final now: record its decision
-      const int col = j0 + q + P * t;
       const T cc = acc[t] * av[t] + bv[t];
       const T zz = rint_t(cc);
       const T rho = cc - zz;
       const T ee = wv[t] - sv[t] * zz;
-      if (rok && col < n) {
-        const int oc = a.colmap ? a.colmap[col] : col;
-        int32_t code = (int32_t)zz;
-        if (a.zeros) code += a.zeros[(int64_t)row * a.ng + oc / a.G];
-        a.codes[(int64_t)row * n + oc] = code;
-        a.E[(int64_t)row * B + q + P * t] = ee;
-        const double sl = (double)sv[t] * (double)a.dg[col];
+      if (ocv[t] >= 0) {
+        codes_row[ocv[t]] = (int32_t)zz + zpv[t];
+        e_row[q + P * t] = ee;
+        const double sl = (double)sv[t] * (double)dv[t];
         loss_d += (double)rho * (double)rho * sl * sl;
         bound += sl * sl;
         dsq += (double)ee * (double)ee;
       } else if (rok) {
-        a.E[(int64_t)row * B + q + P * t] = (T)0;
+        e_row[q + P * t] = (T)0;
       }
     }
-  }
+#pragma unroll
+    for (int t2 = 0; t2 < S; ++t2) lc[t2] = ln[t2];
+    // one column per scheduling region: bounded live ranges
+    __builtin_amdgcn_sched_barrier(0);
+  });
 
   loss_d = wave_sum(loss_d);
   bound = wave_sum(bound);
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int blk, int 
   }
   __syncthreads();
   if (tid == 0) {
-    double* p = a.partials + ((int64_t)blk * gridDim.x + blockIdx.x) * 4;
+    double* p = a.partials + ((int64_t)part * gridDim.x + blockIdx.x) * 4;
     p[0] = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
     p[1] = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
     p[2] = (red[0][2] + red[1][2]) + (red[2][2] + red[3][2]);
@@ -242,19 +248,46 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int blk, int 
 }
 
 // ------------------------------------------------------------ lazy update
-// acc[r, c] (+)= sum_{k < kb} E[r, k] * L[j0 + k, c]   for r < m, c < j0.
+// acc[r, c] (+)= sum_{k < kb} E[r, e_off + k] * L[k_lo + k, c]
+//   for r < m and c in [c_lo, j0); "first" stores instead of adding.
+// 128 x 128 output tiles, K in chunks of 32 staged through LDS; the next
+// chunk's global loads are in flight while the current chunk's MFMAs run.
 template <typename T>
-__global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int B, int kb,
-                                                   const T* __restrict__ L, int n, int j0,
-                                                   int m, T* __restrict__ acc, int first,
+__global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int B, int e_off,
+                                                   int kb, const T* __restrict__ L, int n,
+                                                   int k_lo, int c_lo, int j0, int m,
+                                                   T* __restrict__ acc, int first,
                                                    const DevFlags* flags) {
   constexpr int TM = 128, KC = 32, LDA = KC + 1, LDB = TM + 1;
+  constexpr int PE = TM * KC / 256;   // elements per thread per operand
   __shared__ T Es[TM * LDA];
   __shared__ T Lt[KC * LDB];
-  if (flags->info != 0) return;
-  const int c0 = blockIdx.x * TM, r0 = blockIdx.y * TM;
+  (void)flags;
+  E += e_off;
+  const int c0 = c_lo + blockIdx.x * TM, r0 = blockIdx.y * TM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  T re[PE], rl[PE];
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e / KC, k = e % KC;          // E tile [TM][KC]
+      re[i] = (r0 + r < m && kc + k < kb) ? E[(int64_t)(r0 + r) * B + kc + k] : (T)0;
+      const int kr = e / TM, cc = e % TM;        // L tile [KC][TM]
+      rl[i] = (kc + kr < kb && c0 + cc < j0) ? L[(int64_t)(k_lo + kc + kr) * n + c0 + cc]
+                                             : (T)0;
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int e = tid + 256 * i;
+      Es[(e / KC) * LDA + e % KC] = re[i];
+      Lt[(e / TM) * LDB + e % TM] = rl[i];
+    }
+  };
+  gload(0);
 
   if constexpr (sizeof(T) == 4) {
     f32x16_t cc[2][2];
@@ -266,14 +299,9 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
         for (int r = 0; r < 16; ++r) cc[i][j][r] = 0.0f;
     for (int kc = 0; kc < kb; kc += KC) {
       __syncthreads();
-      for (int e = tid; e < TM * KC; e += 256) {
-        const int r = e / KC, k = e % KC;
-        Es[r * LDA + k] = (r0 + r < m && kc + k < kb) ? E[(int64_t)(r0 + r) * B + kc + k] : 0.0f;
-        const int kr = e / TM, cc_ = e % TM;
-        Lt[kr * LDB + cc_] = (kc + kr < kb && c0 + cc_ < j0)
-                                 ? L[(int64_t)(j0 + kc + kr) * n + c0 + cc_] : 0.0f;
-      }
+      lstore();
       __syncthreads();
+      if (kc + KC < kb) gload(kc + KC);
 #pragma unroll
       for (int k = 0; k < KC; k += 2) {
         const int ko = k + (lane >> 5);
@@ -287,6 +315,7 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
         cc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, cc[1][1], 0, 0, 0);
       }
     }
+    float old[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -295,10 +324,17 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
         for (int r = 0; r < 16; ++r) {
           const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          if (gr < m && gc < j0) {
-            T* p = acc + (int64_t)gr * n + gc;
-            *p = first ? cc[i][j][r] : *p + cc[i][j][r];
-          }
+          old[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
+        }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = old[i][j][r] + cc[i][j][r];
         }
   } else {
     f64x4_t cc[4][4];
@@ -310,14 +346,9 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
         for (int r = 0; r < 4; ++r) cc[i][j][r] = 0.0;
     for (int kc = 0; kc < kb; kc += KC) {
       __syncthreads();
-      for (int e = tid; e < TM * KC; e += 256) {
-        const int r = e / KC, k = e % KC;
-        Es[r * LDA + k] = (r0 + r < m && kc + k < kb) ? E[(int64_t)(r0 + r) * B + kc + k] : 0.0;
-        const int kr = e / TM, cc_ = e % TM;
-        Lt[kr * LDB + cc_] = (kc + kr < kb && c0 + cc_ < j0)
-                                 ? L[(int64_t)(j0 + kc + kr) * n + c0 + cc_] : 0.0;
-      }
+      lstore();
       __syncthreads();
+      if (kc + KC < kb) gload(kc + KC);
 #pragma unroll 2
       for (int k = 0; k < KC; k += 4) {
         const int ko = k + (lane >> 4);
@@ -335,18 +366,25 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      double old[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          if (gr < m && gc < j0) {
-            T* p = acc + (int64_t)gr * n + gc;
-            *p = first ? cc[i][j][r] : *p + cc[i][j][r];
-          }
+          old[j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0;
         }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = old[j][r] + cc[i][j][r];
+        }
+    }
   }
 }
 
@@ -358,10 +396,12 @@ __global__ __launch_bounds__(256) void finalize(const double* __restrict__ parti
   __shared__ double s[3][256];
   if (flags->info != 0) return;
   double a = 0.0, b = 0.0, c = 0.0;
+#pragma unroll 8
   for (int i = threadIdx.x; i < count; i += 256) {
-    a += partials[(int64_t)i * 4 + 0];
-    b += partials[(int64_t)i * 4 + 1];
-    c += partials[(int64_t)i * 4 + 2];
+    const double4 v = *(const double4*)(partials + (int64_t)i * 4);
+    a += v.x;
+    b += v.y;
+    c += v.z;
   }
   s[0][threadIdx.x] = a;
   s[1][threadIdx.x] = b;
@@ -383,7 +423,25 @@ __global__ __launch_bounds__(256) void finalize(const double* __restrict__ parti
   }
 }
 
-template <typename T, int B>
+// Columns swept per kernel launch: a lazy block of B columns is swept in
+// sub-blocks of Bi, with a small MFMA update inside the block between them
+// (the same arithmetic regrouped; keeps the per-lane state in registers).
+int inner_block(int32_t prec, int32_t block) {
+  const int cap = 128;
+  return block < cap ? block : cap;
+}
+
+int64_t sweep_parts(int64_t n, int32_t block, int32_t prec) {
+  const int bi = inner_block(prec, block);
+  int64_t parts = 0;
+  for (int64_t jb0 = 0; jb0 < n; jb0 += block) {
+    const int64_t w = (n - jb0 < block) ? n - jb0 : block;
+    parts += (w + bi - 1) / bi;
+  }
+  return parts;
+}
+
+template <typename T, int Bi>
 hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
   SweepArgs<T> a;
   a.W = sl.W; a.wdtype = sl.wdtype; a.ldw = sl.ldw; a.m = (int)sl.m; a.n = (int)sl.n;
@@ -395,22 +453,35 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
   diag_prep<T><<<(unsigned)((sl.n + 255) / 256), 256, 0, st>>>(
       (const T*)sl.L, (int)sl.n, sl.colspacing, sl.c, sl.colmap, (T*)sl.invd, (T*)sl.dg,
       (T*)sl.alpha, sl.scales_out, sl.flags);
-  const int nblk = (int)((sl.n + B - 1) / B);
-  const unsigned nwg = (unsigned)((sl.m + 15) / 16);
+  const int n = (int)sl.n, m = (int)sl.m, B = sl.block;
+  const int nblk = (n + B - 1) / B;
+  const unsigned nwg = (unsigned)((m + 15) / 16);
+  const unsigned mt = (unsigned)((m + 127) / 128);
+  int part = 0;
   for (int b = nblk - 1; b >= 0 && nwg > 0; --b) {
-    const int first = b == nblk - 1;
-    sweep_block<T, B><<<nwg, 256, 0, st>>>(a, b, first);
-    const int j0 = b * B;
-    if (j0 > 0) {
-      const int kb = (int)(sl.n - j0 < B ? sl.n - j0 : B);
-      dim3 g((unsigned)((j0 + 127) / 128), (unsigned)((sl.m + 127) / 128));
-      lazy_update<T><<<g, 256, 0, st>>>((const T*)sl.E, B, kb, (const T*)sl.L, (int)sl.n, j0,
-                                        (int)sl.m, (T*)sl.acc, first, sl.flags);
+    const int jb0 = b * B, jb1 = (n < jb0 + B) ? n : jb0 + B;
+    const int nsub = (jb1 - jb0 + Bi - 1) / Bi;
+    for (int s = nsub - 1; s >= 0; --s) {
+      const int js0 = jb0 + s * Bi;
+      const int first_sub = (b == nblk - 1) && (s == nsub - 1);
+      sweep_block<T, Bi><<<nwg, 256, 0, st>>>(a, js0, B, js0 - jb0, first_sub, part++);
+      if (s > 0) {
+        // the sub-block's errors reach the open columns of its own block
+        const int kb = (jb1 - js0 < Bi) ? jb1 - js0 : Bi;
+        dim3 g((unsigned)((js0 - jb0 + 127) / 128), mt);
+        lazy_update<T><<<g, 256, 0, st>>>((const T*)sl.E, B, js0 - jb0, kb, (const T*)sl.L, n,
+                                          js0, jb0, js0, m, (T*)sl.acc, first_sub, sl.flags);
+      }
+    }
+    if (jb0 > 0) {
+      dim3 g((unsigned)((jb0 + 127) / 128), mt);
+      lazy_update<T><<<g, 256, 0, st>>>((const T*)sl.E, B, 0, jb1 - jb0, (const T*)sl.L, n, jb0,
+                                        0, jb0, m, (T*)sl.acc, b == nblk - 1, sl.flags);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  finalize<<<1, 256, 0, st>>>(sl.partials, nblk * (int)nwg, sl.result, sl.flags);
+  finalize<<<1, 256, 0, st>>>(sl.partials, part * (int)nwg, sl.result, sl.flags);
   return hipGetLastError();
 }
 
@@ -425,26 +496,24 @@ hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n
   return hipGetLastError();
 }
 
-size_t sweep_partials_bytes(int64_t m, int64_t n, int32_t block) {
-  const int64_t nblk = (n + block - 1) / block;
+size_t sweep_partials_bytes(int64_t m, int64_t n, int32_t block, int32_t prec) {
   const int64_t nwg = (m + 15) / 16;
-  return (size_t)(nblk * nwg * 4) * sizeof(double);
+  return (size_t)(sweep_parts(n, block, prec) * nwg * 4) * sizeof(double);
 }
 
 hipError_t launch_sweep(const SweepLaunch& sl, hipStream_t st) {
+  const int bi = inner_block(sl.prec, sl.block);
   if (sl.prec == PWQ_F64) {
-    switch (sl.block) {
+    switch (bi) {
       case 32: return run_sweep<double, 32>(sl, st);
       case 64: return run_sweep<double, 64>(sl, st);
       case 128: return run_sweep<double, 128>(sl, st);
-      case 256: return run_sweep<double, 256>(sl, st);
     }
   } else {
-    switch (sl.block) {
+    switch (bi) {
       case 32: return run_sweep<float, 32>(sl, st);
       case 64: return run_sweep<float, 64>(sl, st);
       case 128: return run_sweep<float, 128>(sl, st);
-      case 256: return run_sweep<float, 256>(sl, st);
     }
   }
   return hipErrorInvalidValue;
