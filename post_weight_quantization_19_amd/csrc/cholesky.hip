@@ -9,10 +9,10 @@
 //
 // Design (gfx950): right-looking blocked Cholesky with 64-column panels, in
 // place on an n x n working copy (float or double).  Per panel:
-//   chol_panel_step  every workgroup factors the 64x64 diagonal block in
-//                    registers (one wave, lane = row, readlane broadcasts);
-//                    workgroup 0 stores it, the others solve 64 panel rows
-//                    L_ik = A_ik L_kk^-T by forward substitution
+//   chol_panel_step  every workgroup factors the tall panel made of the
+//                    64x64 diagonal block and its own 64 panel rows (4 waves,
+//                    lane = row, one LDS broadcast + barrier per column), so
+//                    L_kk and L_ik = A_ik L_kk^-T come out of one pass
 //   chol_trailing    the trailing lower triangle A_ij -= L_ik L_jk^T as 128x128
 //                 MFMA tiles (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64);
 //                 both operands are panel rows, contiguous along K.
@@ -100,78 +100,121 @@ __device__ __forceinline__ double readlane_t(double v, int l) {
                                           (unsigned long long)(unsigned)lo));
 }
 
-// One panel step.  Workgroup b (one wave) owns rows k0 + 64 b .. + 64; b = 0
-// is the diagonal block.  Every workgroup factors the 64 x 64 diagonal block
-// itself, in registers (lane = row, pivot column broadcast with readlane),
-// so no second launch or inter-workgroup wait is needed; the factors are
-// bitwise identical.  Workgroup 0 stores L_kk; the others solve their rows
-// x = a L_kk^-T by forward substitution (L_kk broadcast from LDS).
+// Pivot square root and reciprocal: hardware ops for float (about 1 ulp; the
+// factor's own rounding error is larger), correctly rounded for double.
+__device__ __forceinline__ void pivot_ops(float piv, float& d, float& inv) {
+  d = __builtin_amdgcn_sqrtf(piv);
+  inv = __builtin_amdgcn_rcpf(d);
+}
+__device__ __forceinline__ void pivot_ops(double piv, double& d, double& inv) {
+  d = sqrt(piv);
+  inv = 1.0 / d;
+}
+
+// One panel step on the tall panel [A_kk; A_bk]: workgroup b factors the
+// 64x64 diagonal block (slot 0) together with its own 64 panel rows
+// k0 + 64 b .. (slot 1, b >= 1) in a single right-looking pass, so the panel
+// solve L_bk = A_bk L_kk^-T needs no separate substitution.  Every
+// workgroup repeats the diagonal factorization (bitwise identical results);
+// workgroup 0 stores L_kk.  Lane = row; wave w keeps columns 16w..16w+15 of
+// both slots in registers.  Columns go in groups of 4: the owner wave
+// factors the group in registers (pivot rows broadcast with readlane) and
+// publishes it in LDS; after one barrier every wave applies the rank-4
+// update to its later columns.  The group buffer is double buffered, so one
+// barrier per group suffices.
 template <typename T>
-__global__ __launch_bounds__(64) void chol_panel_step(T* __restrict__ A, int n, int k0,
+__global__ __launch_bounds__(256) void chol_panel_step(T* __restrict__ A, int n, int k0,
                                                       DevFlags* flags,
                                                       pwq_result* __restrict__ res) {
-  __shared__ T Ls[NB][NB + 1];
+  __shared__ __attribute__((aligned(16))) T gbuf[2][2][4][NB];
+  __shared__ int fail_col;
   if (flags->info != 0) return;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = min(NB, n - k0);
-  T a[NB];
+  const int row1 = k0 + NB * blockIdx.x + lane;     // slot-1 row (blockIdx.x >= 1)
+  const bool has1 = blockIdx.x > 0 && row1 < n;
+  T d0[16], d1[16];
   {
-    const T* src = A + (int64_t)(k0 + lane) * n + k0;
+    const T* src0 = A + (int64_t)(k0 + min(lane, nb - 1)) * n + k0 + 16 * wave;
+    const T* src1 = A + (int64_t)(has1 ? row1 : k0) * n + k0 + 16 * wave;
 #pragma unroll
-    for (int c = 0; c < NB; ++c)
-      a[c] = (lane < nb && c <= lane) ? src[c] : (c == lane ? (T)1 : (T)0);
+    for (int c = 0; c < 16; ++c) {
+      const int col = 16 * wave + c;
+      d0[c] = (lane < nb) ? (col <= lane ? src0[c] : (T)0) : (col == lane ? (T)1 : (T)0);
+      d1[c] = has1 ? src1[c] : (T)0;
+    }
   }
-  int fail_col = -1;
-  static_for_up<NB>([&](auto J) {
-    constexpr int j = decltype(J)::value;
-    const T piv = readlane_t(a[j], j);
-    const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
-    if (bad && fail_col < 0) fail_col = j;
-    const T d = sqrt(piv);
-    const T inv = (T)1 / d;
-    a[j] = (lane == j) ? d : a[j] * inv;
-    static_for_up<NB - j - 1>([&](auto K) {
-      constexpr int k = j + 1 + decltype(K)::value;
-      const T lkj = readlane_t(a[j], k);
-      a[k] -= a[j] * lkj;
-    });
+  if (tid == 0) fail_col = -1;
+  __syncthreads();
+  static_for_up<NB / 4>([&](auto G) {
+    constexpr int g = decltype(G)::value;
+    constexpr int j0 = 4 * g, wj = j0 / 16, jl0 = j0 % 16;
+    if (wave == wj) {
+      static_for_up<4>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        constexpr int j = j0 + u, jl = jl0 + u;
+        const T piv = readlane_t(d0[jl], j);
+        const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
+        if (bad && lane == 0 && fail_col < 0) fail_col = j;
+        T d, inv;
+        pivot_ops(piv, d, inv);
+        d0[jl] = (lane == j) ? d : d0[jl] * inv;
+        d1[jl] = d1[jl] * inv;
+        static_for_up<3 - u>([&](auto V) {
+          constexpr int k = j + 1 + decltype(V)::value;
+          const T lkj = readlane_t(d0[jl], k);
+          d0[jl0 + (k - j0)] -= d0[jl] * lkj;
+          d1[jl0 + (k - j0)] -= d1[jl] * lkj;
+        });
+        gbuf[g & 1][0][u][lane] = d0[jl];
+        gbuf[g & 1][1][u][lane] = d1[jl];
+      });
+    }
+    __syncthreads();
+    if (wave >= wj) {
+      T li0[4], li1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        li0[u] = gbuf[g & 1][0][u][lane];
+        li1[u] = gbuf[g & 1][1][u][lane];
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int k = 16 * wave + c;
+        if (k >= j0 + 4) {                      // uniform per wave
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const T lkj = gbuf[g & 1][0][u][k];
+            d0[c] -= li0[u] * lkj;
+            d1[c] -= li1[u] * lkj;
+          }
+        }
+      }
+    }
   });
-  if (fail_col >= 0 && fail_col < nb) {
-    if (blockIdx.x == 0 && lane == 0) {
-      flags->info = k0 + fail_col + 1;
-      res->info = k0 + fail_col + 1;
+  __syncthreads();
+  const int fc = fail_col;
+  if (fc >= 0 && fc < nb) {
+    if (blockIdx.x == 0 && tid == 0) {
+      flags->info = k0 + fc + 1;
+      res->info = k0 + fc + 1;
     }
     return;
   }
   if (blockIdx.x == 0) {
     if (lane < nb) {
-      T* dst = A + (int64_t)(k0 + lane) * n + k0;
+      T* dst = A + (int64_t)(k0 + lane) * n + k0 + 16 * wave;
 #pragma unroll
-      for (int c = 0; c < NB; ++c)
-        if (c <= lane && c < nb) dst[c] = a[c];
+      for (int c = 0; c < 16; ++c) {
+        const int col = 16 * wave + c;
+        if (col <= lane && col < nb) dst[c] = d0[c];
+      }
     }
-    return;
+  } else if (has1) {
+    T* dst = A + (int64_t)row1 * n + k0 + 16 * wave;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) dst[c] = d1[c];
   }
-  // rows below: only reached while a full panel has rows below it (nb == NB)
-#pragma unroll
-  for (int c = 0; c < NB; ++c) Ls[lane][c] = a[c];
-  __syncthreads();
-  const int i = k0 + NB * blockIdx.x + lane;
-  if (i >= n) return;
-  T* row = A + (int64_t)i * n + k0;
-  T x[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) x[j] = row[j];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    x[j] /= Ls[j][j];
-#pragma unroll
-    for (int p = j + 1; p < NB; ++p) x[p] -= x[j] * Ls[p][j];
-    // keep each column's LDS reads next to their use (bounded live ranges)
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) row[j] = x[j];
 }
 
 // Trailing update of the lower triangle: A_ij -= P_i P_j^T, P = the panel
@@ -298,7 +341,7 @@ template <typename T>
 hipError_t factor_impl(T* A, int n, DevFlags* flags, pwq_result* res, hipStream_t st) {
   for (int k0 = 0; k0 < n; k0 += NB) {
     const int rows = n - k0;
-    chol_panel_step<T><<<(rows + NB - 1) / NB, 64, 0, st>>>(A, n, k0, flags, res);
+    chol_panel_step<T><<<(rows + NB - 1) / NB, 256, 0, st>>>(A, n, k0, flags, res);
     const int below = n - k0 - NB;
     if (below > 0) {
       const int nt = (below + 127) / 128;

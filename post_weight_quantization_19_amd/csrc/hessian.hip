@@ -39,13 +39,45 @@ template <> struct SyrkCfg<float> {
   static constexpr int VEC = 4;
 };
 
-__device__ __forceinline__ void tile_coords(int t, int& ti, int& tj) {
-  // t enumerates the lower-triangular tiles row by row: (0,0),(1,0),(1,1),...
+__device__ __forceinline__ void tri_index(int t, int& a, int& b) {
+  // t enumerates a lower triangle row by row: (0,0),(1,0),(1,1),(2,0),...
   int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while ((r + 1) * (r + 2) / 2 <= t) ++r;
   while (r * (r + 1) / 2 > t) --r;
-  ti = r;
-  tj = t - r * (r + 1) / 2;
+  a = r;
+  b = t - r * (r + 1) / 2;
+}
+
+// Tile order: lower-triangular 8x8 super-blocks of 128x128 tiles, each
+// super-block's tiles consecutive.  Workgroups that run together on one XCD
+// take consecutive positions, so they share at most 16 row panels of X in
+// that XCD's L2.
+constexpr int SUPER = 8;
+__device__ __forceinline__ void tile_coords(int pos, int nt, int& ti, int& tj) {
+  const int ns = (nt + SUPER - 1) / SUPER;
+  int base = 0;
+  for (int I = 0; I < ns; ++I) {
+    const int rows = min(SUPER, nt - SUPER * I);
+    for (int J = 0; J <= I; ++J) {
+      const int cols = min(SUPER, nt - SUPER * J);
+      const int cnt = (I == J) ? rows * (rows + 1) / 2 : rows * cols;
+      if (pos < base + cnt) {
+        const int local = pos - base;
+        int a, b;
+        if (I == J) {
+          tri_index(local, a, b);
+        } else {
+          a = local / cols;
+          b = local % cols;
+        }
+        ti = SUPER * I + a;
+        tj = SUPER * J + b;
+        return;
+      }
+      base += cnt;
+    }
+  }
+  ti = tj = 0;  // not reached for pos < nt (nt + 1) / 2
 }
 
 // One 16-byte vector of X (or fewer elements at a ragged token tail).
@@ -65,11 +97,14 @@ __device__ __forceinline__ uint4 load_vec(const XT* X, int64_t ldx, int row,
   return v;
 }
 
+// Work item = (split, tile position), split-major.  Workgroup w runs on XCD
+// w % 8 (round-robin dispatch); XCD x takes items [x Q, (x+1) Q), so with 8
+// splits each XCD owns one token range of every tile.
 template <typename XT>
 __global__ __launch_bounds__(NT) void syrk_tiles(
     const XT* __restrict__ X, int n, int64_t ntok, int64_t ldx, int64_t kps,
     int aligned, float* __restrict__ partial, float* __restrict__ H,
-    int direct, int accumulate) {
+    int direct, int accumulate, int ntiles, int nsplit, int per_xcd) {
   constexpr int BK = SyrkCfg<XT>::BK, PAD = SyrkCfg<XT>::PAD,
                 VEC = SyrkCfg<XT>::VEC, LD = BK + PAD;
   constexpr int VPR = BK / VEC;                 // vectors per tile row
@@ -77,9 +112,12 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
   __shared__ __attribute__((aligned(16))) XT As[2][BM * LD];
   __shared__ __attribute__((aligned(16))) XT Bs[2][BM * LD];
 
-  const int tile = blockIdx.x, split = blockIdx.y;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= ntiles * nsplit) return;
+  const int split = item / ntiles, tile = item % ntiles;
+  const int nt = (n + BM - 1) / BM;
   int ti, tj;
-  tile_coords(tile, ti, tj);
+  tile_coords(tile, nt, ti, tj);
   const bool diag = ti == tj;
   const int r0 = ti * BM, c0 = tj * BM;
   const int64_t kbeg = (int64_t)split * kps;
@@ -159,7 +197,7 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
   }
 
   if (!direct) {
-    float* P = partial + ((int64_t)split * gridDim.x + tile) * (BM * BM);
+    float* P = partial + ((int64_t)split * ntiles + tile) * (BM * BM);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -190,25 +228,201 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
       }
 }
 
+// Large-tile variant for bf16 X: 256x256 output tiles computed by 8 waves,
+// each 64x128 (2x4 v_mfma_f32_32x32x16_bf16 accumulators), two waves per
+// SIMD so one wave's LDS waits hide behind the other's MFMAs; 32 tokens per
+// stage.  Twice the arithmetic per byte moved from L2 of a 128x128 tile.
+// X streams HBM -> LDS with global_load_lds_dwordx4 (no register staging)
+// through a ring of 5 stages (the whole 160 KB LDS), issued 4 stages ahead,
+// so about 2 us of load latency is covered.  LDS rows are 64 B (four 16-byte
+// chunks) with the chunk index XOR-swizzled by bits 2..3 of the row: 16
+// consecutive rows read at one logical chunk hit 16 distinct bank groups.
+constexpr int BL = 256;        // large tile edge
+constexpr int BKL = 32;        // tokens per stage
+constexpr int NSLOT = 5;       // LDS ring slots
+constexpr int AHEAD = 4;       // stages in flight ahead of the one computed
+constexpr int NTL = 512;       // threads (8 waves)
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= v and lgkmcnt = 0.
+constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
+
+__global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
+    const uint16_t* __restrict__ X, int n, int64_t ntok, int64_t ldx, int64_t kps,
+    int aligned, float* __restrict__ partial, float* __restrict__ H, int direct,
+    int accumulate, int ntiles, int nsplit, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint4 Ls[NSLOT][2][BL * 4];
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= ntiles * nsplit) return;
+  const int split = item / ntiles, tile = item % ntiles;
+  const int nt = (n + BL - 1) / BL;
+  int ti, tj;
+  tile_coords(tile, nt, ti, tj);
+  const bool diag = ti == tj;
+  const int r0 = ti * BL, c0 = tj * BL;
+  const int64_t kbeg = (int64_t)split * kps;
+  const int64_t kend = min(ntok, kbeg + kps);
+  const int nstage = (int)((kend - kbeg + BKL - 1) / BKL);
+  const int nfull = (int)((kend - kbeg) / BKL);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;      // rows 64 wm, cols 128 wn
+  // waves entirely above the diagonal of a diagonal tile have nothing to do
+  const bool skip = diag && (64 * wm + 63 < 128 * wn);
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // DMA: each stage and panel is 16 wave-chunks of 1 KB (64 lanes x 16 B);
+  // wave w fills chunks 2w, 2w+1.  Lane l of chunk q fills LDS unit
+  // u = 64 q + l = row u/4, physical chunk u%4, i.e. logical chunk
+  // (u%4) ^ ((row>>2)&3).  Rows past n read row n-1 (those products only
+  // reach outputs >= n, which are never stored).
+  const uint16_t* ga[2];
+  const uint16_t* gb[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int u = (2 * wave + q) * 64 + lane, r = u >> 2;
+    const int c = (u & 3) ^ ((r >> 2) & 3);
+    ga[q] = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
+    gb[q] = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
+  }
+  auto issue = [&](int stage) {
+    const int slot = stage % NSLOT;
+    const int64_t ko = (int64_t)stage * BKL;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(ga[q] + ko),
+          (__attribute__((address_space(3))) void*)&Ls[slot][0][(2 * wave + q) * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(gb[q] + ko),
+          (__attribute__((address_space(3))) void*)&Ls[slot][1][(2 * wave + q) * 64], 16, 0, 0);
+    }
+  };
+  auto compute = [&](int slot) {
+    if (skip) return;
+    const uint4* A = Ls[slot][0];
+    const uint4* B = Ls[slot][1];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 2 * ks + (lane >> 5);
+      bf16x8_t a[2], b[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * 64 + 32 * t + (lane & 31), c)]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Wait until this wave's DMA for the stage about to be computed has landed
+  // (`later` stages, 4 instructions each, may stay in flight) and its own LDS
+  // reads are done, then meet the other waves.
+  auto sync_stage = [&](int later) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    switch (later) {
+      case 0: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8)); break;
+      default: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(12)); break;
+    }
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  for (int s = 0; s < AHEAD && s < nfull; ++s) issue(s);
+  int s = 0;
+  // steady state: stages s+1..s+3 in flight while stage s is waited for;
+  // stage s+4 goes into the slot computed in the previous iteration, which
+  // every wave has finished reading (barrier above)
+  for (; s + AHEAD < nfull; ++s) {
+    sync_stage(AHEAD - 1);
+    issue(s + AHEAD);
+    compute(s % NSLOT);
+  }
+  for (; s < nfull; ++s) {
+    sync_stage(nfull - 1 - s);
+    compute(s % NSLOT);
+  }
+  if (nstage > nfull) {
+    // ragged token tail: one masked stage through registers
+    sync_stage(0);
+    const int slot = nfull % NSLOT;
+    const int64_t k0 = kbeg + (int64_t)nfull * BKL;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (tid >> 2) + 128 * i;
+      const int64_t kk = k0 + (tid & 3) * 8;
+      Ls[slot][0][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, r0 + row, n, kk, kend, aligned);
+      Ls[slot][1][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, c0 + row, n, kk, kend, aligned);
+    }
+    __syncthreads();
+    compute(slot);
+  }
+
+  if (!direct) {
+    float* P = partial + ((int64_t)split * ntiles + tile) * (BL * BL);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = wn * 128 + j * 32 + (lane & 31);
+          P[row * BL + col] = acc[i][j][r];
+        }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int gc = c0 + wn * 128 + j * 32 + (lane & 31);
+        if (gr < n && gc <= gr) {
+          float v = 2.0f * acc[i][j][r];
+          if (accumulate) v += H[(int64_t)gr * n + gc];
+          H[(int64_t)gr * n + gc] = v;
+          if (gc != gr) H[(int64_t)gc * n + gr] = v;
+        }
+      }
+}
+
 // Sum split partials in split order, x2, (+H), write lower and mirror.
-// One workgroup per 64x64 quarter of an output tile.
+// One workgroup per 64x64 sub-block of a TE x TE output tile.
+template <int TE>
 __global__ __launch_bounds__(256) void syrk_reduce(
     const float* __restrict__ partial, int ntiles, int nsplit, int n,
     float* __restrict__ H, int accumulate) {
+  constexpr int QB = TE / 64;           // sub-blocks per tile edge
   __shared__ float T[64][65];
-  const int tile = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int tile = blockIdx.x / (QB * QB), q = blockIdx.x % (QB * QB);
   int ti, tj;
-  tile_coords(tile, ti, tj);
-  const int qr = (quarter >> 1) * 64, qc = (quarter & 1) * 64;
-  const int r0 = ti * BM + qr, c0 = tj * BM + qc;
-  if (ti == tj && qr < qc) return;  // strictly-upper quarter of a diagonal tile
+  tile_coords(tile, (n + TE - 1) / TE, ti, tj);
+  const int qr = (q / QB) * 64, qc = (q % QB) * 64;
+  const int r0 = ti * TE + qr, c0 = tj * TE + qc;
+  if (ti == tj && qr < qc) return;  // strictly-upper sub-block of a diagonal tile
   const int tid = threadIdx.x;
   for (int e = tid; e < 64 * 64; e += 256) {
     const int lr = e >> 6, lc = e & 63;
-    const int64_t off = (int64_t)(qr + lr) * BM + qc + lc;
+    const int64_t off = (int64_t)(qr + lr) * TE + qc + lc;
     float s = 0.0f;
 #pragma unroll 8
-    for (int sp = 0; sp < nsplit; ++sp) s += partial[((int64_t)sp * ntiles + tile) * (BM * BM) + off];
+    for (int sp = 0; sp < nsplit; ++sp) s += partial[((int64_t)sp * ntiles + tile) * (TE * TE) + off];
     const int gr = r0 + lr, gc = c0 + lc;
     float v = 2.0f * s;
     if (gr < n && gc < n && gc <= gr) {
@@ -228,45 +442,73 @@ __global__ __launch_bounds__(256) void syrk_reduce(
 
 }  // namespace
 
-void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, SyrkPlan* p) {
-  const int bk = xdtype == 1 ? SyrkCfg<uint16_t>::BK : SyrkCfg<float>::BK;
-  const int64_t nt = (n + BM - 1) / BM;
+bool syrk_aligned(const void* X, int64_t ldx, int32_t xdtype) {
+  return ((uintptr_t)X % 16 == 0) && ((ldx * (xdtype == 1 ? 2 : 4)) % 16 == 0);
+}
+
+void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* p) {
+  // bf16 inputs on layers of >= 1024 channels (16-byte aligned rows) use the
+  // 256x256 tile
+  const bool big = xdtype == 1 && n >= 1024 && aligned;
+  const int te = big ? BL : BM;
+  const int bk = big ? BKL : (xdtype == 1 ? SyrkCfg<uint16_t>::BK : SyrkCfg<float>::BK);
+  const int64_t nt = (n + te - 1) / te;
+  p->tile = te;
   p->ntiles = nt * (nt + 1) / 2;
   const int64_t stages = (ntok + bk - 1) / bk;
-  int64_t want = (2048 + p->ntiles - 1) / p->ntiles;    // ~8 workgroups per CU
-  int64_t maxs = stages / 8 > 0 ? stages / 8 : 1;       // >= 8 stages per split
-  int64_t ns = want < maxs ? want : maxs;
-  if (ns < 1) ns = 1;
+  // Enough work items for a few rounds of workgroups; below that, a multiple
+  // of 8 splits so that each XCD streams its own token range.
+  const int64_t slots = big ? 256 : 512;      // resident workgroups
+  int64_t ns = 1;
+  if (p->ntiles < 3 * slots) {
+    const int64_t want = (4 * slots + p->ntiles - 1) / p->ntiles;
+    ns = (want + 7) / 8 * 8;
+    if (big && ns > 16) ns = 16;
+  }
+  const int64_t maxs = stages / 8 > 0 ? stages / 8 : 1;  // >= 8 stages per split
+  if (ns > maxs) ns = maxs;
   if (ns > 64) ns = 64;
+  if (ns < 1) ns = 1;
   int64_t kps = ((stages + ns - 1) / ns) * bk;
   if (kps < bk) kps = bk;           // ntok == 0: one empty split
   ns = (ntok + kps - 1) / kps;
   if (ns < 1) ns = 1;
   p->nsplit = ns;
   p->kps = kps;
-  p->partial_bytes = ns > 1 ? (size_t)ns * p->ntiles * BM * BM * sizeof(float) : 0;
+  p->partial_bytes = ns > 1 ? (size_t)ns * p->ntiles * te * te * sizeof(float) : 0;
 }
 
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
                           int64_t ntok, int64_t ldx, int32_t accumulate,
                           const SyrkPlan& p, void* partial, hipStream_t st) {
-  const bool aligned =
-      ((uintptr_t)X % 16 == 0) && ((ldx * (xdtype == 1 ? 2 : 4)) % 16 == 0);
+  const bool aligned = syrk_aligned(X, ldx, xdtype);
   const int direct = p.nsplit == 1;
-  dim3 grid((unsigned)p.ntiles, (unsigned)p.nsplit);
-  if (xdtype == 1)
+  const int64_t items = p.ntiles * p.nsplit;
+  const int per_xcd = (int)((items + 7) / 8);
+  const unsigned grid = (unsigned)(8 * per_xcd);
+  if (p.tile == BL && !aligned) return hipErrorInvalidValue;  // checked by the caller
+  if (p.tile == BL)
+    syrk_tiles256<<<grid, NTL, 0, st>>>((const uint16_t*)X, (int)n, ntok, ldx, p.kps, aligned,
+                                       (float*)partial, H, direct, accumulate, (int)p.ntiles,
+                                       (int)p.nsplit, per_xcd);
+  else if (xdtype == 1)
     syrk_tiles<uint16_t><<<grid, NT, 0, st>>>((const uint16_t*)X, (int)n, ntok, ldx,
                                               p.kps, aligned, (float*)partial, H,
-                                              direct, accumulate);
+                                              direct, accumulate, (int)p.ntiles,
+                                              (int)p.nsplit, per_xcd);
   else
     syrk_tiles<float><<<grid, NT, 0, st>>>((const float*)X, (int)n, ntok, ldx, p.kps,
                                            aligned, (float*)partial, H, direct,
-                                           accumulate);
+                                           accumulate, (int)p.ntiles, (int)p.nsplit,
+                                           per_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || direct) return e;
-  syrk_reduce<<<(unsigned)(p.ntiles * 4), 256, 0, st>>>((const float*)partial,
-                                                        (int)p.ntiles, (int)p.nsplit,
-                                                        (int)n, H, accumulate);
+  if (p.tile == BL)
+    syrk_reduce<BL><<<(unsigned)(p.ntiles * 16), 256, 0, st>>>(
+        (const float*)partial, (int)p.ntiles, (int)p.nsplit, (int)n, H, accumulate);
+  else
+    syrk_reduce<BM><<<(unsigned)(p.ntiles * 4), 256, 0, st>>>(
+        (const float*)partial, (int)p.ntiles, (int)p.nsplit, (int)n, H, accumulate);
   return hipGetLastError();
 }
 

@@ -116,7 +116,8 @@ struct LayerWs {
 };
 
 void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool need_h,
-                 bool need_l, int32_t xdtype, int32_t block, int32_t prec, LayerWs* w) {
+                 bool need_l, int32_t xdtype, bool x_aligned, int32_t block, int32_t prec,
+                 LayerWs* w) {
   w->flags = (DevFlags*)c.take(sizeof(DevFlags));
   w->lam = (double*)c.take(sizeof(double));
   w->perm = (int32_t*)c.take((size_t)n * 4);
@@ -126,7 +127,7 @@ void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool
   w->partial = nullptr;
   if (has_x) {
     SyrkPlan p;
-    syrk_plan(n, ntok, xdtype, &p);
+    syrk_plan(n, ntok, xdtype, x_aligned, &p);
     w->partial = p.partial_bytes ? c.take(p.partial_bytes) : nullptr;
   }
   w->L = need_l ? c.take((size_t)n * n * elem(prec)) : nullptr;
@@ -154,10 +155,13 @@ const char* pwq_last_error(void) { return g_last_error.c_str(); }
 
 size_t pwq_hessian_workspace_size(int64_t n, int64_t ntok) {
   if (n <= 0 || ntok < 0) return 0;
-  SyrkPlan a, b;
-  syrk_plan(n, ntok, PWQ_BF16, &a);
-  syrk_plan(n, ntok, PWQ_F32, &b);
-  size_t need = a.partial_bytes > b.partial_bytes ? a.partial_bytes : b.partial_bytes;
+  size_t need = 0;
+  for (int dt = 0; dt < 2; ++dt)
+    for (int al = 0; al < 2; ++al) {
+      SyrkPlan p;
+      syrk_plan(n, ntok, dt == 0 ? PWQ_BF16 : PWQ_F32, al != 0, &p);
+      if (p.partial_bytes > need) need = p.partial_bytes;
+    }
   return (need + kAlign - 1) / kAlign * kAlign;
 }
 
@@ -172,7 +176,7 @@ pwq_status pwq_hessian_accum(float* H, int64_t n, const void* X, int32_t xdtype,
     return fail(PWQ_ERR_INVALID_ARG, "X dtype must be PWQ_BF16 or PWQ_F32");
   if (ldx < ntok) return fail(PWQ_ERR_INVALID_ARG, "ldx < ntok");
   SyrkPlan p;
-  syrk_plan(n, ntok, xdtype, &p);
+  syrk_plan(n, ntok, xdtype, syrk_aligned(X, ldx, xdtype), &p);
   pwq_status s = check_ws(ws, ws_bytes, p.partial_bytes);
   if (s != PWQ_OK) return s;
   hipError_t e = launch_hessian(H, n, X, xdtype, ntok, ldx, accumulate, p, ws,
@@ -309,16 +313,18 @@ size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_
                                       int32_t order_kind, int32_t block, int32_t prec) {
   (void)order_kind;
   if (m < 0 || n <= 0 || !valid_block(block)) return 0;
-  Carver c(nullptr);
-  LayerWs w;
-  // size for the worst case: H and L kept in the workspace, bf16 or fp32 X
-  size_t a, b;
-  carve_layer(c, m, n, ntok, has_x != 0, has_x != 0, true, PWQ_BF16, block, prec, &w);
-  a = c.size();
-  Carver c2(nullptr);
-  carve_layer(c2, m, n, ntok, has_x != 0, has_x != 0, true, PWQ_F32, block, prec, &w);
-  b = c2.size();
-  return a > b ? a : b;
+  // size for the worst case: H and L kept in the workspace, any X dtype and
+  // alignment
+  size_t need = 0;
+  for (int dt = 0; dt < 2; ++dt)
+    for (int al = 0; al < 2; ++al) {
+      Carver c(nullptr);
+      LayerWs w;
+      carve_layer(c, m, n, ntok, has_x != 0, has_x != 0, true, dt == 0 ? PWQ_BF16 : PWQ_F32,
+                  al != 0, block, prec, &w);
+      if (c.size() > need) need = c.size();
+    }
+  return need;
 }
 
 pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
@@ -348,13 +354,14 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
 
   const bool need_h = has_x && !H_out;
   const bool need_l = !L_out;
+  const bool xal = has_x && syrk_aligned(X, ldx, xdtype);
   Carver measure(nullptr);
   LayerWs w;
-  carve_layer(measure, m, n, ntok, has_x, need_h, need_l, xdtype, block, prec, &w);
+  carve_layer(measure, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, &w);
   s = check_ws(ws, ws_bytes, measure.size());
   if (s != PWQ_OK) return s;
   Carver c(ws);
-  carve_layer(c, m, n, ntok, has_x, need_h, need_l, xdtype, block, prec, &w);
+  carve_layer(c, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, &w);
   hipStream_t st = (hipStream_t)stream;
   float* Hm = has_x ? (H_out ? H_out : w.H) : (float*)H;
   void* Lm = L_out ? L_out : w.L;
@@ -362,7 +369,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   hipError_t e = launch_init_flags(w.flags, result, 1, st);
   if (e == hipSuccess && has_x) {
     SyrkPlan p;
-    syrk_plan(n, ntok, xdtype, &p);
+    syrk_plan(n, ntok, xdtype, xal, &p);
     e = launch_hessian(Hm, n, X, xdtype, ntok, ldx, 0, p, w.partial, st);
   }
   const int32_t* colmap = nullptr;

@@ -78,6 +78,18 @@ __device__ __forceinline__ void tile_to_lds(T* __restrict__ dst, int tid, Get&& 
   }
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations (lgkmcnt(0)) and meets the other waves, without the release
+// fence of __syncthreads(), whose vmcnt(0) would drain global loads that are
+// deliberately still in flight.  The signal fences stop the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Empty register constraint: the value must exist in a VGPR at this point.
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin(double& v) { asm volatile("" : "+v"(v)); }

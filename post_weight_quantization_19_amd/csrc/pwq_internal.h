@@ -11,13 +11,15 @@
 namespace pwq {
 
 struct SyrkPlan {
+  int tile;              // output tile edge (128 or 256)
   int64_t ntiles;
   int64_t nsplit;
   int64_t kps;           // tokens per split (multiple of the LDS stage)
   size_t partial_bytes;  // 0 when a single split writes H directly
 };
 
-void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, SyrkPlan* p);
+bool syrk_aligned(const void* X, int64_t ldx, int32_t xdtype);
+void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* p);
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype, int64_t ntok,
                           int64_t ldx, int32_t accumulate, const SyrkPlan& p, void* partial,
                           hipStream_t st);

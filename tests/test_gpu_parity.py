@@ -65,6 +65,23 @@ def test_hessian_stage(layers, case):
     assert err <= TOL_H, err
 
 
+@pytest.mark.parametrize("n,ntok", [(1100, 3000), (2048, 20480)])
+def test_hessian_large_tiles(n, ntok):
+    """Layers of >= 1024 channels take the 256x256-tile SYRK (ragged channel
+    and token tails; the second case is split over the token axis)."""
+    cfg = synth.config(2).resized(m=16, n=n, ntok=ntok)
+    lay = synth.make_layer(cfg)
+    _, X, _ = upload(lay)
+    H = P.hessian_accum(X)
+    torch.cuda.synchronize()
+    Hg = to_np(H)
+    assert np.array_equal(Hg, Hg.T)
+    assert rel_fro(Hg, O.hessian(lay.X64())) <= TOL_H
+    H2 = P.hessian_accum(X, H=H.clone(), accumulate=True)
+    torch.cuda.synchronize()
+    assert rel_fro(to_np(H2), 2 * Hg) <= 1e-6
+
+
 def test_hessian_accumulate_and_empty(layers):
     lay = layers["qproj_small"]
     _, X, _ = upload(lay)
