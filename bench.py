@@ -8,8 +8,9 @@ loss/bound reduction.  Workload: W 4096 x 4096 bf16, X 4096 x 131072 bf16
 damp 0.01 -- synthetic, seeded.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the Hessian
-SYRK): algorithmic flops n(n+1)N per launch over its average duration,
-measured here with HIP events on the stream the library launches on.
+SYRK tiles): algorithmic flops n(n+1)N per launch over its average duration,
+measured with HIP events that the library records around each launch of that
+kernel during the timed steps, on the stream it launches on.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -37,7 +38,31 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-token-fraction", type=int, default=8,
                     help="oracle Hessian is timed on 1/k of the tokens, scaled by k")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (the reference kernel "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_tiles256_qproj_4096x4096_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "post_weight_quantization_19_amd", "csrc", "hessian.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None if the kernel source has changed since
+    the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if t.get("kernel_source_sha256") != h:
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(lay, cfg, frac):
@@ -111,27 +136,24 @@ def main():
         step()
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    # The dominant kernel (the Hessian SYRK tiles) records a HIP event pair
+    # around each of its launches inside the timed steps, on the stream the
+    # library launches it on.
+    timer = P.HessianTileTimer(args.steps)
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    with timer:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+    tiles_ms = timer.durations_ms()
+    t_tiles = sum(tiles_ms) / len(tiles_ms) / 1e3
+    flops_h = float(n) * (n + 1) * N
+    achieved = flops_h / t_tiles / 1e12
 
-    # dominant kernel: the Hessian SYRK, timed with events on the library's stream
     stream = torch.cuda.current_stream()
     H = torch.empty((n, n), dtype=torch.float32, device=dev)
-    reps = max(3, args.steps)
-    P.hessian_accum(X, H=H)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(reps):
-        P.hessian_accum(X, H=H)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_h = ev0.elapsed_time(ev1) / 1e3 / reps
-    flops_h = float(n) * (n + 1) * N
-    achieved = flops_h / t_h / 1e12
 
     # stage breakdown (same library calls, separately)
     def timed(fn, r=3):
@@ -144,8 +166,10 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / r
+    P.hessian_accum(X, H=H)
     Lf, dead, _ = P.damp_cholesky(H, damp=cfg.damp)
     s, z = P.grid_steps(W, grid)
+    t_hess = timed(lambda: P.hessian_accum(X, H=H))
     t_chol = timed(lambda: P.damp_cholesky(H, damp=cfg.damp))
     t_sweep = timed(lambda: P.babai_sweep(W, Lf, grid, scales=s, zeros=z, block=cfg.block))
     flops_upd = float(m) * n * (n - cfg.block)
@@ -168,16 +192,27 @@ def main():
                                f"{cfg.grid_kind} {cfg.bits}-bit group {cfg.group}, "
                                f"block {cfg.block}, damp {cfg.damp}",
                    "m": m, "n": n, "ntok": N, "layer_quantize_time_s": dt},
-        "roofline": {"bound": "mfma", "kernel": "hessian_accum (bf16 SYRK)",
+        "roofline": {"bound": "mfma", "kernel": "syrk_tiles256 (bf16 SYRK tiles of H = 2 X X^T)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
-        "stages_ms": {"hessian": t_h * 1e3, "damp_cholesky": t_chol, "sweep_and_update": t_sweep},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "avg_launch_ms": t_tiles * 1e3, "launches_timed": len(tiles_ms),
+                     "flops_per_launch": flops_h},
+        "stages_ms": {"hessian_accum": t_hess, "damp_cholesky": t_chol,
+                      "sweep_and_update": t_sweep},
         "update_mfma_util_upper": (flops_upd / (t_sweep / 1e3) / 1e12) / PEAK_F32_TFLOPS,
         "loss": res0["loss"], "bound": res0["bound"],
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(lay, cfg, args.cpu_token_fraction)
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(line), flush=True)
 
 

@@ -212,6 +212,25 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
                            int32_t* zeros, pwq_result* result, float* H_out,
                            void* L_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------- *
+ * Kernel timing hook (measurement only; no effect on any result).
+ * Attaches caller-owned HIP events (hipEvent_t handles) to one kernel:
+ * after attach, launch i (i = 0 .. capacity-1) of that kernel records
+ * starts[i] immediately before and stops[i] immediately after itself on
+ * the stream it is launched on; later launches are not recorded.
+ *   kernel   : PWQ_TIMER_HESSIAN_TILES = the Hessian product kernel (the
+ *              bf16/fp32 SYRK tiles of pwq_hessian_accum and of
+ *              pwq_quant_layer, without the split-K reduction).
+ *   capacity : number of event pairs; 0 (with NULL arrays) detaches.
+ * The arrays must stay valid until detach.  Process-wide state, not
+ * thread safe: attach, run, synchronise, detach from one thread.
+ * pwq_kernel_timer_count returns the pairs recorded since the last attach.
+ * ---------------------------------------------------------------------- */
+typedef enum { PWQ_TIMER_HESSIAN_TILES = 0 } pwq_timed_kernel;
+pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* const* stops,
+                                   int64_t capacity);
+int64_t pwq_kernel_timer_count(void);
+
 #ifdef __cplusplus
 }
 #endif

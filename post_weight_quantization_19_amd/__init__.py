@@ -9,6 +9,7 @@ quantization", technical summary 2), behind the C ABI of ``libpwq.so``
 memory) and the current stream into that ABI; the HIP kernels do all the
 work and there is no CPU fallback.
 """
+import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
@@ -18,7 +19,7 @@ from . import _lib
 from ._lib import PwqError, check, lib, make_grid, parse_result
 
 __all__ = ["Grid", "hessian_accum", "damp_cholesky", "grid_steps", "babai_sweep",
-           "quant_layer", "read_result", "PwqError"]
+           "quant_layer", "read_result", "PwqError", "HessianTileTimer"]
 
 
 @dataclass(frozen=True)
@@ -195,3 +196,36 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
         o["result"].data_ptr(), _ptr(o.get("H")), _ptr(o.get("L")), ws.data_ptr(),
         ws.numel(), _stream()))
     return o
+
+
+class HessianTileTimer:
+    """Times the Hessian product kernel itself (pwq_kernel_timer_attach):
+    inside the ``with`` block, its first ``capacity`` launches record a pair
+    of HIP events on the stream they run on.  Measurement only."""
+
+    def __init__(self, capacity: int):
+        self.starts = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        self.stops = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for e in self.starts + self.stops:
+            e.record()          # torch creates the HIP event on its first record
+        arr = ctypes.c_void_p * max(capacity, 1)
+        self._s = arr(*[e.cuda_event for e in self.starts])
+        self._e = arr(*[e.cuda_event for e in self.stops])
+        self.capacity = capacity
+        self.count = 0
+
+    def __enter__(self):
+        check(lib().pwq_kernel_timer_attach(_lib.PWQ_TIMER_HESSIAN_TILES, self._s, self._e,
+                                            self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        self.count = int(lib().pwq_kernel_timer_count())
+        check(lib().pwq_kernel_timer_attach(_lib.PWQ_TIMER_HESSIAN_TILES, None, None, 0))
+        return False
+
+    def durations_ms(self):
+        """Per-launch durations (synchronises)."""
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in zip(self.starts[:self.count],
+                                                  self.stops[:self.count])]

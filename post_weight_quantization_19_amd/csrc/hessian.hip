@@ -487,6 +487,11 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
   const int per_xcd = (int)((items + 7) / 8);
   const unsigned grid = (unsigned)(8 * per_xcd);
   if (p.tile == BL && !aligned) return hipErrorInvalidValue;  // checked by the caller
+  const int64_t ti = g_timer_hessian_tiles.next();
+  if (ti >= 0) {
+    const hipError_t e = hipEventRecord(g_timer_hessian_tiles.starts[ti], st);
+    if (e != hipSuccess) return e;
+  }
   if (p.tile == BL)
     syrk_tiles256<<<grid, NTL, 0, st>>>((const uint16_t*)X, (int)n, ntok, ldx, p.kps, aligned,
                                        (float*)partial, H, direct, accumulate, (int)p.ntiles,
@@ -502,6 +507,7 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
                                            accumulate, (int)p.ntiles, (int)p.nsplit,
                                            per_xcd);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ti >= 0) e = hipEventRecord(g_timer_hessian_tiles.stops[ti], st);
   if (e != hipSuccess || direct) return e;
   if (p.tile == BL)
     syrk_reduce<BL><<<(unsigned)(p.ntiles * 16), 256, 0, st>>>(

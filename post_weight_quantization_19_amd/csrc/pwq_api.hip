@@ -10,6 +10,10 @@
 
 using namespace pwq;
 
+namespace pwq {
+KernelTimer g_timer_hessian_tiles;
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -400,5 +404,22 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   if (e != hipSuccess) return hip_fail(e, "quant_layer launch");
   return ok();
 }
+
+pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* const* stops,
+                                   int64_t capacity) {
+  if (kernel != PWQ_TIMER_HESSIAN_TILES)
+    return fail(PWQ_ERR_INVALID_ARG, "unknown timed kernel %d", kernel);
+  if (capacity < 0) return fail(PWQ_ERR_INVALID_ARG, "capacity must be >= 0");
+  if (capacity > 0 && (!starts || !stops))
+    return fail(PWQ_ERR_INVALID_ARG, "event arrays are NULL");
+  KernelTimer& t = g_timer_hessian_tiles;
+  t.starts = capacity ? (hipEvent_t*)starts : nullptr;
+  t.stops = capacity ? (hipEvent_t*)stops : nullptr;
+  t.capacity = capacity;
+  t.used = 0;
+  return ok();
+}
+
+int64_t pwq_kernel_timer_count(void) { return g_timer_hessian_tiles.used; }
 
 }  // extern "C"

@@ -65,4 +65,15 @@ hipError_t launch_order(int32_t order_kind, const float* H, int64_t n, const int
                         hipStream_t st);
 hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, hipStream_t st);
 
+// Event pairs recorded around launches of one kernel (pwq_kernel_timer_attach).
+struct KernelTimer {
+  hipEvent_t* starts = nullptr;
+  hipEvent_t* stops = nullptr;
+  int64_t capacity = 0;
+  int64_t used = 0;
+  // Returns the pair index to record, or -1 when not attached / full.
+  int64_t next() { return used < capacity ? used++ : -1; }
+};
+extern KernelTimer g_timer_hessian_tiles;
+
 }  // namespace pwq

@@ -1,0 +1,179 @@
+"""Summaries of rocprofv3 CSV output (host-side text processing only).
+
+    python -m post_weight_quantization_19_amd.profiling stats DIR --command CMD --out FILE.md
+        per-kernel call count / average / total from DIR/*_kernel_stats.csv
+    python -m post_weight_quantization_19_amd.profiling traffic --fetch DIR --write DIR \
+            --kernel NAME --algorithmic-bytes B --source FILE --command CMD ... --out FILE.json
+        HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE,
+        WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
+        reads for the 1 GiB device copy in the same run.
+
+The scale factors exist because FETCH_SIZE/WRITE_SIZE count cache-line
+requests of particular sizes; a plain copy of known size calibrates them.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+COPY_KERNEL = "copyBuffer"
+COPY_KIB = 1 << 20          # the calibration copy moves 1 GiB each way
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def short_name(name: str) -> str:
+    """Kernel name without namespaces and argument list (template arguments kept)."""
+    s = re.sub(r"^void\s+", "", name.replace("(anonymous namespace)::", ""))
+    depth = 0
+    for i, ch in enumerate(s):
+        depth += (ch == "<") - (ch == ">")
+        if ch == "(" and depth == 0:
+            s = s[:i]
+            break
+    head = s.split("<", 1)[0]
+    return head.split("::")[-1] + s[len(head):]
+
+
+def kernel_stats(d):
+    rows = []
+    with open(_one(os.path.join(d, "*kernel_stats.csv"))) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3,
+                         "total_ms": float(r["TotalDurationNs"]) / 1e6,
+                         "pct": float(r["Percentage"]),
+                         "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3})
+    return rows
+
+
+def launch_durations_us(d, kernel):
+    """Durations of every launch of one kernel, in launch order (kernel trace)."""
+    out = []
+    with open(_one(os.path.join(d, "*kernel_trace.csv"))) as f:
+        for r in csv.DictReader(f):
+            if short_name(r["Kernel_Name"]) == kernel:
+                out.append((int(r["Start_Timestamp"]),
+                            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    return [x for _, x in sorted(out)]
+
+
+def stats_markdown(d, command, title, launches=None, bench_log=None):
+    rows = kernel_stats(d)
+    out = [f"# {title}", "", "Command (from the repository root):", "", "```", command, "```",
+           "", "| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | % |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.1f} | {r['min_us']:.1f} | "
+                   f"{r['max_us']:.1f} | {r['total_ms']:.3f} | {r['pct']:.2f} |")
+    if launches:
+        d_us = launch_durations_us(d, launches)
+        out += ["", f"Every launch of {launches}, in order (us):", "",
+                " ".join(f"{x:.1f}" for x in d_us)]
+        if bench_log:
+            line = None
+            with open(bench_log) as f:
+                for ln in f:
+                    if ln.startswith("{"):
+                        line = json.loads(ln)
+            if line is not None:
+                rf = line["roofline"]
+                k, w = line["steps"], line["warmup"]
+                # launches before the timed steps: the first call and the warmup steps
+                timed = d_us[1 + w:1 + w + k]
+                out += ["", f"bench.py's own HIP-event average over its {k} timed launches: "
+                        f"{rf['avg_launch_ms'] * 1e3:.1f} us; the same {len(timed)} launches "
+                        f"in this trace (launches {2 + w}..{1 + w + k}): "
+                        f"{sum(timed) / max(len(timed), 1):.1f} us; "
+                        f"achieved {rf['achieved']:.1f} {rf['unit']} = "
+                        f"{100 * rf['frac']:.1f}% of {rf['peak']:.0f}."]
+    return "\n".join(out) + "\n"
+
+
+def counter_per_dispatch(d, counter):
+    """{short kernel name: [value per dispatch ...]} for one counter."""
+    vals = {}
+    with open(_one(os.path.join(d, "*counter_collection.csv"))) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_dir, write_dir, kernel, algorithmic_bytes, source, commands, title,
+            workload):
+    fv = counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    wv = counter_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def pick(vals, key):
+        for k, v in vals.items():
+            if key in k:
+                return v
+        raise SystemExit(f"kernel {key} not in the counter run")
+    kf, kw = pick(fv, kernel), pick(wv, kernel)
+    cf, cw = pick(fv, COPY_KERNEL), pick(wv, COPY_KERNEL)
+    f_fac = COPY_KIB / max(cf)
+    w_fac = COPY_KIB / max(cw)
+    fkib = sum(kf) / len(kf)
+    wkib = sum(kw) / len(kw)
+    rd = fkib * f_fac * 1024
+    wr = wkib * w_fac * 1024
+    with open(source, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return {
+        "title": title, "kernel": kernel, "workload": workload, "commands": commands,
+        "fetch_size_kib_per_dispatch": fkib, "fetch_dispatches": len(kf),
+        "write_size_kib_per_dispatch": wkib, "write_dispatches": len(kw),
+        "calibration": {"kernel": "1 GiB device-to-device copy (bench.py --copy-calibration)",
+                        "fetch_size_kib": max(cf), "write_size_kib": max(cw),
+                        "known_kib_each_way": COPY_KIB, "fetch_factor": f_fac,
+                        "write_factor": w_fac},
+        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": algorithmic_bytes,
+        "kernel_source": os.path.relpath(source), "kernel_source_sha256": sha,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel statistics")
+    s.add_argument("--launches", help="list every launch of this kernel")
+    s.add_argument("--bench-log", help="bench.py output of the same run (JSON line)")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--algorithmic-bytes", type=float, required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--command", action="append", required=True)
+    t.add_argument("--title", default="HBM traffic per launch")
+    t.add_argument("--workload", default="")
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        txt = stats_markdown(a.dir, a.command, a.title, a.launches, a.bench_log)
+    else:
+        txt = json.dumps(traffic(a.fetch, a.write, a.kernel, a.algorithmic_bytes, a.source,
+                                 a.command, a.title, a.workload), indent=1) + "\n"
+    with open(a.out, "w") as f:
+        f.write(txt)
+    sys.stdout.write(txt)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,14 +18,14 @@ OK, INVALID, UNSUP, WS = (B.PWQ_OK, B.PWQ_ERR_INVALID_ARG, B.PWQ_ERR_UNSUPPORTED
 
 def header_functions():
     txt = open(os.path.join(ROOT, "include", "pwq.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|pwq_status)\s+(pwq_\w+)\s*\(",
-                                 txt, re.M)))
+    return sorted(set(re.findall(
+        r"^\s*(?:const char\*|size_t|int64_t|pwq_status)\s+(pwq_\w+)\s*\(", txt, re.M)))
 
 
 def test_exports_match_header():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     assert sorted(B.EXPORTS) == names
     for nm in names:
         assert getattr(L, nm) is not None
@@ -132,3 +132,12 @@ def test_workspace_sizes_grow_with_the_problem():
     assert 0 < a < b < c
     assert L.pwq_sweep_workspace_size(64, 128, 100, 0) == 0
     assert L.pwq_quant_layer_workspace_size(64, 0, 0, 0, 0, 128, 0) == 0
+
+
+def test_kernel_timer_validation():
+    L = B.lib()
+    assert L.pwq_kernel_timer_attach(5, None, None, 0) == INVALID
+    assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, -1) == INVALID
+    assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, 4) == INVALID
+    assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, 0) == OK
+    assert L.pwq_kernel_timer_count() == 0
