@@ -13,7 +13,8 @@ def dev_tensor(vals32, bits, device="cuda"):
 
 def upload(layer, device="cuda"):
     W = dev_tensor(layer.W, layer.W_bits, device)
-    X = dev_tensor(layer.X, layer.X_bits, device) if layer.X is not None else None
+    has_x = layer.X is not None or layer.X_bits is not None
+    X = dev_tensor(layer.X, layer.X_bits, device) if has_x else None
     H = torch.from_numpy(layer.H).to(device) if layer.H is not None else None
     return W, X, H
 
