@@ -7,15 +7,20 @@
 // Hessian gives the same closest-vector instance, so the square Cholesky
 // factor replaces the tall input matrix.
 //
-// Design (gfx950): right-looking blocked Cholesky with 64-column panels, in
-// place on an n x n working copy (float or double).  Per panel:
-//   chol_panel_step  every workgroup factors the tall panel made of the
-//                    64x64 diagonal block and its own 64 panel rows (4 waves,
-//                    lane = row, one LDS broadcast + barrier per column), so
-//                    L_kk and L_ik = A_ik L_kk^-T come out of one pass
-//   chol_trailing    the trailing lower triangle A_ij -= L_ik L_jk^T as 128x128
-//                 MFMA tiles (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64);
-//                 both operands are panel rows, contiguous along K.
+// Design (gfx950): right-looking blocked Cholesky with 64-column panels and
+// a one-panel look-ahead, in place on an n x n working copy (float or
+// double).  chol_panel_first factors the first tall panel; then one
+// chol_step launch per panel both factors the next panel (after applying the
+// current panel's update to it) and applies the current panel to the
+// trailing triangle beyond it, so the serial panel work overlaps the
+// parallel trailing update instead of alternating with it:
+//   panel role     every workgroup factors the tall panel made of the 64x64
+//                  diagonal block and its own 64 panel rows (4 waves, lane =
+//                  row, rank-4 column groups through LDS), so L_kk and
+//                  L_ik = A_ik L_kk^-T come out of one pass
+//   trailing role  A_ij -= L_ik L_jk^T as 128x128 MFMA tiles
+//                  (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64); both
+//                  operands are panel rows, contiguous along K.
 // A non-positive or non-finite pivot stops the factorization and records the
 // LAPACK-style order of the failing minor; every later kernel sees the flag
 // and returns at once.
@@ -111,40 +116,38 @@ __device__ __forceinline__ void pivot_ops(double piv, double& d, double& inv) {
   inv = 1.0 / d;
 }
 
-// One panel step on the tall panel [A_kk; A_bk]: workgroup b factors the
-// 64x64 diagonal block (slot 0) together with its own 64 panel rows
-// k0 + 64 b .. (slot 1, b >= 1) in a single right-looking pass, so the panel
-// solve L_bk = A_bk L_kk^-T needs no separate substitution.  Every
-// workgroup repeats the diagonal factorization (bitwise identical results);
-// workgroup 0 stores L_kk.  Lane = row; wave w keeps columns 16w..16w+15 of
-// both slots in registers.  Columns go in groups of 4: the owner wave
-// factors the group in registers (pivot rows broadcast with readlane) and
-// publishes it in LDS; after one barrier every wave applies the rank-4
-// update to its later columns.  The group buffer is double buffered, so one
-// barrier per group suffices.
+// LDS of one workgroup of the factorization kernels (either role).
 template <typename T>
-__global__ __launch_bounds__(256) void chol_panel_step(T* __restrict__ A, int n, int k0,
-                                                      DevFlags* flags,
-                                                      pwq_result* __restrict__ res) {
-  __shared__ __attribute__((aligned(16))) T gbuf[2][2][4][NB];
-  __shared__ int fail_col;
-  if (flags->info != 0) return;
+struct CholSmem {
+  static constexpr int LD = NB + 1;                                  // padded row
+  static constexpr size_t trail = 2 * 128 * LD * sizeof(T);          // two 128-row panels
+  static constexpr size_t panel = 4 * 64 * LD * sizeof(T)            // Q, P, U0, U1
+                                  + 2 * 2 * 4 * NB * sizeof(T);      // column groups
+  static constexpr size_t bytes = trail > panel ? trail : panel;
+};
+
+// Factor the tall panel [A_kk; A_bk] held in registers and store it: the
+// 64x64 diagonal block (slot 0, d0) together with the workgroup's own 64
+// panel rows k0 + 64 b .. (slot 1, d1, b >= 1) in a single right-looking
+// pass, so the panel solve L_bk = A_bk L_kk^-T needs no separate
+// substitution.  Every workgroup repeats the diagonal factorization
+// (bitwise identical results); workgroup b = 0 stores L_kk.  Lane = row;
+// wave w keeps columns 16w..16w+15 of both slots in registers.  Columns go
+// in groups of 4: the owner wave factors the group in registers (pivot rows
+// broadcast with readlane) and publishes it in LDS; after one barrier every
+// wave applies the rank-4 update to its later columns.  The group buffer is
+// double buffered, so one barrier per group suffices.
+template <typename T>
+__device__ __forceinline__ void panel_factor_store(T* __restrict__ A, int n, int k0, int b,
+                                                   T (&d0)[16], T (&d1)[16],
+                                                   T (*gbuf)[2][4][NB], int* fail_col,
+                                                   T* __restrict__ dbuf, DevFlags* flags,
+                                                   pwq_result* res) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = min(NB, n - k0);
-  const int row1 = k0 + NB * blockIdx.x + lane;     // slot-1 row (blockIdx.x >= 1)
-  const bool has1 = blockIdx.x > 0 && row1 < n;
-  T d0[16], d1[16];
-  {
-    const T* src0 = A + (int64_t)(k0 + min(lane, nb - 1)) * n + k0 + 16 * wave;
-    const T* src1 = A + (int64_t)(has1 ? row1 : k0) * n + k0 + 16 * wave;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int col = 16 * wave + c;
-      d0[c] = (lane < nb) ? (col <= lane ? src0[c] : (T)0) : (col == lane ? (T)1 : (T)0);
-      d1[c] = has1 ? src1[c] : (T)0;
-    }
-  }
-  if (tid == 0) fail_col = -1;
+  const int row1 = k0 + NB * b + lane;
+  const bool has1 = b > 0 && row1 < n;
+  if (tid == 0) *fail_col = -1;
   __syncthreads();
   static_for_up<NB / 4>([&](auto G) {
     constexpr int g = decltype(G)::value;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(256) void chol_panel_step(T* __restrict__ A, int n,
         constexpr int j = j0 + u, jl = jl0 + u;
         const T piv = readlane_t(d0[jl], j);
         const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
-        if (bad && lane == 0 && fail_col < 0) fail_col = j;
+        if (bad && lane == 0 && *fail_col < 0) *fail_col = j;
         T d, inv;
         pivot_ops(piv, d, inv);
         d0[jl] = (lane == j) ? d : d0[jl] * inv;
@@ -193,17 +196,19 @@ __global__ __launch_bounds__(256) void chol_panel_step(T* __restrict__ A, int n,
     }
   });
   __syncthreads();
-  const int fc = fail_col;
+  const int fc = *fail_col;
   if (fc >= 0 && fc < nb) {
-    if (blockIdx.x == 0 && tid == 0) {
+    if (b == 0 && tid == 0) {
       flags->info = k0 + fc + 1;
       res->info = k0 + fc + 1;
     }
     return;
   }
-  if (blockIdx.x == 0) {
+  if (b == 0) {
+    // L_kk goes to the side buffer: the diagonal block in A is still being
+    // read by workgroups of this launch that started later
     if (lane < nb) {
-      T* dst = A + (int64_t)(k0 + lane) * n + k0 + 16 * wave;
+      T* dst = dbuf + lane * NB + 16 * wave;
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         const int col = 16 * wave + c;
@@ -217,19 +222,128 @@ __global__ __launch_bounds__(256) void chol_panel_step(T* __restrict__ A, int n,
   }
 }
 
-// Trailing update of the lower triangle: A_ij -= P_i P_j^T, P = the panel
-// (columns k0..k0+64 of the rows below the diagonal block), 128x128 tiles.
+// Registers of the tall panel at k0 for workgroup b: the lower 64x64
+// diagonal block (identity-padded past n) and the workgroup's panel rows.
 template <typename T>
-__global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, int k0,
-                                                     const DevFlags* flags) {
-  constexpr int TB = 128, LD = NB + 1;
-  __shared__ T As[TB * LD];
-  __shared__ T Bs[TB * LD];
+__device__ __forceinline__ void panel_load(const T* __restrict__ A, int n, int k0, int b,
+                                           T (&d0)[16], T (&d1)[16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = min(NB, n - k0);
+  const int row1 = k0 + NB * b + lane;
+  const bool has1 = b > 0 && row1 < n;
+  const T* src0 = A + (int64_t)(k0 + min(lane, nb - 1)) * n + k0 + 16 * wave;
+  const T* src1 = A + (int64_t)(has1 ? row1 : k0) * n + k0 + 16 * wave;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int col = 16 * wave + c;
+    d0[c] = (lane < nb) ? (col <= lane ? src0[c] : (T)0) : (col == lane ? (T)1 : (T)0);
+    d1[c] = has1 ? src1[c] : (T)0;
+  }
+}
+
+// Diagonal block kq..kq+63 of L from the side buffer into A (lower part).
+template <typename T>
+__device__ __forceinline__ void diag_copy(T* __restrict__ A, int n, int kq,
+                                          const T* __restrict__ dbuf) {
+  const int nb = min(NB, n - kq);
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    if (r < nb && c <= r) A[(int64_t)(kq + r) * n + kq + c] = dbuf[e];
+  }
+}
+
+// First panel (nothing to apply before it).  L_00 goes to side buffer 0.
+template <typename T>
+__global__ __launch_bounds__(256) void chol_panel_first(T* __restrict__ A, int n,
+                                                       T* __restrict__ dbuf, DevFlags* flags,
+                                                       pwq_result* __restrict__ res) {
+  __shared__ __attribute__((aligned(16))) T gbuf[2][2][4][NB];
+  __shared__ int fail_col;
   if (flags->info != 0) return;
-  const int base = k0 + NB;
+  T d0[16], d1[16];
+  panel_load<T>(A, n, 0, blockIdx.x, d0, d1);
+  panel_factor_store<T>(A, n, 0, blockIdx.x, d0, d1, gbuf, &fail_col, dbuf, flags, res);
+}
+
+// The last diagonal block, after the final step.
+template <typename T>
+__global__ __launch_bounds__(256) void chol_diag_last(T* __restrict__ A, int n, int kq,
+                                                     const T* __restrict__ dbuf,
+                                                     const DevFlags* flags) {
+  if (flags->info != 0) return;
+  diag_copy<T>(A, n, kq, dbuf);
+}
+
+// U = S Q^T for 64x64 operands in LDS (rows x NB, padded), result to LDS.
+// Wave w computes the 32x32 block (w>>1, w&1).
+template <typename T>
+__device__ __forceinline__ void mfma_64x64x64(const T* __restrict__ S, const T* __restrict__ Q,
+                                              T* __restrict__ U) {
+  constexpr int LD = NB + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if constexpr (sizeof(T) == 4) {
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < NB; k += 2) {
+      const int ko = k + (lane >> 5);
+      const float a = S[(wm * 32 + (lane & 31)) * LD + ko];
+      const float bq = Q[(wn * 32 + (lane & 31)) * LD + ko];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      U[(wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LD + wn * 32 + (lane & 31)] =
+          acc[r];
+  } else {
+    f64x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0;
+#pragma unroll 4
+    for (int k = 0; k < NB; k += 4) {
+      const int ko = k + (lane >> 4);
+      double av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        av[i] = S[(wm * 32 + i * 16 + (lane & 15)) * LD + ko];
+        bv[i] = Q[(wn * 32 + i * 16 + (lane & 15)) * LD + ko];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          U[(wm * 32 + i * 16 + 4 * r + (lane >> 4)) * LD + wn * 32 + j * 16 + (lane & 15)] =
+              acc[i][j][r];
+  }
+}
+
+// Trailing update of one 128x128 lower-triangle tile t (row-major triangle
+// order) of A[base:, base:] by the panel at columns k0..k0+63:
+// A_ij -= P_i P_j^T with P the panel rows, K = 64 on MFMA
+// (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64); both operands are panel
+// rows, contiguous along K.
+template <typename T>
+__device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, int base, int t,
+                                              char* smem) {
+  constexpr int TB = 128, LD = NB + 1;
+  T* As = (T*)smem;
+  T* Bs = As + TB * LD;
   int ti, tj;
   {
-    const int t = blockIdx.x;
     int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
     while ((r + 1) * (r + 2) / 2 <= t) ++r;
     while (r * (r + 1) / 2 > t) --r;
@@ -337,27 +451,93 @@ __global__ __launch_bounds__(256) void chol_trailing(T* __restrict__ A, int n, i
   }
 }
 
+// One step with look-ahead, given the finished panel at k0 (columns
+// k0..k0+63 of every row >= k0 hold L).  Two roles in one launch, reading
+// only that panel, so they run concurrently:
+//  * workgroups 0 .. np-1 take the NEXT panel p1 = k0 + 64: each applies the
+//    panel-k0 update to the rows it factors (the diagonal block and its own
+//    64 rows; A -= P Q^T with K = 64 on MFMA through LDS) and factors them
+//    as above -- the serial part of the factorization;
+//  * the remaining workgroups update the trailing triangle beyond the next
+//    panel, A[k0+128:, k0+128:], with the same panel.
+// The next panel's columns are written by the first role only, the columns
+// beyond it by the second only.
 template <typename T>
-hipError_t factor_impl(T* A, int n, DevFlags* flags, pwq_result* res, hipStream_t st) {
-  for (int k0 = 0; k0 < n; k0 += NB) {
-    const int rows = n - k0;
-    chol_panel_step<T><<<(rows + NB - 1) / NB, 256, 0, st>>>(A, n, k0, flags, res);
-    const int below = n - k0 - NB;
-    if (below > 0) {
-      const int nt = (below + 127) / 128;
-      chol_trailing<T><<<nt * (nt + 1) / 2, 256, 0, st>>>(A, n, k0, flags);
-    }
+__global__ __launch_bounds__(256) void chol_step(T* __restrict__ A, int n, int k0, int np,
+                                                 int ntrail, T* __restrict__ dbuf,
+                                                 DevFlags* flags, pwq_result* __restrict__ res) {
+  constexpr int LD = NB + 1;
+  __shared__ __attribute__((aligned(16))) char smem[CholSmem<T>::bytes];
+  __shared__ int fail_col;
+  if (flags->info != 0) return;
+  const int q = k0 / NB;
+  if ((int)blockIdx.x >= np + ntrail) {
+    // the finished diagonal block of panel k0 (no workgroup of this launch
+    // reads rows k0..k0+63)
+    diag_copy<T>(A, n, k0, dbuf + (q & 1) * NB * NB);
+    return;
+  }
+  if ((int)blockIdx.x >= np) {
+    trailing_tile<T>(A, n, k0, k0 + 2 * NB, blockIdx.x - np, smem);
+    return;
+  }
+  const int b = blockIdx.x, p1 = k0 + NB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  T* Q = (T*)smem;                 // panel-k0 columns of rows p1 .. p1+63
+  T* S = Q + 64 * LD;              // panel-k0 columns of rows p1+64b .. (b >= 1)
+  T* U0 = S + 64 * LD;
+  T* U1 = U0 + 64 * LD;
+  T(*gbuf)[2][4][NB] = (T(*)[2][4][NB])(U1 + 64 * LD);
+  T d0[16], d1[16];
+  panel_load<T>(A, n, p1, b, d0, d1);
+  tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
+    return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + k0 + k] : (T)0;
+  });
+  if (b > 0)
+    tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
+      const int row = p1 + NB * b + r;
+      return (row < n) ? A[(int64_t)row * n + k0 + k] : (T)0;
+    });
+  __syncthreads();
+  mfma_64x64x64<T>(Q, Q, U0);
+  if (b > 0) mfma_64x64x64<T>(S, Q, U1);
+  __syncthreads();
+  const int nb = min(NB, n - p1);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int col = 16 * wave + c;
+    if (lane < nb && col <= lane) d0[c] -= U0[lane * LD + col];
+    if (b > 0) d1[c] -= U1[lane * LD + col];
+  }
+  panel_factor_store<T>(A, n, p1, b, d0, d1, gbuf, &fail_col, dbuf + ((q + 1) & 1) * NB * NB,
+                        flags, res);
+}
+
+// dbuf: two 64x64 side buffers (T) for the diagonal blocks in flight.
+template <typename T>
+hipError_t factor_impl(T* A, int n, T* dbuf, DevFlags* flags, pwq_result* res,
+                       hipStream_t st) {
+  chol_panel_first<T><<<(n + NB - 1) / NB, 256, 0, st>>>(A, n, dbuf, flags, res);
+  int k0 = 0;
+  for (; k0 + NB < n; k0 += NB) {
+    const int p1 = k0 + NB;
+    const int np = (n - p1 + NB - 1) / NB;
+    const int base2 = k0 + 2 * NB;
+    const int nt = base2 < n ? (n - base2 + 127) / 128 : 0;
+    const int ntrail = nt * (nt + 1) / 2;
+    chol_step<T><<<np + ntrail + 1, 256, 0, st>>>(A, n, k0, np, ntrail, dbuf, flags, res);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  chol_diag_last<T><<<1, 256, 0, st>>>(A, n, k0, dbuf + ((k0 / NB) & 1) * NB * NB, flags);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                                 const int32_t* perm, void* L, int32_t* dead,
-                                pwq_result* res, DevFlags* flags, double* lam,
+                                pwq_result* res, DevFlags* flags, double* lam, void* dscratch,
                                 hipStream_t st) {
   damp_prep<<<1, 256, 0, st>>>(H, (int)n, damp, dead, res, flags, lam);
   dim3 g((unsigned)((n + 255) / 256), (unsigned)n);
@@ -365,12 +545,12 @@ hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t 
     copy_damped<double><<<g, 256, 0, st>>>(H, (int)n, perm, lam, (double*)L, flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return factor_impl<double>((double*)L, (int)n, flags, res, st);
+    return factor_impl<double>((double*)L, (int)n, (double*)dscratch, flags, res, st);
   }
   copy_damped<float><<<g, 256, 0, st>>>(H, (int)n, perm, lam, (float*)L, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return factor_impl<float>((float*)L, (int)n, flags, res, st);
+  return factor_impl<float>((float*)L, (int)n, (float*)dscratch, flags, res, st);
 }
 
 }  // namespace pwq

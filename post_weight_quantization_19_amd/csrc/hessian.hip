@@ -241,7 +241,11 @@ constexpr int BL = 256;        // large tile edge
 constexpr int BKL = 32;        // tokens per stage
 constexpr int NSLOT = 5;       // LDS ring slots
 constexpr int AHEAD = 4;       // stages in flight ahead of the one computed
-constexpr int NTL = 512;       // threads (8 waves)
+#ifndef SYRK_NWAVE
+#define SYRK_NWAVE 8
+#endif
+constexpr int NWL = SYRK_NWAVE;  // waves per workgroup (8: 64x128 per wave, 4: 128x128)
+constexpr int NTL = 64 * NWL;    // threads
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
@@ -252,6 +256,9 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     const uint16_t* __restrict__ X, int n, int64_t ntok, int64_t ldx, int64_t kps,
     int aligned, float* __restrict__ partial, float* __restrict__ H, int direct,
     int accumulate, int ntiles, int nsplit, int per_xcd) {
+  constexpr int WR = 512 / NWL;        // rows per wave (the wave grid is (NWL/2) x 2)
+  constexpr int TI = WR / 32;          // 32-row accumulator blocks per wave
+  constexpr int CPW = 16 / NWL;        // 1 KB DMA chunks per wave per panel and stage
   __shared__ __attribute__((aligned(16))) uint4 Ls[NSLOT][2][BL * 4];
   const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (item >= ntiles * nsplit) return;
@@ -266,28 +273,28 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
   const int nstage = (int)((kend - kbeg + BKL - 1) / BKL);
   const int nfull = (int)((kend - kbeg) / BKL);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;      // rows 64 wm, cols 128 wn
+  const int wm = wave >> 1, wn = wave & 1;      // rows WR wm, cols 128 wn
   // waves entirely above the diagonal of a diagonal tile have nothing to do
-  const bool skip = diag && (64 * wm + 63 < 128 * wn);
+  const bool skip = diag && (WR * wm + WR - 1 < 128 * wn);
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[TI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // DMA: each stage and panel is 16 wave-chunks of 1 KB (64 lanes x 16 B);
-  // wave w fills chunks 2w, 2w+1.  Lane l of chunk q fills LDS unit
-  // u = 64 q + l = row u/4, physical chunk u%4, i.e. logical chunk
+  // wave w fills chunks CPW w .. CPW w + CPW-1.  Lane l of chunk q fills LDS
+  // unit u = 64 q + l = row u/4, physical chunk u%4, i.e. logical chunk
   // (u%4) ^ ((row>>2)&3).  Rows past n read row n-1 (those products only
   // reach outputs >= n, which are never stored).
-  const uint16_t* ga[2];
-  const uint16_t* gb[2];
+  const uint16_t* ga[CPW];
+  const uint16_t* gb[CPW];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int u = (2 * wave + q) * 64 + lane, r = u >> 2;
+  for (int q = 0; q < CPW; ++q) {
+    const int u = (CPW * wave + q) * 64 + lane, r = u >> 2;
     const int c = (u & 3) ^ ((r >> 2) & 3);
     ga[q] = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
     gb[q] = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
@@ -296,13 +303,15 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     const int slot = stage % NSLOT;
     const int64_t ko = (int64_t)stage * BKL;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < CPW; ++q) {
       __builtin_amdgcn_global_load_lds(
           (const void*)(ga[q] + ko),
-          (__attribute__((address_space(3))) void*)&Ls[slot][0][(2 * wave + q) * 64], 16, 0, 0);
+          (__attribute__((address_space(3))) void*)&Ls[slot][0][(CPW * wave + q) * 64], 16, 0,
+          0);
       __builtin_amdgcn_global_load_lds(
           (const void*)(gb[q] + ko),
-          (__attribute__((address_space(3))) void*)&Ls[slot][1][(2 * wave + q) * 64], 16, 0, 0);
+          (__attribute__((address_space(3))) void*)&Ls[slot][1][(CPW * wave + q) * 64], 16, 0,
+          0);
     }
   };
   auto compute = [&](int slot) {
@@ -312,30 +321,30 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = 2 * ks + (lane >> 5);
-      bf16x8_t a[2], b[4];
+      bf16x8_t a[TI], b[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * 64 + 32 * t + (lane & 31), c)]);
+      for (int t = 0; t < TI; ++t)
+        a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * WR + 32 * t + (lane & 31), c)]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   };
   // Wait until this wave's DMA for the stage about to be computed has landed
-  // (`later` stages, 4 instructions each, may stay in flight) and its own LDS
-  // reads are done, then meet the other waves.
+  // (`later` stages, 2 CPW instructions each, may stay in flight) and its own
+  // LDS reads are done, then meet the other waves.
   auto sync_stage = [&](int later) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     switch (later) {
       case 0: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0)); break;
-      case 1: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4)); break;
-      case 2: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8)); break;
-      default: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(12)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * CPW)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * CPW)); break;
+      default: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(6 * CPW)); break;
     }
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -361,8 +370,8 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     const int slot = nfull % NSLOT;
     const int64_t k0 = kbeg + (int64_t)nfull * BKL;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (tid >> 2) + 128 * i;
+    for (int i = 0; i < 1024 / NTL; ++i) {
+      const int row = (tid >> 2) + (NTL / 4) * i;
       const int64_t kk = k0 + (tid & 3) * 8;
       Ls[slot][0][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, r0 + row, n, kk, kend, aligned);
       Ls[slot][1][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, c0 + row, n, kk, kend, aligned);
@@ -374,24 +383,24 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
   if (!direct) {
     float* P = partial + ((int64_t)split * ntiles + tile) * (BL * BL);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = wm * WR + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int col = wn * 128 + j * 32 + (lane & 31);
           P[row * BL + col] = acc[i][j][r];
         }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int gr = r0 + wm * WR + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int gc = c0 + wn * 128 + j * 32 + (lane & 31);
         if (gr < n && gc <= gr) {
           float v = 2.0f * acc[i][j][r];
@@ -469,6 +478,9 @@ void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* 
   if (ns > maxs) ns = maxs;
   if (ns > 64) ns = 64;
   if (ns < 1) ns = 1;
+#ifdef SYRK_FORCE_NS
+  if (big) ns = SYRK_FORCE_NS;
+#endif
   int64_t kps = ((stages + ns - 1) / ns) * bk;
   if (kps < bk) kps = bk;           // ntok == 0: one empty split
   ns = (ntok + kps - 1) / kps;

@@ -116,6 +116,7 @@ struct LayerWs {
   float* H;
   void* partial;
   void* L;
+  void* dscratch;
   SweepWs sw;
 };
 
@@ -135,6 +136,7 @@ void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool
     w->partial = p.partial_bytes ? c.take(p.partial_bytes) : nullptr;
   }
   w->L = need_l ? c.take((size_t)n * n * elem(prec)) : nullptr;
+  w->dscratch = c.take(kCholScratchBytes);
   carve_sweep(c, m, n, block, prec, &w->sw);
 }
 
@@ -197,6 +199,7 @@ size_t pwq_cholesky_workspace_size(int64_t n, int32_t prec) {
   Carver c(nullptr);
   c.take(sizeof(DevFlags));
   c.take(sizeof(double));
+  c.take(kCholScratchBytes);
   return c.size();
 }
 
@@ -213,10 +216,12 @@ pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t pre
   Carver c(ws);
   DevFlags* flags = (DevFlags*)c.take(sizeof(DevFlags));
   double* lam = (double*)c.take(sizeof(double));
+  void* dscratch = c.take(kCholScratchBytes);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_init_flags(flags, result, 1, st);
   if (e == hipSuccess)
-    e = launch_damp_cholesky(H, n, damp, prec, nullptr, L, dead, result, flags, lam, st);
+    e = launch_damp_cholesky(H, n, damp, prec, nullptr, L, dead, result, flags, lam, dscratch,
+                             st);
   if (e != hipSuccess) return hip_fail(e, "damp_cholesky launch");
   return ok();
 }
@@ -383,7 +388,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   }
   if (e == hipSuccess)
     e = launch_damp_cholesky(Hm, n, damp, prec, colmap, Lm, w.dead, result, w.flags, w.lam,
-                             st);
+                             w.dscratch, st);
   const bool colsp = grid->kind == PWQ_GRID_COLSPACING;
   const int G = colsp ? 1 : group_of(grid, n);
   if (e == hipSuccess && !colsp && m > 0)

@@ -24,9 +24,11 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype, in
                           int64_t ldx, int32_t accumulate, const SyrkPlan& p, void* partial,
                           hipStream_t st);
 
+// dscratch: kCholScratchBytes of workspace (diagonal blocks in flight).
+constexpr size_t kCholScratchBytes = 2 * 64 * 64 * sizeof(double);
 hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                                 const int32_t* perm, void* L, int32_t* dead, pwq_result* res,
-                                DevFlags* flags, double* lam, hipStream_t st);
+                                DevFlags* flags, double* lam, void* dscratch, hipStream_t st);
 
 hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
                              const int32_t* dead, int kind, int bits, int G, float* scales,
