@@ -354,28 +354,36 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
   const int r0 = base + ti * TB, c0 = base + tj * TB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  tile_to_lds<T, TB, NB, 256, LD>(As, tid, [&](int r, int k) {
-    return (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
-  });
-  if (!diag)
-    tile_to_lds<T, TB, NB, 256, LD>(Bs, tid, [&](int r, int k) {
-      return (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
-    });
-  __syncthreads();
-  const T* Bp = diag ? As : Bs;
+  // The accumulators start from the current tile (loads issued first, so
+  // their latency overlaps the panel loads) and the panel enters negated:
+  // acc = A_ij + sum (-P_ik) P_jk.
   if constexpr (sizeof(T) == 4) {
+    // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) {
+          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+          acc[i][j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0f;
+        }
+    tile_to_lds<T, TB, NB, 256, LD>(As, tid, [&](int r, int k) {
+      return (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
+    });
+    if (!diag)
+      tile_to_lds<T, TB, NB, 256, LD>(Bs, tid, [&](int r, int k) {
+        return (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
+      });
+    __syncthreads();
+    const T* Bp = diag ? As : Bs;
 #pragma unroll 8
     for (int k = 0; k < NB; k += 2) {
       const int ko = k + (lane >> 5);
-      const float a0 = As[(wm * 64 + (lane & 31)) * LD + ko];
-      const float a1 = As[(wm * 64 + 32 + (lane & 31)) * LD + ko];
+      const float a0 = -As[(wm * 64 + (lane & 31)) * LD + ko];
+      const float a1 = -As[(wm * 64 + 32 + (lane & 31)) * LD + ko];
       const float b0 = Bp[(wn * 64 + (lane & 31)) * LD + ko];
       const float b1 = Bp[(wn * 64 + 32 + (lane & 31)) * LD + ko];
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
@@ -383,8 +391,6 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
-    // epilogue: all loads first, then the stores
-    float old[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -393,33 +399,37 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
         for (int r = 0; r < 16; ++r) {
           const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          old[i][j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0f;
-        }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = old[i][j][r] - acc[i][j][r];
+          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = acc[i][j][r];
         }
   } else {
+    // 16x16 f64 result layout: lane l, register r -> row 4r + l/16, col l%16
     f64x4_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0;
+        for (int r = 0; r < 4; ++r) {
+          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+          acc[i][j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0;
+        }
+    tile_to_lds<T, TB, NB, 256, LD>(As, tid, [&](int r, int k) {
+      return (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
+    });
+    if (!diag)
+      tile_to_lds<T, TB, NB, 256, LD>(Bs, tid, [&](int r, int k) {
+        return (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
+      });
+    __syncthreads();
+    const T* Bp = diag ? As : Bs;
 #pragma unroll 4
     for (int k = 0; k < NB; k += 4) {
       const int ko = k + (lane >> 4);
       double av[4], bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        av[i] = As[(wm * 64 + i * 16 + (lane & 15)) * LD + ko];
+        av[i] = -As[(wm * 64 + i * 16 + (lane & 15)) * LD + ko];
         bv[i] = Bp[(wn * 64 + i * 16 + (lane & 15)) * LD + ko];
       }
 #pragma unroll
@@ -429,25 +439,15 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      double old[4][4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          old[j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0;
+          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = acc[i][j][r];
         }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
-          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = old[j][r] - acc[i][j][r];
-        }
-    }
   }
 }
 

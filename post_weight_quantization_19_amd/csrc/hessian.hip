@@ -241,11 +241,11 @@ constexpr int BL = 256;        // large tile edge
 constexpr int BKL = 32;        // tokens per stage
 constexpr int NSLOT = 5;       // LDS ring slots
 constexpr int AHEAD = 4;       // stages in flight ahead of the one computed
-#ifndef SYRK_NWAVE
-#define SYRK_NWAVE 8
-#endif
-constexpr int NWL = SYRK_NWAVE;  // waves per workgroup (8: 64x128 per wave, 4: 128x128)
-constexpr int NTL = 64 * NWL;    // threads
+// 8 waves of 64x128 (two per SIMD) measured faster than 4 waves of 128x128:
+// the second wave per SIMD hides LDS latency better than the halved LDS
+// traffic of the larger wave tile saves.
+constexpr int NWL = 8;         // waves per workgroup
+constexpr int NTL = 64 * NWL;  // threads
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
@@ -468,19 +468,26 @@ void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* 
   // Enough work items for a few rounds of workgroups; below that, a multiple
   // of 8 splits so that each XCD streams its own token range.
   const int64_t slots = big ? 256 : 512;      // resident workgroups
+  const int64_t maxs = stages / 8 > 0 ? stages / 8 : 1;  // >= 8 stages per split
   int64_t ns = 1;
-  if (p->ntiles < 3 * slots) {
+  if (p->ntiles < 3 * slots && big) {
+    // 8..16 splits: the count whose last round of workgroups is fullest,
+    // i.e. the least rounds x stages-per-split (ties: fewer partials)
+    int64_t best = -1;
+    for (int64_t c = 8; c <= 16; ++c) {
+      const int64_t cost = ((p->ntiles * c + slots - 1) / slots) * ((stages + c - 1) / c);
+      if (best < 0 || cost < best) {
+        best = cost;
+        ns = c;
+      }
+    }
+  } else if (p->ntiles < 3 * slots) {
     const int64_t want = (4 * slots + p->ntiles - 1) / p->ntiles;
     ns = (want + 7) / 8 * 8;
-    if (big && ns > 16) ns = 16;
   }
-  const int64_t maxs = stages / 8 > 0 ? stages / 8 : 1;  // >= 8 stages per split
   if (ns > maxs) ns = maxs;
   if (ns > 64) ns = 64;
   if (ns < 1) ns = 1;
-#ifdef SYRK_FORCE_NS
-  if (big) ns = SYRK_FORCE_NS;
-#endif
   int64_t kps = ((stages + ns - 1) / ns) * bk;
   if (kps < bk) kps = bk;           // ntok == 0: one empty split
   ns = (ntok + kps - 1) / kps;

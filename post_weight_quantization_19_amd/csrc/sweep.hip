@@ -250,14 +250,16 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int l
 // ------------------------------------------------------------ lazy update
 // acc[r, c] (+)= sum_{k < kb} E[r, e_off + k] * L[k_lo + k, c]
 //   for r < m and c in [c_lo, j0); "first" stores instead of adding.
-// 128 x 128 output tiles, K in chunks of 32 staged through LDS; the next
-// chunk's global loads are in flight while the current chunk's MFMAs run.
+// 128 x 128 output tiles.  The accumulators start from the current acc
+// values (their loads are issued first, so their latency overlaps the
+// operand loads and the MFMAs), K runs in chunks of 32 staged through LDS
+// with the next chunk's global loads in flight while the current chunk's
+// MFMAs run, and the tile is stored once.
 template <typename T>
-__global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int B, int e_off,
-                                                   int kb, const T* __restrict__ L, int n,
-                                                   int k_lo, int c_lo, int j0, int m,
-                                                   T* __restrict__ acc, int first,
-                                                   const DevFlags* flags) {
+__global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void lazy_update(
+    const T* __restrict__ E, int B, int e_off, int kb, const T* __restrict__ L, int n,
+    int k_lo, int c_lo, int j0, int m, T* __restrict__ acc, int first,
+    const DevFlags* flags) {
   constexpr int TM = 128, KC = 32, LDA = KC + 1, LDB = TM + 1;
   constexpr int PE = TM * KC / 256;   // elements per thread per operand
   __shared__ T Es[TM * LDA];
@@ -287,16 +289,21 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
       Lt[(e / TM) * LDB + e % TM] = rl[i];
     }
   };
-  gload(0);
 
   if constexpr (sizeof(T) == 4) {
+    // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
     f32x16_t cc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) {
+          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+          cc[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
+        }
+    gload(0);
     for (int kc = 0; kc < kb; kc += KC) {
       __syncthreads();
       lstore();
@@ -315,7 +322,6 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
         cc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, cc[1][1], 0, 0, 0);
       }
     }
-    float old[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -324,26 +330,22 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
         for (int r = 0; r < 16; ++r) {
           const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          old[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
-        }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = old[i][j][r] + cc[i][j][r];
+          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[i][j][r];
         }
   } else {
+    // 16x16 f64 result layout: lane l, register r -> row 4r + l/16, col l%16
     f64x4_t cc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cc[i][j][r] = 0.0;
+        for (int r = 0; r < 4; ++r) {
+          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+          cc[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0;
+        }
+    gload(0);
     for (int kc = 0; kc < kb; kc += KC) {
       __syncthreads();
       lstore();
@@ -366,26 +368,175 @@ __global__ __launch_bounds__(256) void lazy_update(const T* __restrict__ E, int 
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      double old[4][4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          old[j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0;
+          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[i][j][r];
         }
+  }
+}
+
+// fp32 form of the same update for 16-byte aligned rows of L (n % 4 == 0),
+// K <= 128.  Persistent, one 512-thread workgroup per CU: workgroup w owns
+// row strip w % nstrip (128 rows) and visits the column tiles w / nstrip,
+// w / nstrip + ngrp, ...  Each of the 8 waves keeps its 32 rows of E in
+// registers for the whole launch as the MFMA A operand; the tile's panel of
+// L (K x 128 columns, 64 KB) is copied into an LDS double buffer with
+// global_load_lds_dwordx4 while the previous tile computes, and the next
+// tile's acc values are loaded into registers at the same time, so HBM
+// traffic and MFMAs overlap.  K is visited in a permuted order so that a
+// lane's A values are four consecutive k of its row (one 16-byte load): in
+// group g, MFMA t pairs k = 8g + t (lanes 0..31) with k = 8g + 4 + t
+// (lanes 32..63).
+constexpr int UPD_NT = 512;
+__global__ __launch_bounds__(UPD_NT, 1) void lazy_update_f32(
+    const float* __restrict__ E, int B, int e_off, int kb, const float* __restrict__ L, int n,
+    int k_lo, int c_lo, int j0, int m, float* __restrict__ acc, int first, int nstrip,
+    int ngrp) {
+  constexpr int TM = 128, KMAX = 128;
+  __shared__ __attribute__((aligned(16))) float Ls[2][KMAX * TM];   // [k][col]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;   // rows 32 wm, cols 64 wn
+  const int ncol = (j0 - c_lo + TM - 1) / TM;
+  const int r0 = (blockIdx.x % nstrip) * TM;
+  const int tile0 = blockIdx.x / nstrip;
+  if (tile0 >= ncol) return;
+
+  // this wave's 32 rows of E: lane (row, h) holds k = 8g + 4h .. 8g + 4h + 3
+  f32x4_t ea[16];
+  {
+    const int gr = r0 + wm * 32 + (lane & 31);
+    const float* er = E + (int64_t)(gr < m ? gr : 0) * B + e_off + 4 * h;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int g = 0; g < 16; ++g) {
+      f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int k = 8 * g + 4 * h;
+      if (gr < m && k + 3 < kb) {
+        v = *(const f32x4_t*)(er + 8 * g);
+      } else if (gr < m && k < kb) {   // ragged end of K: element by element
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
-          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = old[j][r] + cc[i][j][r];
-        }
+        for (int t = 0; t < 4; ++t)
+          if (k + t < kb) v[t] = er[8 * g + t];
+      }
+      ea[g] = v;
     }
   }
+  // L panel rows k_lo .. k_lo + kb - 1, columns c0 .. c0 + 127 -> LDS
+  // buffer.  Rows past kb repeat row k_lo (their E values are zero); column
+  // chunks past n read the last chunk of the row (those outputs are not
+  // stored).
+  auto fetch_l = [&](int c0, int buf) {
+#pragma unroll
+    for (int i = 0; i < KMAX * TM / 4 / UPD_NT; ++i) {
+      const int ci = tid + UPD_NT * i;         // 16-byte chunk of the [k][col] panel
+      const int k = ci / (TM / 4), q = ci % (TM / 4);
+      const int row = k_lo + (k < kb ? k : 0);
+      const int col = min(c0 + 4 * q, n - 4);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(L + (int64_t)row * n + col),
+          (__attribute__((address_space(3))) void*)&Ls[buf][(wave * 64 + UPD_NT * i) * 4], 16,
+          0, 0);
+    }
+  };
+  // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
+  const int rbase = r0 + wm * 32 + 4 * (lane >> 5);
+  auto fetch_c = [&](int c0, f32x16_t (&cn)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = rbase + 8 * (r >> 2) + (r & 3);
+        cn[j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
+      }
+    }
+  };
+
+  f32x16_t cc[2], cn[2];
+  int t = tile0, buf = 0;
+  fetch_l(c_lo + t * TM, 0);
+  fetch_c(c_lo + t * TM, cn);
+  while (true) {
+    const int c0 = c_lo + t * TM;
+    __builtin_amdgcn_s_waitcnt(0);   // this tile's L panel and acc values (and the
+    __syncthreads();                 // previous tile's stores) have landed
+    cc[0] = cn[0];
+    cc[1] = cn[1];
+    const int tn = t + ngrp;
+    if (tn < ncol) {                 // the next tile's data, during this tile's MFMAs
+      fetch_l(c_lo + tn * TM, buf ^ 1);
+      fetch_c(c_lo + tn * TM, cn);
+    }
+    // Every group runs: past kb the E values are zero (and the L rows
+    // finite), so the extra products add exactly 0.  The B values of group
+    // g + 1 are read from LDS while group g's MFMAs run.
+    const float* Lb = Ls[buf] + 4 * h * TM + wn * 64 + (lane & 31);
+    float bv[2][4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      bv[0][tt][0] = Lb[tt * TM];
+      bv[0][tt][1] = Lb[tt * TM + 32];
+    }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      if (g + 1 < 16) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          bv[(g + 1) & 1][tt][0] = Lb[(8 * (g + 1) + tt) * TM];
+          bv[(g + 1) & 1][tt][1] = Lb[(8 * (g + 1) + tt) * TM + 32];
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        cc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(ea[g][tt], bv[g & 1][tt][0], cc[0], 0, 0, 0);
+        cc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(ea[g][tt], bv[g & 1][tt][1], cc[1], 0, 0, 0);
+      }
+      // keep that order: the next group's 4 LDS reads first, then these 8
+      // MFMAs (left alone, the scheduler sinks each read to its use)
+      if (g + 1 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = rbase + 8 * (r >> 2) + (r & 3);
+        if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[j][r];
+      }
+    }
+    if (tn >= ncol) break;
+    t = tn;
+    buf ^= 1;
+  }
+}
+
+// One lazy update launch (either form).
+template <typename T>
+void update_launch(const T* E, int B, int e_off, int kb, const T* L, int n, int k_lo, int c_lo,
+                   int j0, int m, T* acc, int first, const DevFlags* flags, hipStream_t st) {
+  dim3 g((unsigned)((j0 - c_lo + 127) / 128), (unsigned)((m + 127) / 128));
+  if constexpr (sizeof(T) == 4) {
+    if (n % 4 == 0 && ((uintptr_t)L % 16) == 0 && ((uintptr_t)E % 16) == 0 && B % 4 == 0 &&
+        e_off % 4 == 0) {
+      // one workgroup per CU: every row strip, as many column groups as fit
+      const int nstrip = (m + 127) / 128;
+      const int ncol = (j0 - c_lo + 127) / 128;
+      int ngrp = 256 / nstrip;
+      if (ngrp < 1) ngrp = 1;
+      if (ngrp > ncol) ngrp = ncol;
+      for (int kh = 0; kh < kb; kh += 128)   // K <= 128 per launch
+        lazy_update_f32<<<(unsigned)(nstrip * ngrp), UPD_NT, 0, st>>>(
+            E, B, e_off + kh, min(128, kb - kh), L, n, k_lo + kh, c_lo, j0, m, acc,
+            first && kh == 0, nstrip, ngrp);
+      return;
+    }
+  }
+  lazy_update<T><<<g, 256, 0, st>>>(E, B, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first, flags);
 }
 
 // ---------------------------------------------------------------- finalize
@@ -456,7 +607,6 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
   const int n = (int)sl.n, m = (int)sl.m, B = sl.block;
   const int nblk = (n + B - 1) / B;
   const unsigned nwg = (unsigned)((m + 15) / 16);
-  const unsigned mt = (unsigned)((m + 127) / 128);
   int part = 0;
   for (int b = nblk - 1; b >= 0 && nwg > 0; --b) {
     const int jb0 = b * B, jb1 = (n < jb0 + B) ? n : jb0 + B;
@@ -468,16 +618,13 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
       if (s > 0) {
         // the sub-block's errors reach the open columns of its own block
         const int kb = (jb1 - js0 < Bi) ? jb1 - js0 : Bi;
-        dim3 g((unsigned)((js0 - jb0 + 127) / 128), mt);
-        lazy_update<T><<<g, 256, 0, st>>>((const T*)sl.E, B, js0 - jb0, kb, (const T*)sl.L, n,
-                                          js0, jb0, js0, m, (T*)sl.acc, first_sub, sl.flags);
+        update_launch<T>((const T*)sl.E, B, js0 - jb0, kb, (const T*)sl.L, n, js0, jb0, js0, m,
+                         (T*)sl.acc, first_sub, sl.flags, st);
       }
     }
-    if (jb0 > 0) {
-      dim3 g((unsigned)((jb0 + 127) / 128), mt);
-      lazy_update<T><<<g, 256, 0, st>>>((const T*)sl.E, B, 0, jb1 - jb0, (const T*)sl.L, n, jb0,
-                                        0, jb0, m, (T*)sl.acc, b == nblk - 1, sl.flags);
-    }
+    if (jb0 > 0)   // the block's errors reach every earlier column
+      update_launch<T>((const T*)sl.E, B, 0, jb1 - jb0, (const T*)sl.L, n, jb0, 0, jb0, m,
+                       (T*)sl.acc, b == nblk - 1, sl.flags, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
