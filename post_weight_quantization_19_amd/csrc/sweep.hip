@@ -392,6 +392,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void lazy_update(
 // lane's A values are four consecutive k of its row (one 16-byte load): in
 // group g, MFMA t pairs k = 8g + t (lanes 0..31) with k = 8g + 4 + t
 // (lanes 32..63).
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= v, expcnt and lgkmcnt not waited for.
+constexpr int waitcnt_vm(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70 | 0xF00; }
+
 constexpr int UPD_NT = 512;
 __global__ __launch_bounds__(UPD_NT, 1) void lazy_update_f32(
     const float* __restrict__ E, int B, int e_off, int kb, const float* __restrict__ L, int n,
@@ -442,76 +445,86 @@ __global__ __launch_bounds__(UPD_NT, 1) void lazy_update_f32(
           0, 0);
     }
   };
+  // acc goes through a buffer resource: an element outside the tile's valid
+  // range gets an out-of-range offset, so its load returns 0 and its store
+  // is dropped, and every lane issues the same 32 loads / 32 stores per tile
+  // (the in-order vmcnt wait below relies on that count).
+  const __amdgpu_buffer_rsrc_t racc =
+      __builtin_amdgcn_make_buffer_rsrc(acc, 0, m * n * 4, 0x00020000);
   // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
   const int rbase = r0 + wm * 32 + 4 * (lane >> 5);
+  auto c_off = [&](int c0, int j, int r) -> int {
+    const int gr = rbase + 8 * (r >> 2) + (r & 3);
+    const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+    return (gr < m && gc < j0) ? (gr * n + gc) * 4 : -1;
+  };
+  // on the first block acc is written, not read: every load is out of range
+  const int lmask = first ? -1 : 0;
   auto fetch_c = [&](int c0, f32x16_t (&cn)[2]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = rbase + 8 * (r >> 2) + (r & 3);
-        cn[j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
-      }
-    }
+      for (int r = 0; r < 16; ++r)
+        cn[j][r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(racc, c_off(c0, j, r) | lmask, 0, 0));
   };
 
-  f32x16_t cc[2], cn[2];
-  int t = tile0, buf = 0;
-  fetch_l(c_lo + t * TM, 0);
-  fetch_c(c_lo + t * TM, cn);
-  while (true) {
+  // One tile: its acc values (already in `cur`) += E L; the next tile's L
+  // panel and acc values go to the other buffer and `nxt` meanwhile.
+  // Returns false after the last tile.  Two register sets alternate, so the
+  // loop below is unrolled by two.
+  int t = tile0;
+  auto step = [&](f32x16_t (&cur)[2], f32x16_t (&nxt)[2], int buf) -> bool {
     const int c0 = c_lo + t * TM;
-    __builtin_amdgcn_s_waitcnt(0);   // this tile's L panel and acc values (and the
-    __syncthreads();                 // previous tile's stores) have landed
-    cc[0] = cn[0];
-    cc[1] = cn[1];
+    // This tile's L panel and acc values were issued before the previous
+    // tile's 32 stores; vector memory counts complete in order, so waiting
+    // until at most 32 remain leaves only those stores in flight.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(32));
+    lds_barrier();
     const int tn = t + ngrp;
-    if (tn < ncol) {                 // the next tile's data, during this tile's MFMAs
+    if (tn < ncol) {
       fetch_l(c_lo + tn * TM, buf ^ 1);
-      fetch_c(c_lo + tn * TM, cn);
+      // all LDS copies before the acc loads: a copy placed after them makes
+      // the compiler wait for every outstanding load first
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_c(c_lo + tn * TM, nxt);
     }
     // Every group runs: past kb the E values are zero (and the L rows
-    // finite), so the extra products add exactly 0.  The B values of group
-    // g + 1 are read from LDS while group g's MFMAs run.
+    // finite), so the extra products add exactly 0.  Each group's 4 LDS
+    // reads are issued together ahead of its 8 MFMAs.
     const float* Lb = Ls[buf] + 4 * h * TM + wn * 64 + (lane & 31);
-    float bv[2][4][2];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      bv[0][tt][0] = Lb[tt * TM];
-      bv[0][tt][1] = Lb[tt * TM + 32];
-    }
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      if (g + 1 < 16) {
+      float bv[4][2];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          bv[(g + 1) & 1][tt][0] = Lb[(8 * (g + 1) + tt) * TM];
-          bv[(g + 1) & 1][tt][1] = Lb[(8 * (g + 1) + tt) * TM + 32];
-        }
+      for (int tt = 0; tt < 4; ++tt) {
+        bv[tt][0] = Lb[(8 * g + tt) * TM];
+        bv[tt][1] = Lb[(8 * g + tt) * TM + 32];
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        cc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(ea[g][tt], bv[g & 1][tt][0], cc[0], 0, 0, 0);
-        cc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(ea[g][tt], bv[g & 1][tt][1], cc[1], 0, 0, 0);
+        cur[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(ea[g][tt], bv[tt][0], cur[0], 0, 0, 0);
+        cur[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(ea[g][tt], bv[tt][1], cur[1], 0, 0, 0);
       }
-      // keep that order: the next group's 4 LDS reads first, then these 8
-      // MFMAs (left alone, the scheduler sinks each read to its use)
-      if (g + 1 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = rbase + 8 * (r >> 2) + (r & 3);
-        if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[j][r];
-      }
-    }
-    if (tn >= ncol) break;
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur[j][r]), racc,
+                                              c_off(c0, j, r), 0, 0);
     t = tn;
-    buf ^= 1;
+    return tn < ncol;
+  };
+
+  f32x16_t ca[2], cb[2];
+  fetch_l(c_lo + t * TM, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_c(c_lo + t * TM, ca);
+  __builtin_amdgcn_s_waitcnt(0);     // E, the first L panel and acc values
+  while (step(ca, cb, 0) && step(cb, ca, 1)) {
   }
 }
 
@@ -522,7 +535,7 @@ void update_launch(const T* E, int B, int e_off, int kb, const T* L, int n, int 
   dim3 g((unsigned)((j0 - c_lo + 127) / 128), (unsigned)((m + 127) / 128));
   if constexpr (sizeof(T) == 4) {
     if (n % 4 == 0 && ((uintptr_t)L % 16) == 0 && ((uintptr_t)E % 16) == 0 && B % 4 == 0 &&
-        e_off % 4 == 0) {
+        e_off % 4 == 0 && (int64_t)m * n * 4 < ((int64_t)1 << 31)) {
       // one workgroup per CU: every row strip, as many column groups as fit
       const int nstrip = (m + 127) / 128;
       const int ncol = (j0 - c_lo + 127) / 128;
