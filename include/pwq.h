@@ -213,6 +213,24 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
                            void* L_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- *
+ * Rate: the empirical Shannon entropy of each column's codes, in bits
+ * [WSIC 2, items 1 and 3: columns get unequal rates and the unclipped codes
+ * are entropy coded, so a column's rate is the entropy of its codes].
+ *   codes : m x n int32, row stride ldc >= n (as written by pwq_quant_layer
+ *           or pwq_babai_sweep; zero points make no difference).
+ *   bits  : n doubles: bits[k] = -sum_v p_v log2 p_v over the distinct
+ *           values v of column k, p_v = (count of v) / m; 0 when m = 0;
+ *           NaN for a column whose codes span more than 32768 values.
+ *   mean   : optional double: the mean of bits over the n columns.
+ *   ws     : pwq_rate_workspace_size(n) bytes.
+ * Counts are exact (integer), and the sums run in a fixed order.
+ * ---------------------------------------------------------------------- */
+size_t pwq_rate_workspace_size(int64_t n);
+pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                              double* bits, double* mean, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* ---------------------------------------------------------------------- *
  * Kernel timing hook (measurement only; no effect on any result).
  * Attaches caller-owned HIP events (hipEvent_t handles) to one kernel:
  * after attach, launch i (i = 0 .. capacity-1) of that kernel records

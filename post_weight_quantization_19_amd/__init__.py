@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import PwqError, check, lib, make_grid, parse_result
 
 __all__ = ["Grid", "hessian_accum", "damp_cholesky", "grid_steps", "babai_sweep",
-           "quant_layer", "read_result", "PwqError", "HessianTileTimer"]
+           "quant_layer", "column_entropy", "read_result", "PwqError", "HessianTileTimer"]
 
 
 @dataclass(frozen=True)
@@ -196,6 +196,23 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
         o["result"].data_ptr(), _ptr(o.get("H")), _ptr(o.get("L")), ws.data_ptr(),
         ws.numel(), _stream()))
     return o
+
+
+def column_entropy(codes: torch.Tensor):
+    """Per-column empirical entropy (bits) of int32 codes [m, n] and its mean
+    over the columns: (bits [n] float64, mean [] float64), both on the GPU."""
+    _require_cuda(codes)
+    if codes.dtype != torch.int32:
+        raise TypeError("codes must be int32")
+    m, n = codes.shape
+    ldc = _row_major(codes) if m > 0 else n
+    bits = torch.empty(n, dtype=torch.float64, device=codes.device)
+    mean = torch.empty((), dtype=torch.float64, device=codes.device)
+    L_ = lib()
+    ws = _workspace(L_.pwq_rate_workspace_size(n), codes.device)
+    check(L_.pwq_column_entropy(codes.data_ptr(), m, n, ldc, bits.data_ptr(), mean.data_ptr(),
+                                ws.data_ptr(), ws.numel(), _stream()))
+    return bits, mean
 
 
 class HessianTileTimer:

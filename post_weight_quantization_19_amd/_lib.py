@@ -24,6 +24,7 @@ EXPORTS = [
     "pwq_grid_steps",
     "pwq_sweep_workspace_size", "pwq_babai_sweep",
     "pwq_quant_layer_workspace_size", "pwq_quant_layer",
+    "pwq_rate_workspace_size", "pwq_column_entropy",
     "pwq_kernel_timer_attach", "pwq_kernel_timer_count",
 ]
 PWQ_TIMER_HESSIAN_TILES = 0
@@ -66,6 +67,8 @@ _SIGS = {
     "pwq_quant_layer": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _i64, _i64, _vp,
                                ctypes.POINTER(PwqGrid), _i32, _vp, _f64, _i32, _i32, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_rate_workspace_size": (_sz, [_i64]),
+    "pwq_column_entropy": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "pwq_kernel_timer_attach": (_i32, [_i32, _vp, _vp, _i64]),
     "pwq_kernel_timer_count": (_i64, []),
 }

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpwq.so")
-SOURCES = ["pwq_api.hip", "hessian.hip", "cholesky.hip", "sweep.hip", "order.hip"]
+SOURCES = ["pwq_api.hip", "hessian.hip", "cholesky.hip", "sweep.hip", "order.hip", "rate.hip"]
 ARCH = "gfx950"
 
 

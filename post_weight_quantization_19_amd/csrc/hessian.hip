@@ -426,19 +426,35 @@ __global__ __launch_bounds__(256) void syrk_reduce(
   const int r0 = ti * TE + qr, c0 = tj * TE + qc;
   if (ti == tj && qr < qc) return;  // strictly-upper sub-block of a diagonal tile
   const int tid = threadIdx.x;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int lr = e >> 6, lc = e & 63;
-    const int64_t off = (int64_t)(qr + lr) * TE + qc + lc;
-    float s = 0.0f;
+  const int64_t split_stride = (int64_t)ntiles * (TE * TE) / 4;   // float4 units
+  // four float4 per thread; every split's loads of them in flight together,
+  // summed in split order
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int e4 = tid + 256 * v;
+    const int lr = e4 >> 4, lc = (e4 & 15) * 4;
+    const float4* src = (const float4*)(partial + (int64_t)tile * (TE * TE) +
+                                        (int64_t)(qr + lr) * TE + qc + lc);
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 8
-    for (int sp = 0; sp < nsplit; ++sp) s += partial[((int64_t)sp * ntiles + tile) * (TE * TE) + off];
-    const int gr = r0 + lr, gc = c0 + lc;
-    float v = 2.0f * s;
-    if (gr < n && gc < n && gc <= gr) {
-      if (accumulate) v += H[(int64_t)gr * n + gc];
-      H[(int64_t)gr * n + gc] = v;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float4 p = src[sp * split_stride];
+      s.x += p.x;
+      s.y += p.y;
+      s.z += p.z;
+      s.w += p.w;
     }
-    T[lr][lc] = v;
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gr = r0 + lr, gc = c0 + lc + u;
+      float val = 2.0f * sv[u];
+      if (gr < n && gc < n && gc <= gr) {
+        if (accumulate) val += H[(int64_t)gr * n + gc];
+        H[(int64_t)gr * n + gc] = val;
+      }
+      T[lr][lc + u] = val;
+    }
   }
   __syncthreads();
   // mirrored writes, coalesced along the destination row

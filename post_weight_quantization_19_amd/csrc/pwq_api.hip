@@ -410,6 +410,34 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   return ok();
 }
 
+size_t pwq_rate_workspace_size(int64_t n) {
+  if (n <= 0) return 0;
+  Carver c(nullptr);
+  c.take((size_t)n * 4);
+  c.take((size_t)n * 4);
+  return c.size();
+}
+
+pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                              double* bits, double* mean, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (m < 0 || n < 0 || m > INT32_MAX || n > INT32_MAX)
+    return fail(PWQ_ERR_INVALID_ARG, "m and n must be in [0, 2^31)");
+  if (ldc < n) return fail(PWQ_ERR_INVALID_ARG, "ldc (%lld) < n (%lld)", (long long)ldc,
+                           (long long)n);
+  if (n > 0 && (!bits || (m > 0 && !codes)))
+    return fail(PWQ_ERR_INVALID_ARG, "codes and bits must be non-NULL");
+  pwq_status s = check_ws(ws, ws_bytes, pwq_rate_workspace_size(n));
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  int32_t* cmin = n > 0 ? (int32_t*)c.take((size_t)n * 4) : nullptr;
+  int32_t* cmax = n > 0 ? (int32_t*)c.take((size_t)n * 4) : nullptr;
+  const hipError_t e = launch_column_entropy(codes, m, n, ldc, bits, mean, cmin, cmax,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "column_entropy launch");
+  return ok();
+}
+
 pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* const* stops,
                                    int64_t capacity) {
   if (kernel != PWQ_TIMER_HESSIAN_TILES)

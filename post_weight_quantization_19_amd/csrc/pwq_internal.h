@@ -67,6 +67,11 @@ hipError_t launch_order(int32_t order_kind, const float* H, int64_t n, const int
                         hipStream_t st);
 hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, hipStream_t st);
 
+// cmin / cmax: n int32 each of workspace.
+hipError_t launch_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                                 double* bits, double* mean, int32_t* cmin, int32_t* cmax,
+                                 hipStream_t st);
+
 // Event pairs recorded around launches of one kernel (pwq_kernel_timer_attach).
 struct KernelTimer {
   hipEvent_t* starts = nullptr;

@@ -38,6 +38,7 @@ namespace {
 
 // ---------------------------------------------------------------- steps
 
+// One 16-lane quarter of a wave per (row, group): 16 groups per workgroup.
 __global__ __launch_bounds__(256) void grid_steps_kernel(
     const void* __restrict__ W, int32_t wdtype, int m, int n, int64_t ldw,
     const int32_t* __restrict__ dead, int kind, int bits, int G,
@@ -45,21 +46,27 @@ __global__ __launch_bounds__(256) void grid_steps_kernel(
     const DevFlags* flags) {
   if (flags && flags->info != 0) return;
   const int ng = n / G;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wid >= m * ng) return;
-  const int r = wid / ng, g = wid % ng;
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = gid < (int64_t)m * ng;
+  const int r = live ? (int)(gid / ng) : 0, g = live ? (int)(gid % ng) : 0;
   float mx = -INFINITY, mn = INFINITY, amax = 0.0f;
-  for (int c = g * G + lane; c < (g + 1) * G; c += 64) {
-    float w = load_w<float>(W, wdtype, (int64_t)r * ldw + c);
-    if (dead && dead[c]) w = 0.0f;
-    mx = fmaxf(mx, w);
-    mn = fminf(mn, w);
-    amax = fmaxf(amax, fabsf(w));
+  if (live) {
+    for (int c = g * G + sub; c < (g + 1) * G; c += 16) {
+      float w = load_w<float>(W, wdtype, (int64_t)r * ldw + c);
+      if (dead && dead[c]) w = 0.0f;
+      mx = fmaxf(mx, w);
+      mn = fminf(mn, w);
+      amax = fmaxf(amax, fabsf(w));
+    }
   }
-  mx = wave_max(mx);
-  mn = wave_min(mn);
-  amax = wave_max(amax);
-  if (lane != 0) return;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+    mn = fminf(mn, __shfl_xor(mn, o, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  }
+  if (!live || sub != 0) return;
   if (kind == PWQ_GRID_SYM) {
     float s = amax / (float)((1 << (bits - 1)) - 1);
     if (s == 0.0f) s = 1.0f;
@@ -650,8 +657,8 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
 hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
                              const int32_t* dead, int kind, int bits, int G, float* scales,
                              int32_t* zeros, const DevFlags* flags, hipStream_t st) {
-  const int64_t waves = m * (n / G);
-  grid_steps_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, st>>>(
+  const int64_t groups = m * (n / G);
+  grid_steps_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, st>>>(
       W, wdtype, (int)m, (int)n, ldw, dead, kind, bits, G, scales, zeros, flags);
   return hipGetLastError();
 }

@@ -25,7 +25,7 @@ def header_functions():
 def test_exports_match_header():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert sorted(B.EXPORTS) == names
     for nm in names:
         assert getattr(L, nm) is not None
@@ -141,3 +141,14 @@ def test_kernel_timer_validation():
     assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, 4) == INVALID
     assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, 0) == OK
     assert L.pwq_kernel_timer_count() == 0
+
+
+def test_rate_validation():
+    L = B.lib()
+    assert L.pwq_rate_workspace_size(0) == 0
+    assert L.pwq_rate_workspace_size(100) >= 800
+    assert L.pwq_column_entropy(FAKE, -1, 8, 8, FAKE, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(FAKE, 4, 8, 4, FAKE, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(None, 4, 8, 8, FAKE, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(FAKE, 4, 8, 8, None, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(FAKE, 4, 8, 8, FAKE, None, None, 0, None) == WS
