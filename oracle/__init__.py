@@ -6,7 +6,8 @@ runs anything here, and nothing here imports the HIP path.
 """
 from .babai_oracle import (babai_bound, babai_gram_schmidt, certificate,
                            cholesky_lower, colspacing_steps,
-                           column_entropy_bits, cvp_box, cvp_enumerate,
+                           column_entropy_bits, column_huffman_bits, cvp_box,
+                           cvp_enumerate, huffman_cost,
                            expand_group_steps, fix_dead_and_damp,
                            gamma_ratio, gptq_obs_sweep, grid_steps, hessian,
                            nearest_plane_sweep, nearest_plane_sweep_blocked,

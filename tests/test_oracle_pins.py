@@ -366,6 +366,29 @@ def test_column_entropy():
     np.testing.assert_allclose(O.column_entropy_bits(codes), [2.0, 0.0, 1.0])
 
 
+def test_huffman_cost_pins():
+    """Huffman totals against closed forms: a dyadic distribution is coded at
+    exactly its entropy; two symbols cost one bit each; one symbol costs
+    nothing; a hand-built tree; and for any counts the mean length lies in
+    [H, H + 1) (Shannon's bounds)."""
+    assert O.huffman_cost([7]) == 0
+    assert O.huffman_cost([3, 5]) == 8
+    # p = 1/2, 1/4, 1/8, 1/8 -> lengths 1, 2, 3, 3
+    assert O.huffman_cost([4, 2, 1, 1]) == 4 * 1 + 2 * 2 + 1 * 3 + 1 * 3
+    # counts 5, 9, 12, 13, 16, 45 -> lengths 4, 4, 3, 3, 3, 1 (by hand)
+    assert O.huffman_cost([5, 9, 12, 13, 16, 45]) == 5 * 4 + 9 * 4 + 12 * 3 + 13 * 3 + 16 * 3 + 45
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        cnt = rng.integers(1, 1000, size=rng.integers(2, 40))
+        m = cnt.sum()
+        p = cnt / m
+        H = -np.sum(p * np.log2(p))
+        L = O.huffman_cost(cnt) / m
+        assert H - 1e-12 <= L < H + 1
+    codes = np.array([[0, 1, 5], [1, 1, 5], [2, 1, 6], [3, 1, 6]])
+    np.testing.assert_array_equal(O.column_huffman_bits(codes), [8, 0, 4])
+
+
 def test_damping_hand_example():
     """[OAEM 3] damped form H + lambda I; reading lambda = damp * mean diag H.
     By hand: mean diag of [[4,2,2],[2,5,3],[2,3,6]] is 5, damp 0.2 -> 1."""
