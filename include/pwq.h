@@ -215,20 +215,29 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
 /* ---------------------------------------------------------------------- *
  * Rate: the empirical Shannon entropy of each column's codes, in bits
  * [WSIC 2, items 1 and 3: columns get unequal rates and the unclipped codes
- * are entropy coded, so a column's rate is the entropy of its codes].
+ * are entropy coded, so a column's rate is the entropy of its codes], and
+ * optionally their Huffman-coded length [GEOM 3, HPTQ: the unconstrained
+ * integer codes are Huffman coded].
  *   codes : m x n int32, row stride ldc >= n (as written by pwq_quant_layer
  *           or pwq_babai_sweep; zero points make no difference).
  *   bits  : n doubles: bits[k] = -sum_v p_v log2 p_v over the distinct
  *           values v of column k, p_v = (count of v) / m; 0 when m = 0;
  *           NaN for a column whose codes span more than 32768 values.
- *   mean   : optional double: the mean of bits over the n columns.
- *   ws     : pwq_rate_workspace_size(n) bytes.
- * Counts are exact (integer), and the sums run in a fixed order.
+ *   mean  : optional double: the mean of bits over the n columns.
+ *   huff  : optional n int64: total length in bits of column k's m codes
+ *           under a Huffman code built for that column (codebook not
+ *           counted; one distinct value costs 0); -1 where not computed (a
+ *           span above 32768 values, or more than 16385 distinct values in
+ *           a column spanning more than 512).
+ *   ws    : pwq_rate_workspace_size(n) bytes.
+ * Counts are exact (integer), and the sums run in a fixed order; the
+ * Huffman totals are exact integers (every optimal prefix code of the same
+ * counts has the same total).
  * ---------------------------------------------------------------------- */
 size_t pwq_rate_workspace_size(int64_t n);
 pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
-                              double* bits, double* mean, void* ws, size_t ws_bytes,
-                              void* stream);
+                              double* bits, double* mean, int64_t* huff, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- *
  * Kernel timing hook (measurement only; no effect on any result).

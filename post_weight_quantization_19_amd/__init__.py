@@ -198,9 +198,11 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
     return o
 
 
-def column_entropy(codes: torch.Tensor):
+def column_entropy(codes: torch.Tensor, huffman: bool = False):
     """Per-column empirical entropy (bits) of int32 codes [m, n] and its mean
-    over the columns: (bits [n] float64, mean [] float64), both on the GPU."""
+    over the columns: (bits [n] float64, mean [] float64), both on the GPU;
+    with ``huffman`` also each column's Huffman-coded length in bits
+    ([n] int64, -1 where not computed) as a third element."""
     _require_cuda(codes)
     if codes.dtype != torch.int32:
         raise TypeError("codes must be int32")
@@ -208,11 +210,12 @@ def column_entropy(codes: torch.Tensor):
     ldc = _row_major(codes) if m > 0 else n
     bits = torch.empty(n, dtype=torch.float64, device=codes.device)
     mean = torch.empty((), dtype=torch.float64, device=codes.device)
+    huff = torch.empty(n, dtype=torch.int64, device=codes.device) if huffman else None
     L_ = lib()
     ws = _workspace(L_.pwq_rate_workspace_size(n), codes.device)
     check(L_.pwq_column_entropy(codes.data_ptr(), m, n, ldc, bits.data_ptr(), mean.data_ptr(),
-                                ws.data_ptr(), ws.numel(), _stream()))
-    return bits, mean
+                                _ptr(huff), ws.data_ptr(), ws.numel(), _stream()))
+    return (bits, mean, huff) if huffman else (bits, mean)
 
 
 class HessianTileTimer:

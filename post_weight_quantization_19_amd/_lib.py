@@ -68,7 +68,7 @@ _SIGS = {
                                ctypes.POINTER(PwqGrid), _i32, _vp, _f64, _i32, _i32, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_rate_workspace_size": (_sz, [_i64]),
-    "pwq_column_entropy": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_column_entropy": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_kernel_timer_attach": (_i32, [_i32, _vp, _vp, _i64]),
     "pwq_kernel_timer_count": (_i64, []),
 }

@@ -419,8 +419,8 @@ size_t pwq_rate_workspace_size(int64_t n) {
 }
 
 pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
-                              double* bits, double* mean, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              double* bits, double* mean, int64_t* huff, void* ws,
+                              size_t ws_bytes, void* stream) {
   if (m < 0 || n < 0 || m > INT32_MAX || n > INT32_MAX)
     return fail(PWQ_ERR_INVALID_ARG, "m and n must be in [0, 2^31)");
   if (ldc < n) return fail(PWQ_ERR_INVALID_ARG, "ldc (%lld) < n (%lld)", (long long)ldc,
@@ -432,7 +432,7 @@ pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_
   Carver c(ws);
   int32_t* cmin = n > 0 ? (int32_t*)c.take((size_t)n * 4) : nullptr;
   int32_t* cmax = n > 0 ? (int32_t*)c.take((size_t)n * 4) : nullptr;
-  const hipError_t e = launch_column_entropy(codes, m, n, ldc, bits, mean, cmin, cmax,
+  const hipError_t e = launch_column_entropy(codes, m, n, ldc, bits, mean, huff, cmin, cmax,
                                              (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "column_entropy launch");
   return ok();

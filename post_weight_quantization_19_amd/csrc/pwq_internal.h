@@ -69,8 +69,8 @@ hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, h
 
 // cmin / cmax: n int32 each of workspace.
 hipError_t launch_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
-                                 double* bits, double* mean, int32_t* cmin, int32_t* cmax,
-                                 hipStream_t st);
+                                 double* bits, double* mean, int64_t* huff, int32_t* cmin,
+                                 int32_t* cmax, hipStream_t st);
 
 // Event pairs recorded around launches of one kernel (pwq_kernel_timer_attach).
 struct KernelTimer {

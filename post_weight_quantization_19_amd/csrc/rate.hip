@@ -14,6 +14,14 @@
 // summed in bin order per lane and reduced in a fixed order (deterministic).
 // Columns whose code range exceeds 512 values are done by colhist_wide, one
 // workgroup per column with a 32768-bin histogram; wider ranges give NaN.
+//
+// Huffman-coded length ("The Geometry of LLM Quantization ...", technical
+// summary 3, HPTQ: the unconstrained integer codes are Huffman coded): the
+// column's counts are sorted (bitonic network in LDS) and merged with the
+// two-queue method -- leaves in ascending order in one queue, merged nodes
+// (non-decreasing) in the other, each step joins the two smallest fronts --
+// and the total length is the sum of the merged weights, an integer that
+// every optimal prefix code of those counts shares.
 #include "pwq_device.h"
 #include "pwq_internal.h"
 
@@ -64,11 +72,60 @@ __device__ __forceinline__ double entropy_from_hist(const int32_t* h, int nbin, 
   return wave_sum(s);
 }
 
+// Sort h[0..len) ascending in place (len a power of two); the calling
+// threads tid = 0 .. nthr-1 of a wave or workgroup take the compare-exchange
+// pairs in turn; `sync` orders the stages.
+template <typename Sync>
+__device__ __forceinline__ void bitonic_sort(int32_t* h, int len, int tid, int nthr, Sync&& sync) {
+  for (int size = 2; size <= len; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < len / 2; t += nthr) {
+        const int i = (t / stride) * 2 * stride + (t % stride), j = i + stride;
+        const int32_t a = h[i], b = h[j];
+        const bool asc = (i & size) == 0;
+        if ((a > b) == asc) {
+          h[i] = b;
+          h[j] = a;
+        }
+      }
+      sync();
+    }
+}
+
+// Two-queue Huffman total over the ascending counts leaf[lo..hi) (zeros
+// already skipped); merged weights go to node[] (capacity hi - lo).  One
+// thread.
+__device__ __forceinline__ int64_t huffman_merge(const int32_t* leaf, int lo, int hi,
+                                                 int32_t* node) {
+  int li = lo, nh = 0, nt = 0;
+  int64_t total = 0;
+  auto pop = [&]() -> int32_t {
+    if (nh < nt && (li >= hi || node[nh] < leaf[li])) return node[nh++];
+    return leaf[li++];
+  };
+  for (int left = hi - lo; left > 1; --left) {
+    const int32_t a = pop();
+    const int32_t b = pop();
+    const int32_t w = a + b;
+    total += w;
+    node[nt++] = w;
+  }
+  return total;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS accesses done
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __global__ __launch_bounds__(256) void colhist(const int32_t* __restrict__ codes, int m, int n,
                                                int64_t ldc, const int32_t* __restrict__ cmin,
                                                const int32_t* __restrict__ cmax,
-                                               double* __restrict__ bits) {
+                                               double* __restrict__ bits,
+                                               int64_t* __restrict__ huff) {
   __shared__ int32_t hist[RC][NBIN];    // 128 KB
+  __shared__ int32_t nodes[4][NBIN];    // Huffman node queue per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = blockIdx.x * RC;
   for (int i = tid; i < RC * NBIN; i += 256) (&hist[0][0])[i] = 0;
@@ -87,6 +144,15 @@ __global__ __launch_bounds__(256) void colhist(const int32_t* __restrict__ codes
     if ((int64_t)cmax[cj] - cmin[cj] >= NBIN) continue;     // colhist_wide
     const double h = m > 0 ? entropy_from_hist(hist[j], NBIN, m) : 0.0;
     if (lane == 0) bits[cj] = h;
+    if (huff) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      bitonic_sort(hist[j], NBIN, lane, 64, wave_lds_sync);
+      int nz = 0;                                  // zero counts come first
+      for (int b = lane; b < NBIN; b += 64) nz += hist[j][b] == 0;
+      for (int o = 32; o >= 1; o >>= 1) nz += __shfl_xor(nz, o, 64);
+      if (lane == 0) huff[cj] = huffman_merge(hist[j], nz, NBIN, nodes[wave]);
+      wave_lds_sync();
+    }
   }
 }
 
@@ -94,13 +160,18 @@ __global__ __launch_bounds__(256) void colhist_wide(const int32_t* __restrict__ 
                                                     int64_t ldc,
                                                     const int32_t* __restrict__ cmin,
                                                     const int32_t* __restrict__ cmax,
-                                                    double* __restrict__ bits) {
+                                                    double* __restrict__ bits,
+                                                    int64_t* __restrict__ huff) {
   __shared__ int32_t hist[NBIN_WIDE];   // 128 KB
+  __shared__ int32_t nzs[4];
   const int col = blockIdx.x;
   const int64_t range = (int64_t)cmax[col] - cmin[col] + 1;
   if (range <= NBIN) return;            // done by colhist
   if (range > NBIN_WIDE) {
-    if (threadIdx.x == 0) bits[col] = __builtin_nan("");
+    if (threadIdx.x == 0) {
+      bits[col] = __builtin_nan("");
+      if (huff) huff[col] = -1;
+    }
     return;
   }
   for (int i = threadIdx.x; i < NBIN_WIDE; i += 256) hist[i] = 0;
@@ -112,6 +183,19 @@ __global__ __launch_bounds__(256) void colhist_wide(const int32_t* __restrict__ 
   if (threadIdx.x < 64) {
     const double h = entropy_from_hist(hist, (int)range, m);
     if (threadIdx.x == 0) bits[col] = h;
+  }
+  if (!huff) return;
+  __syncthreads();
+  bitonic_sort(hist, NBIN_WIDE, threadIdx.x, 256, [] { __syncthreads(); });
+  int nz = 0;
+  for (int b = threadIdx.x; b < NBIN_WIDE; b += 256) nz += hist[b] == 0;
+  for (int o = 32; o >= 1; o >>= 1) nz += __shfl_xor(nz, o, 64);
+  if ((threadIdx.x & 63) == 0) nzs[threadIdx.x >> 6] = nz;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int z = nzs[0] + nzs[1] + nzs[2] + nzs[3];
+    // the merged nodes go into the zero prefix; too many symbols: -1
+    huff[col] = (NBIN_WIDE - z <= z + 1) ? huffman_merge(hist, z, NBIN_WIDE, hist) : -1;
   }
 }
 
@@ -133,13 +217,13 @@ __global__ __launch_bounds__(256) void colmean(const double* __restrict__ bits, 
 }  // namespace
 
 hipError_t launch_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
-                                 double* bits, double* mean, int32_t* cmin, int32_t* cmax,
-                                 hipStream_t st) {
+                                 double* bits, double* mean, int64_t* huff, int32_t* cmin,
+                                 int32_t* cmax, hipStream_t st) {
   if (n > 0) {
     const unsigned g = (unsigned)((n + RC - 1) / RC);
     colrange<<<g, 256, 0, st>>>(codes, (int)m, (int)n, ldc, cmin, cmax);
-    colhist<<<g, 256, 0, st>>>(codes, (int)m, (int)n, ldc, cmin, cmax, bits);
-    colhist_wide<<<(unsigned)n, 256, 0, st>>>(codes, (int)m, ldc, cmin, cmax, bits);
+    colhist<<<g, 256, 0, st>>>(codes, (int)m, (int)n, ldc, cmin, cmax, bits, huff);
+    colhist_wide<<<(unsigned)n, 256, 0, st>>>(codes, (int)m, ldc, cmin, cmax, bits, huff);
   }
   if (mean) colmean<<<1, 256, 0, st>>>(bits, (int)n, mean);
   return hipGetLastError();

@@ -147,8 +147,8 @@ def test_rate_validation():
     L = B.lib()
     assert L.pwq_rate_workspace_size(0) == 0
     assert L.pwq_rate_workspace_size(100) >= 800
-    assert L.pwq_column_entropy(FAKE, -1, 8, 8, FAKE, None, None, 0, None) == INVALID
-    assert L.pwq_column_entropy(FAKE, 4, 8, 4, FAKE, None, None, 0, None) == INVALID
-    assert L.pwq_column_entropy(None, 4, 8, 8, FAKE, None, None, 0, None) == INVALID
-    assert L.pwq_column_entropy(FAKE, 4, 8, 8, None, None, None, 0, None) == INVALID
-    assert L.pwq_column_entropy(FAKE, 4, 8, 8, FAKE, None, None, 0, None) == WS
+    assert L.pwq_column_entropy(FAKE, -1, 8, 8, FAKE, None, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(FAKE, 4, 8, 4, FAKE, None, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(None, 4, 8, 8, FAKE, None, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(FAKE, 4, 8, 8, None, None, None, None, 0, None) == INVALID
+    assert L.pwq_column_entropy(FAKE, 4, 8, 8, FAKE, None, None, None, 0, None) == WS

@@ -213,14 +213,17 @@ def test_full_size_spectral_layer():
     log(f"{cfg.name}: sampled rows {stats}", t0)
 
     t0 = time.time()
-    bits_g, mean_g = P.column_entropy(out["codes"])
+    bits_g, mean_g, huff_g = P.column_entropy(out["codes"], huffman=True)
     torch.cuda.synchronize()
     bits_o = O.column_entropy_bits(codes)
     np.testing.assert_allclose(to_np(bits_g), bits_o, rtol=0, atol=1e-12)
     rate = float(np.mean(bits_o))
     assert abs(float(mean_g.item()) - rate) <= 1e-12
     assert abs(rate - spacing["target_bits"]) <= 0.005, rate
-    log(f"{cfg.name}: rate {rate:.5f} bits at c = {c:.6g} (GPU rate kernel agrees)", t0)
+    huff_o = O.column_huffman_bits(codes)
+    np.testing.assert_array_equal(to_np(huff_g), huff_o)
+    log(f"{cfg.name}: rate {rate:.5f} bits at c = {c:.6g}, Huffman-coded "
+        f"{huff_o.sum() / codes.size:.5f} bits/weight (GPU rate kernel agrees)", t0)
 
     t0 = time.time()
     D = W0 - alpha[None, :] * codes

@@ -1,6 +1,7 @@
 """The rate kernel: per-column empirical entropy of int32 codes, against the
 oracle's entropy of the same codes (exact counts; sums differ only in
-floating-point order)."""
+floating-point order), and per-column Huffman-coded lengths, which are
+integers and must equal the oracle's exactly."""
 import numpy as np
 import pytest
 import torch
@@ -17,12 +18,16 @@ TOL_BITS = 1e-12
 
 def _check(codes_np):
     codes = torch.from_numpy(np.ascontiguousarray(codes_np, dtype=np.int32)).cuda()
-    bits, mean = P.column_entropy(codes)
+    bits, mean, huff = P.column_entropy(codes, huffman=True)
     torch.cuda.synchronize()
     want = O.column_entropy_bits(codes_np.astype(np.int64))
     got = to_np(bits)
     np.testing.assert_allclose(got, want, rtol=0, atol=TOL_BITS)
     assert abs(float(mean.item()) - float(np.mean(want))) <= TOL_BITS
+    np.testing.assert_array_equal(to_np(huff), O.column_huffman_bits(codes_np.astype(np.int64)))
+    m = codes_np.shape[0]
+    # Shannon's bounds per column: H <= Huffman length / m < H + 1
+    assert np.all(to_np(huff) / m >= want - 1e-9) and np.all(to_np(huff) / m < want + 1)
     return got
 
 
@@ -56,10 +61,11 @@ def test_entropy_too_wide_is_nan_and_empty():
     codes = np.zeros((64, 3), np.int32)
     codes[0, 1] = -20000
     codes[1, 1] = 20000
-    bits, _ = P.column_entropy(torch.from_numpy(codes).cuda())
+    bits, _, huff = P.column_entropy(torch.from_numpy(codes).cuda(), huffman=True)
     torch.cuda.synchronize()
     b = to_np(bits)
     assert np.isnan(b[1]) and b[0] == 0.0 and b[2] == 0.0
+    assert list(to_np(huff)) == [0, -1, 0]
     bits, mean = P.column_entropy(torch.zeros((0, 5), dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert np.all(to_np(bits) == 0) and float(mean.item()) == 0.0
