@@ -3,9 +3,11 @@
 A step is one whole quant_layer call on device-resident inputs: H = 2 X X^T
 (bf16 MFMA SYRK), dead features + damping, blocked Cholesky, grid steps,
 the back-to-front nearest-plane sweep with lazy MFMA block updates, and the
-loss/bound reduction.  Workload: W 4096 x 4096 bf16, X 4096 x 131072 bf16
-(Student-t, 8 outlier channels x20), asymmetric 4-bit, group 128, block 128,
-damp 0.01 -- synthetic, seeded.
+loss/bound reduction.  Default workload (--config 2): W 4096 x 4096 bf16,
+X 4096 x 131072 bf16 (Student-t, 8 outlier channels x20), asymmetric 4-bit,
+group 128, block 128, damp 0.01 -- synthetic, seeded.  --config 3 / 4 time
+the up_proj / down_proj layers, --config 5 the spectral layer (H given, fp64
+factor and sweep, no SYRK: `roofline` is null there).
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the Hessian
 SYRK tiles): algorithmic flops n(n+1)N per launch over its average duration,
@@ -25,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3          # MI355X fp32 MFMA
+PEAK_F64_TFLOPS = 78.6           # MI355X fp64 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "layer quantize time (s) & weights quantized/s; MFMA util of SYRK+update"
 
@@ -65,35 +68,57 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def spacing_constant(cfg):
+    """The spectral layer's spacing constant c (mean code entropy 2.5 bits),
+    as searched on the oracle's codes and stored with the tests."""
+    path = os.path.join(ROOT, "tests", "golden", "spectral_layer_spacing.json")
+    with open(path) as f:
+        return float(json.load(f)["c"])
+
+
 def cpu_baseline(lay, cfg, frac):
-    """Time the fp64 oracle on a bounded sample and project the whole layer."""
+    """Time the fp64 oracle on a bounded sample and project the whole layer:
+    the Hessian over 1/frac of the tokens (x frac), the full Cholesky, and
+    the blocked sweep over all rows, or over a row sample (x m / rows) when
+    the sweep would take more than about 10 s."""
     import numpy as np
 
     import oracle as O
+    import synth
     cores = len(os.sched_getaffinity(0))
-    ntok_s = cfg.ntok // frac
-    t0 = time.perf_counter()
-    Xs = lay.X[:, :ntok_s]
-    H_s = O.hessian(Xs)
-    t_h = (time.perf_counter() - t0) * frac
-    H = H_s * frac  # stand-in Hessian of the right scale for timing the rest
+    t_h = 0.0
+    if lay.X_bits is not None:
+        ntok_s = cfg.ntok // frac
+        Xs = synth.gen.bf16_bits_to_f32(lay.X_bits[:, :ntok_s])
+        t0 = time.perf_counter()
+        H_s = O.hessian(Xs)
+        t_h = (time.perf_counter() - t0) * frac
+        H = H_s * frac  # stand-in Hessian of the right scale for timing the rest
+        h_txt = f"Hessian on the first {ntok_s} of {cfg.ntok} tokens, time x{frac}; "
+    else:
+        H = lay.H.astype(np.float64)
+        h_txt = "H given; "
     t0 = time.perf_counter()
     Hd, W0, lam, _ = O.fix_dead_and_damp(H, lay.W64(), cfg.damp)
     L, info = O.cholesky_lower(Hd)
     t_c = time.perf_counter() - t0
+    rows = min(cfg.m, max(64, int(4e11 / (2.0 * cfg.n * cfg.n))))
     t0 = time.perf_counter()
-    s_grp, z = O.grid_steps(W0, cfg.grid_kind, cfg.bits, cfg.group)
-    S = O.expand_group_steps(s_grp, cfg.n)
-    O.nearest_plane_sweep_blocked(W0, L, S, cfg.block)
-    t_s = time.perf_counter() - t0
+    if cfg.grid_kind == "colspacing":
+        S = np.broadcast_to(O.colspacing_steps(L, spacing_constant(cfg))[None, :],
+                            (rows, cfg.n))
+    else:
+        s_grp, z = O.grid_steps(W0[:rows], cfg.grid_kind, cfg.bits, cfg.group)
+        S = O.expand_group_steps(s_grp, cfg.n)
+    O.nearest_plane_sweep_blocked(W0[:rows], L, S, cfg.block)
+    t_s = (time.perf_counter() - t0) * cfg.m / rows
     total = t_h + t_c + t_s
     return {
         "value": cfg.m * cfg.n / total, "unit": "weights/s", "cores": cores,
         "kind": "oracle",
-        "sample": (f"fp64 numpy/OpenBLAS oracle: Hessian on the first {ntok_s} of {cfg.ntok} "
-                   f"tokens, time x{frac}; full Cholesky and blocked sweep "
-                   f"({cfg.m}x{cfg.n}); projected whole-layer time {total:.2f} s "
-                   f"(H {t_h:.2f} s, chol {t_c:.2f} s, sweep {t_s:.2f} s)"),
+        "sample": (f"fp64 numpy/OpenBLAS oracle: {h_txt}full Cholesky; blocked sweep of "
+                   f"{rows} of {cfg.m} rows (x{cfg.m / rows:.3g}); projected whole-layer "
+                   f"time {total:.2f} s (H {t_h:.2f} s, chol {t_c:.2f} s, sweep {t_s:.2f} s)"),
     }
 
 
@@ -115,21 +140,28 @@ def main():
     m, n, N = cfg.m, cfg.n, cfg.ntok
     print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
           flush=True)
-    lay = synth.make_layer(cfg, keep_x_f32=not args.no_cpu_baseline)
+    lay = synth.make_layer(cfg, keep_x_f32=False)
     dev = torch.device("cuda:0")
     W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    grid = P.Grid(cfg.grid_kind, cfg.bits, cfg.group)
-    ws = P.workspace_for_layer(m, n, N, True, "back_to_front", cfg.block, "f32", dev)
-    out = P.quant_layer(W, X=X, grid=grid, damp=cfg.damp, block=cfg.block, workspace=ws)
+    has_x = lay.X_bits is not None
+    X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev) if has_x else None
+    Hin = None if has_x else torch.from_numpy(lay.H).to(dev)
+    if cfg.grid_kind == "colspacing":
+        grid = P.Grid("colspacing", 0, 0, spacing_constant(cfg))
+    else:
+        grid = P.Grid(cfg.grid_kind, cfg.bits, cfg.group)
+    prec = "f32" if has_x else "f64"     # the spectral layer is factored and swept in fp64
+    ws = P.workspace_for_layer(m, n, N, has_x, "back_to_front", cfg.block, prec, dev)
+    out = P.quant_layer(W, X=X, H=Hin, grid=grid, damp=cfg.damp, block=cfg.block, prec=prec,
+                        workspace=ws)
     torch.cuda.synchronize()
     res0 = P.read_result(out["result"])
     if res0["info"] != 0:
         raise RuntimeError(f"Cholesky failed: {res0}")
 
     def step():
-        P.quant_layer(W, X=X, grid=grid, damp=cfg.damp, block=cfg.block, workspace=ws,
-                      out=out)
+        P.quant_layer(W, X=X, H=Hin, grid=grid, damp=cfg.damp, block=cfg.block, prec=prec,
+                      workspace=ws, out=out)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -139,7 +171,7 @@ def main():
     # The dominant kernel (the Hessian SYRK tiles) records a HIP event pair
     # around each of its launches inside the timed steps, on the stream the
     # library launches it on.
-    timer = P.HessianTileTimer(args.steps)
+    timer = P.HessianTileTimer(args.steps if has_x else 0)
     torch.cuda.synchronize()
     with timer:
         t0 = time.perf_counter()
@@ -147,13 +179,21 @@ def main():
             step()
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
-    tiles_ms = timer.durations_ms()
-    t_tiles = sum(tiles_ms) / len(tiles_ms) / 1e3
-    flops_h = float(n) * (n + 1) * N
-    achieved = flops_h / t_tiles / 1e12
+    roofline = None
+    if has_x:
+        tiles_ms = timer.durations_ms()
+        t_tiles = sum(tiles_ms) / len(tiles_ms) / 1e3
+        flops_h = float(n) * (n + 1) * N
+        achieved = flops_h / t_tiles / 1e12
+        roofline = {"bound": "mfma",
+                    "kernel": "syrk_tiles256 (bf16 SYRK tiles of H = 2 X X^T)",
+                    "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / PEAK_BF16_TFLOPS,
+                    "traffic": measured_traffic() if args.config == 2 else None,
+                    "avg_launch_ms": t_tiles * 1e3, "launches_timed": len(tiles_ms),
+                    "flops_per_launch": flops_h}
 
     stream = torch.cuda.current_stream()
-    H = torch.empty((n, n), dtype=torch.float32, device=dev)
 
     # stage breakdown (same library calls, separately)
     def timed(fn, r=3):
@@ -166,13 +206,26 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / r
-    P.hessian_accum(X, H=H)
-    Lf, dead, _ = P.damp_cholesky(H, damp=cfg.damp)
-    s, z = P.grid_steps(W, grid)
-    t_hess = timed(lambda: P.hessian_accum(X, H=H))
-    t_chol = timed(lambda: P.damp_cholesky(H, damp=cfg.damp))
+    if has_x:
+        H = torch.empty((n, n), dtype=torch.float32, device=dev)
+        P.hessian_accum(X, H=H)
+        t_hess = timed(lambda: P.hessian_accum(X, H=H))
+    else:
+        H, t_hess = Hin, 0.0
+    Lf, dead, _ = P.damp_cholesky(H, damp=cfg.damp, prec=prec)
+    s, z = (None, None) if cfg.grid_kind == "colspacing" else P.grid_steps(W, grid)
+    t_chol = timed(lambda: P.damp_cholesky(H, damp=cfg.damp, prec=prec))
     t_sweep = timed(lambda: P.babai_sweep(W, Lf, grid, scales=s, zeros=z, block=cfg.block))
     flops_upd = float(m) * n * (n - cfg.block)
+    peak_upd = PEAK_F32_TFLOPS if prec == "f32" else PEAK_F64_TFLOPS
+    if has_x:
+        inputs = (f"X {n}x{N} bf16 " + ("Student-t(4)" if cfg.x_kind == "student_t" else
+                                        "Laplace x LogNormal(0,1) channel scales")
+                  + (f" with {cfg.outliers} outlier channels x20" if cfg.outliers else ""))
+        grid_txt = f"{cfg.grid_kind} {cfg.bits}-bit group {cfg.group}"
+    else:
+        inputs = f"H {n}x{n} fp32 = L0 diag(k^-1.2) L0^T"
+        grid_txt = f"column spacing c/l_kk, c = {grid.c:.6g}"
 
     line = {
         "metric": METRIC,
@@ -185,21 +238,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 products, f32 accumulate/factor/sweep",
+        "dtype": ("bf16 products, f32 accumulate/factor/sweep" if has_x else
+                  "f64 factor and sweep"),
         "data": "synthetic (seeded)",
-        "config": {"workload": f"{cfg.name}: W {m}x{n} bf16, X {n}x{N} bf16 Student-t(4) "
-                               f"with {cfg.outliers} outlier channels x20; "
-                               f"{cfg.grid_kind} {cfg.bits}-bit group {cfg.group}, "
+        "config": {"workload": f"{cfg.name}: W {m}x{n} bf16, {inputs}; {grid_txt}, "
                                f"block {cfg.block}, damp {cfg.damp}",
                    "m": m, "n": n, "ntok": N, "layer_quantize_time_s": dt},
-        "roofline": {"bound": "mfma", "kernel": "syrk_tiles256 (bf16 SYRK tiles of H = 2 X X^T)",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-                     "avg_launch_ms": t_tiles * 1e3, "launches_timed": len(tiles_ms),
-                     "flops_per_launch": flops_h},
+        "roofline": roofline,
         "stages_ms": {"hessian_accum": t_hess, "damp_cholesky": t_chol,
                       "sweep_and_update": t_sweep},
-        "update_mfma_util_upper": (flops_upd / (t_sweep / 1e3) / 1e12) / PEAK_F32_TFLOPS,
+        "update_mfma_util_upper": (flops_upd / (t_sweep / 1e3) / 1e12) / peak_upd,
         "loss": res0["loss"], "bound": res0["bound"],
     }
     if not args.no_cpu_baseline:

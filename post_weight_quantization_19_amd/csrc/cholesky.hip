@@ -32,6 +32,10 @@ namespace pwq {
 namespace {
 
 constexpr int NB = 64;   // panel width
+// Panels per trailing update: fp64 trailing tiles are bound by their
+// read-modify-write, so it pays to apply several panels at once; the fp32
+// tile is not, and the wider K only lengthens the launch.
+template <typename T> constexpr int lazy_panels() { return sizeof(T) == 8 ? 8 : 1; }
 
 // lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;
 // fixed-order fp64 reduction.
@@ -274,62 +278,79 @@ __global__ __launch_bounds__(256) void chol_diag_last(T* __restrict__ A, int n, 
   diag_copy<T>(A, n, kq, dbuf);
 }
 
-// U = S Q^T for 64x64 operands in LDS (rows x NB, padded), result to LDS.
-// Wave w computes the 32x32 block (w>>1, w&1).
+// U (+)= S Q^T for 64 x 64 operands in LDS (rows x NB, padded), accumulated
+// in registers over K chunks and then written to LDS.  Wave w owns the
+// 32x32 block (w>>1, w&1).
 template <typename T>
-__device__ __forceinline__ void mfma_64x64x64(const T* __restrict__ S, const T* __restrict__ Q,
-                                              T* __restrict__ U) {
-  constexpr int LD = NB + 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  if constexpr (sizeof(T) == 4) {
-    f32x16_t acc;
+struct Mfma64 {
+  static constexpr int LD = NB + 1;
+  // fp32: one 32x32 accumulator; fp64: 2x2 16x16 accumulators (lane l,
+  // register r -> row 4r + l/16, col l%16)
+  typename std::conditional<sizeof(T) == 4, f32x16_t, f64x4_t[2][2]>::type acc;
+
+  __device__ __forceinline__ void zero() {
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < NB; k += 2) {
-      const int ko = k + (lane >> 5);
-      const float a = S[(wm * 32 + (lane & 31)) * LD + ko];
-      const float bq = Q[(wn * 32 + (lane & 31)) * LD + ko];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq, acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      U[(wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LD + wn * 32 + (lane & 31)] =
-          acc[r];
-  } else {
-    f64x4_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0;
-#pragma unroll 4
-    for (int k = 0; k < NB; k += 4) {
-      const int ko = k + (lane >> 4);
-      double av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[i] = S[(wm * 32 + i * 16 + (lane & 15)) * LD + ko];
-        bv[i] = Q[(wn * 32 + i * 16 + (lane & 15)) * LD + ko];
-      }
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          U[(wm * 32 + i * 16 + 4 * r + (lane >> 4)) * LD + wn * 32 + j * 16 + (lane & 15)] =
-              acc[i][j][r];
   }
-}
+  __device__ __forceinline__ void add(const T* __restrict__ S, const T* __restrict__ Q) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll 8
+      for (int k = 0; k < NB; k += 2) {
+        const int ko = k + (lane >> 5);
+        const float a = S[(wm * 32 + (lane & 31)) * LD + ko];
+        const float bq = Q[(wn * 32 + (lane & 31)) * LD + ko];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq, acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll 4
+      for (int k = 0; k < NB; k += 4) {
+        const int ko = k + (lane >> 4);
+        double av[2], bv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          av[i] = S[(wm * 32 + i * 16 + (lane & 15)) * LD + ko];
+          bv[i] = Q[(wn * 32 + i * 16 + (lane & 15)) * LD + ko];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* __restrict__ U) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    if constexpr (sizeof(T) == 4) {
+      // 32x32 layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        U[(wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LD + wn * 32 + (lane & 31)] =
+            acc[r];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            U[(wm * 32 + i * 16 + 4 * r + (lane >> 4)) * LD + wn * 32 + j * 16 + (lane & 15)] =
+                acc[i][j][r];
+    }
+  }
+};
 
 // Trailing update of one 128x128 lower-triangle tile t (row-major triangle
 // order) of A[base:, base:] by the panel at columns k0..k0+63:
@@ -337,8 +358,8 @@ __device__ __forceinline__ void mfma_64x64x64(const T* __restrict__ S, const T* 
 // (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64); both operands are panel
 // rows, contiguous along K.
 template <typename T>
-__device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, int base, int t,
-                                              char* smem) {
+__device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int kfrom, int npan,
+                                              int base, int t, char* smem) {
   constexpr int TB = 128, LD = NB + 1;
   T* As = (T*)smem;
   T* Bs = As + TB * LD;
@@ -370,16 +391,23 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
           const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
           acc[i][j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0f;
         }
+    for (int pc = 0; pc < npan; ++pc) {
+    const int k0 = kfrom + pc * NB;
+    if (pc > 0) __syncthreads();          // the previous chunk's LDS reads are done
+    // an opaque copy of n per chunk keeps the compiler from hoisting the 64
+    // row addresses out of the loop (they would stay live in registers)
+    int nl = n;
+    asm volatile("" : "+s"(nl));
     tile_to_lds<T, TB, NB, 256, LD>(As, tid, [&](int r, int k) {
-      return (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
+      return (r0 + r < nl) ? A[(int64_t)(r0 + r) * nl + k0 + k] : (T)0;
     });
     if (!diag)
       tile_to_lds<T, TB, NB, 256, LD>(Bs, tid, [&](int r, int k) {
-        return (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
+        return (c0 + r < nl) ? A[(int64_t)(c0 + r) * nl + k0 + k] : (T)0;
       });
     __syncthreads();
     const T* Bp = diag ? As : Bs;
-#pragma unroll 8
+#pragma unroll 4
     for (int k = 0; k < NB; k += 2) {
       const int ko = k + (lane >> 5);
       const float a0 = -As[(wm * 64 + (lane & 31)) * LD + ko];
@@ -391,6 +419,11 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
+    }
+    // the store addresses are recomputed from an opaque copy of n, so the
+    // 64 load addresses need not stay live through the K loop
+    int ns = n;
+    asm volatile("" : "+s"(ns));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -399,7 +432,7 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
         for (int r = 0; r < 16; ++r) {
           const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = acc[i][j][r];
+          if (gr < ns && gc <= gr) A[(int64_t)gr * ns + gc] = acc[i][j][r];
         }
   } else {
     // 16x16 f64 result layout: lane l, register r -> row 4r + l/16, col l%16
@@ -414,12 +447,19 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
           const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
           acc[i][j][r] = (gr < n && gc <= gr) ? A[(int64_t)gr * n + gc] : 0.0;
         }
+    for (int pc = 0; pc < npan; ++pc) {
+    const int k0 = kfrom + pc * NB;
+    if (pc > 0) __syncthreads();          // the previous chunk's LDS reads are done
+    // an opaque copy of n per chunk keeps the compiler from hoisting the 64
+    // row addresses out of the loop (they would stay live in registers)
+    int nl = n;
+    asm volatile("" : "+s"(nl));
     tile_to_lds<T, TB, NB, 256, LD>(As, tid, [&](int r, int k) {
-      return (r0 + r < n) ? A[(int64_t)(r0 + r) * n + k0 + k] : (T)0;
+      return (r0 + r < nl) ? A[(int64_t)(r0 + r) * nl + k0 + k] : (T)0;
     });
     if (!diag)
       tile_to_lds<T, TB, NB, 256, LD>(Bs, tid, [&](int r, int k) {
-        return (c0 + r < n) ? A[(int64_t)(c0 + r) * n + k0 + k] : (T)0;
+        return (c0 + r < nl) ? A[(int64_t)(c0 + r) * nl + k0 + k] : (T)0;
       });
     __syncthreads();
     const T* Bp = diag ? As : Bs;
@@ -438,6 +478,7 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -452,25 +493,31 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int k0, 
 }
 
 // One step with look-ahead, given the finished panel at k0 (columns
-// k0..k0+63 of every row >= k0 hold L).  Two roles in one launch, reading
-// only that panel, so they run concurrently:
+// k0..k0+63 of every row >= k0 hold L).  The trailing update is applied
+// lazily, several panels at a time: panels kfrom/64 .. k0/64 (npan of them)
+// have not yet been applied to the columns beyond the current panel.  Two
+// roles in one launch, reading only finished panels, so they run
+// concurrently:
 //  * workgroups 0 .. np-1 take the NEXT panel p1 = k0 + 64: each applies the
-//    panel-k0 update to the rows it factors (the diagonal block and its own
-//    64 rows; A -= P Q^T with K = 64 on MFMA through LDS) and factors them
-//    as above -- the serial part of the factorization;
-//  * the remaining workgroups update the trailing triangle beyond the next
-//    panel, A[k0+128:, k0+128:], with the same panel.
+//    pending panels to the rows it factors (the diagonal block and its own
+//    64 rows; A -= P Q^T with K = 64 npan on MFMA through LDS) and factors
+//    them as above -- the serial part of the factorization;
+//  * if ntrail > 0, the next workgroups apply the same pending panels to the
+//    trailing triangle beyond the next panel, A[k0+128:, k0+128:] (a
+//    K = 64 npan update: the read-modify-write of the trailing triangle is
+//    paid once per npan panels).
 // The next panel's columns are written by the first role only, the columns
 // beyond it by the second only.
 template <typename T>
-__global__ __launch_bounds__(256) void chol_step(T* __restrict__ A, int n, int k0, int np,
-                                                 int ntrail, T* __restrict__ dbuf,
+__global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void chol_step(T* __restrict__ A, int n, int k0, int kfrom,
+                                                 int np, int ntrail, T* __restrict__ dbuf,
                                                  DevFlags* flags, pwq_result* __restrict__ res) {
   constexpr int LD = NB + 1;
   __shared__ __attribute__((aligned(16))) char smem[CholSmem<T>::bytes];
   __shared__ int fail_col;
   if (flags->info != 0) return;
   const int q = k0 / NB;
+  const int npan = (k0 - kfrom) / NB + 1;
   if ((int)blockIdx.x >= np + ntrail) {
     // the finished diagonal block of panel k0 (no workgroup of this launch
     // reads rows k0..k0+63)
@@ -478,29 +525,40 @@ __global__ __launch_bounds__(256) void chol_step(T* __restrict__ A, int n, int k
     return;
   }
   if ((int)blockIdx.x >= np) {
-    trailing_tile<T>(A, n, k0, k0 + 2 * NB, blockIdx.x - np, smem);
+    trailing_tile<T>(A, n, kfrom, npan, k0 + 2 * NB, blockIdx.x - np, smem);
     return;
   }
   const int b = blockIdx.x, p1 = k0 + NB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  T* Q = (T*)smem;                 // panel-k0 columns of rows p1 .. p1+63
-  T* S = Q + 64 * LD;              // panel-k0 columns of rows p1+64b .. (b >= 1)
+  T* Q = (T*)smem;                 // pending-panel columns of rows p1 .. p1+63
+  T* S = Q + 64 * LD;              // pending-panel columns of rows p1+64b .. (b >= 1)
   T* U0 = S + 64 * LD;
   T* U1 = U0 + 64 * LD;
   T(*gbuf)[2][4][NB] = (T(*)[2][4][NB])(U1 + 64 * LD);
+  Mfma64<T> u0, u1;
+  u0.zero();
+  u1.zero();
+  for (int pc = 0; pc < npan; ++pc) {
+    const int kc = kfrom + pc * NB;
+    if (pc > 0) __syncthreads();   // the previous chunk's LDS reads are done
+    tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
+      return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + kc + k] : (T)0;
+    });
+    if (b > 0)
+      tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
+        const int row = p1 + NB * b + r;
+        return (row < n) ? A[(int64_t)row * n + kc + k] : (T)0;
+      });
+    __syncthreads();
+    u0.add(Q, Q);
+    if (b > 0) u1.add(S, Q);
+  }
+  // the panel itself is loaded only now: holding it in registers through the
+  // accumulation would cost the trailing role its second workgroup per CU
   T d0[16], d1[16];
   panel_load<T>(A, n, p1, b, d0, d1);
-  tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
-    return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + k0 + k] : (T)0;
-  });
-  if (b > 0)
-    tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
-      const int row = p1 + NB * b + r;
-      return (row < n) ? A[(int64_t)row * n + k0 + k] : (T)0;
-    });
-  __syncthreads();
-  mfma_64x64x64<T>(Q, Q, U0);
-  if (b > 0) mfma_64x64x64<T>(S, Q, U1);
+  u0.store(U0);
+  if (b > 0) u1.store(U1);
   __syncthreads();
   const int nb = min(NB, n - p1);
 #pragma unroll
@@ -519,15 +577,20 @@ hipError_t factor_impl(T* A, int n, T* dbuf, DevFlags* flags, pwq_result* res,
                        hipStream_t st) {
   chol_panel_first<T><<<(n + NB - 1) / NB, 256, 0, st>>>(A, n, dbuf, flags, res);
   int k0 = 0;
+  int kfrom = 0;   // first panel not yet applied to the columns beyond the next panel
   for (; k0 + NB < n; k0 += NB) {
     const int p1 = k0 + NB;
     const int np = (n - p1 + NB - 1) / NB;
     const int base2 = k0 + 2 * NB;
     const int nt = base2 < n ? (n - base2 + 127) / 128 : 0;
-    const int ntrail = nt * (nt + 1) / 2;
-    chol_step<T><<<np + ntrail + 1, 256, 0, st>>>(A, n, k0, np, ntrail, dbuf, flags, res);
+    // the trailing triangle takes the pending panels lazy_panels<T>() at a time
+    const bool trail = nt > 0 && (k0 - kfrom) / NB + 1 >= lazy_panels<T>();
+    const int ntrail = trail ? nt * (nt + 1) / 2 : 0;
+    chol_step<T><<<np + ntrail + 1, 256, 0, st>>>(A, n, k0, kfrom, np, ntrail, dbuf, flags,
+                                                  res);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (trail) kfrom = k0 + NB;
   }
   chol_diag_last<T><<<1, 256, 0, st>>>(A, n, k0, dbuf + ((k0 / NB) & 1) * NB * NB, flags);
   return hipGetLastError();
