@@ -4,8 +4,9 @@ A step is one whole quant_layer call on device-resident inputs: H = 2 X X^T
 (bf16 MFMA SYRK), dead features + damping, blocked Cholesky, grid steps,
 the back-to-front nearest-plane sweep with lazy MFMA block updates, and the
 loss/bound reduction.  Default workload (--config 2): W 4096 x 4096 bf16,
-X 4096 x 131072 bf16 (Student-t, 8 outlier channels x20), asymmetric 4-bit,
-group 128, block 128, damp 0.01 -- synthetic, seeded.  --config 3 / 4 time
+X 4096 x 131072 bf16 (Student-t, 8 outlier channels x20) stored token-major
+(131072 rows of 4096 channels; --x-layout channels stores it 4096 x 131072),
+asymmetric 4-bit, group 128, block 128, damp 0.01 -- synthetic, seeded.  --config 3 / 4 time
 the up_proj / down_proj layers, --config 5 the spectral layer (H given, fp64
 factor and sweep, no SYRK: `roofline` is null there).
 
@@ -38,6 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload table entry")
+    ap.add_argument("--x-layout", choices=["channels", "tokens"], default="tokens",
+                    help="storage of the activations: token-major [ntok, n] (one row per "
+                         "token, as a layer's inputs are captured; the default) or [n, ntok]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-token-fraction", type=int, default=8,
                     help="oracle Hessian is timed on 1/k of the tokens, scaled by k")
@@ -145,6 +149,9 @@ def main():
     W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     has_x = lay.X_bits is not None
     X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev) if has_x else None
+    xl = args.x_layout
+    if has_x and xl == "tokens":
+        X = X.t().contiguous()          # the same matrix, one row per token
     Hin = None if has_x else torch.from_numpy(lay.H).to(dev)
     if cfg.grid_kind == "colspacing":
         grid = P.Grid("colspacing", 0, 0, spacing_constant(cfg))
@@ -153,7 +160,7 @@ def main():
     prec = "f32" if has_x else "f64"     # the spectral layer is factored and swept in fp64
     ws = P.workspace_for_layer(m, n, N, has_x, "back_to_front", cfg.block, prec, dev)
     out = P.quant_layer(W, X=X, H=Hin, grid=grid, damp=cfg.damp, block=cfg.block, prec=prec,
-                        workspace=ws)
+                        workspace=ws, x_layout=xl)
     torch.cuda.synchronize()
     res0 = P.read_result(out["result"])
     if res0["info"] != 0:
@@ -161,7 +168,7 @@ def main():
 
     def step():
         P.quant_layer(W, X=X, H=Hin, grid=grid, damp=cfg.damp, block=cfg.block, prec=prec,
-                      workspace=ws, out=out)
+                      workspace=ws, out=out, x_layout=xl)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -208,8 +215,8 @@ def main():
         return a.elapsed_time(b) / r
     if has_x:
         H = torch.empty((n, n), dtype=torch.float32, device=dev)
-        P.hessian_accum(X, H=H)
-        t_hess = timed(lambda: P.hessian_accum(X, H=H))
+        P.hessian_accum(X, H=H, x_layout=xl)
+        t_hess = timed(lambda: P.hessian_accum(X, H=H, x_layout=xl))
     else:
         H, t_hess = Hin, 0.0
     Lf, dead, _ = P.damp_cholesky(H, damp=cfg.damp, prec=prec)
@@ -219,7 +226,8 @@ def main():
     flops_upd = float(m) * n * (n - cfg.block)
     peak_upd = PEAK_F32_TFLOPS if prec == "f32" else PEAK_F64_TFLOPS
     if has_x:
-        inputs = (f"X {n}x{N} bf16 " + ("Student-t(4)" if cfg.x_kind == "student_t" else
+        stored = "stored token-major [ntok, n]" if xl == "tokens" else "stored [n, ntok]"
+        inputs = (f"X {n}x{N} bf16 {stored} " + ("Student-t(4)" if cfg.x_kind == "student_t" else
                                         "Laplace x LogNormal(0,1) channel scales")
                   + (f" with {cfg.outliers} outlier channels x20" if cfg.outliers else ""))
         grid_txt = f"{cfg.grid_kind} {cfg.bits}-bit group {cfg.group}"
@@ -243,7 +251,8 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": f"{cfg.name}: W {m}x{n} bf16, {inputs}; {grid_txt}, "
                                f"block {cfg.block}, damp {cfg.damp}",
-                   "m": m, "n": n, "ntok": N, "layer_quantize_time_s": dt},
+                   "m": m, "n": n, "ntok": N, "x_layout": xl if has_x else None,
+                   "layer_quantize_time_s": dt},
         "roofline": roofline,
         "stages_ms": {"hessian_accum": t_hess, "damp_cholesky": t_chol,
                       "sweep_and_update": t_sweep},

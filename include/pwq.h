@@ -58,6 +58,13 @@ typedef enum {
  * factor / running target / sweep (PWQ_F32 or PWQ_F64). */
 typedef enum { PWQ_F32 = 0, PWQ_BF16 = 1, PWQ_F64 = 2 } pwq_dtype;
 
+/* Layout flag OR'ed into the X dtype (xdtype) of pwq_hessian_accum and
+ * pwq_quant_layer: X is stored ntok x n, one row per token with the n
+ * channels contiguous (row stride ldx >= n), the layout in which a layer's
+ * input activations are usually captured.  Without it X is n x ntok (row
+ * stride ldx >= ntok).  Both describe the same matrix X and give the same H. */
+enum { PWQ_X_TOKEN_MAJOR = 0x100 };
+
 /* Quantization grid.  The lattice of one row is s * Z per column (no
  * clipping: codes are any int32) [GEOM 2.1, 2.3].
  *   SYM        : s = max|w| / (2^(bits-1) - 1) over each group of
@@ -123,7 +130,9 @@ const char* pwq_last_error(void);
  * calibration inputs; WSIC 1: output error of Y = W X].
  *   H        : n x n float32, full symmetric result (both triangles
  *              written; with accumulate != 0 the previous H is added).
- *   X        : n x ntok, xdtype PWQ_BF16 or PWQ_F32, row stride ldx >= ntok.
+ *   X        : n x ntok, xdtype PWQ_BF16 or PWQ_F32, row stride ldx >= ntok;
+ *              or, with xdtype | PWQ_X_TOKEN_MAJOR, stored ntok x n with row
+ *              stride ldx >= n.
  *   Products are exact in fp32 for bf16 inputs; accumulation is fp32 in a
  *   fixed order.  Calling it once per calibration chunk with accumulate = 1
  *   streams the Hessian over any number of tokens.
@@ -187,7 +196,8 @@ pwq_status pwq_babai_sweep(const void* W, int32_t wdtype, int64_t m, int64_t n,
 /* ---------------------------------------------------------------------- *
  * The whole layer: quant_layer(W, X or H, grid, order, damp) ->
  * codes + steps + proxy loss [GEOM 1, 2.1-2.3; WSIC 1-2; OAEM 3].
- *   Exactly one of X (n x ntok, xdtype) and H (n x n float32) is non-NULL.
+ *   Exactly one of X (n x ntok, xdtype, layout as for pwq_hessian_accum)
+ *   and H (n x n float32) is non-NULL.
  *   order_kind : pwq_order_kind; perm (device int32 [n]) only for PERM.
  *   damp       : lambda = damp * mean(diag H) (0 for none).
  *   block      : 32, 64, 128 or 256.   prec : PWQ_F32 or PWQ_F64.

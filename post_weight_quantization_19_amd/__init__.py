@@ -82,18 +82,31 @@ def read_result(res: torch.Tensor) -> dict:
     return parse_result(bytes(res.cpu().numpy().tobytes()))
 
 
-def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None,
-                  accumulate: bool = False) -> torch.Tensor:
-    """H (+)= 2 X X^T for X [n, ntok] (bf16 or fp32)."""
-    _require_cuda(X, H)
-    n, ntok = X.shape
+def _x_args(X: torch.Tensor, x_layout: str):
+    """(n, ntok, ldx, xdtype) of activations X: ``x_layout`` "channels" for
+    X [n, ntok], "tokens" for X [ntok, n] (one row per token)."""
     ldx = _row_major(X)
+    if x_layout == "channels":
+        n, ntok = X.shape
+        return n, ntok, ldx, _dtype_code(X)
+    if x_layout == "tokens":
+        ntok, n = X.shape
+        return n, ntok, ldx, _dtype_code(X) | _lib.PWQ_X_TOKEN_MAJOR
+    raise ValueError(f"x_layout must be 'channels' or 'tokens', not {x_layout!r}")
+
+
+def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None,
+                  accumulate: bool = False, x_layout: str = "channels") -> torch.Tensor:
+    """H (+)= 2 X X^T for activations X (bf16 or fp32) stored [n, ntok]
+    (``x_layout="channels"``) or [ntok, n] (``x_layout="tokens"``)."""
+    _require_cuda(X, H)
+    n, ntok, ldx, xdt = _x_args(X, x_layout)
     if H is None:
         H = torch.empty((n, n), dtype=torch.float32, device=X.device)
     L = lib()
     wsb = L.pwq_hessian_workspace_size(n, ntok)
     ws = _workspace(wsb, X.device)
-    check(L.pwq_hessian_accum(H.data_ptr(), n, X.data_ptr(), _dtype_code(X), ntok, ldx,
+    check(L.pwq_hessian_accum(H.data_ptr(), n, X.data_ptr(), xdt, ntok, ldx,
                               int(accumulate), ws.data_ptr(), ws.numel(), _stream()))
     return H
 
@@ -161,13 +174,19 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
                 order: str = "back_to_front", perm: Optional[torch.Tensor] = None,
                 damp: float = 0.01, block: int = 128, prec: str = "f32",
                 want_H: bool = False, want_L: bool = False,
-                workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+                workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                x_layout: str = "channels"):
     """quant_layer(W, X or H, grid, order, damp) -> dict(codes, scales, zeros,
-    result[, H, L]).  ``out`` may pass preallocated outputs (same keys)."""
+    result[, H, L]).  ``out`` may pass preallocated outputs (same keys);
+    ``x_layout`` as for hessian_accum."""
     _require_cuda(W, X, H, perm)
     m, n = W.shape
     dev = W.device
-    ntok, ldx = (X.shape[1], _row_major(X)) if X is not None else (0, 0)
+    ntok, ldx, xdt = 0, 0, 0
+    if X is not None:
+        nx, ntok, ldx, xdt = _x_args(X, x_layout)
+        if nx != n:
+            raise ValueError(f"X has {nx} channels, W has {n} columns")
     G = n if grid.kind == "colspacing" else (grid.group or n)
     o = dict(out or {})
     if "codes" not in o:
@@ -190,7 +209,7 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
     g = grid.c_struct()
     check(lib().pwq_quant_layer(
         W.data_ptr(), _dtype_code(W), m, n, _row_major(W),
-        _ptr(X), _dtype_code(X) if X is not None else 0, ntok, ldx, _ptr(H), g,
+        _ptr(X), xdt, ntok, ldx, _ptr(H), g,
         _lib.ORDERS[order], _ptr(perm), float(damp), int(block), _prec(prec),
         o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o["zeros"]),
         o["result"].data_ptr(), _ptr(o.get("H")), _ptr(o.get("L")), ws.data_ptr(),

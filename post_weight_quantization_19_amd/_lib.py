@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libpwq.so")
 
 PWQ_OK, PWQ_ERR_INVALID_ARG, PWQ_ERR_UNSUPPORTED, PWQ_ERR_WORKSPACE, PWQ_ERR_HIP = range(5)
 PWQ_F32, PWQ_BF16, PWQ_F64 = 0, 1, 2
+PWQ_X_TOKEN_MAJOR = 0x100     # X stored ntok x n (one row per token)
 GRID_KINDS = {"sym": 0, "asym": 1, "colspacing": 2}
 ORDERS = {"back_to_front": 0, "front_to_back": 1, "perm": 2, "act_order": 3}
 

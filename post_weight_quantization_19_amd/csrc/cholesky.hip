@@ -492,6 +492,90 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int kfro
   }
 }
 
+// fp32 trailing tile with 16-byte aligned rows (n % 4 == 0): the same update
+// as trailing_tile, with both operands loaded straight into registers.  Lane
+// l of a wave takes the 32 consecutive K values 32 (l/32) .. 32 (l/32) + 31
+// of its rows (eight 16-byte loads per row), so MFMA step s sums K = s and
+// K = 32 + s; the same order is used for both operands, so this is the
+// product over all 64 K, in a different rounding order.  No LDS and no
+// barriers: the 128 MFMAs of a wave run back to back.  Rows and columns past
+// n are clamped into the matrix (they only reach outputs that are not
+// stored).
+__device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int n, int kfrom,
+                                                      int npan, int base, int t) {
+  constexpr int TB = 128;
+  int ti, tj;
+  {
+    int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    while (r * (r + 1) / 2 > t) --r;
+    ti = r;
+    tj = t - r * (r + 1) / 2;
+  }
+  const int r0 = base + ti * TB, c0 = base + tj * TB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, li = lane & 31;
+  // acc = A_ij - sum_k P_ik P_jk: the accumulators start from the tile
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = min(r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3), n - 1);
+        const int gc = min(c0 + wn * 64 + j * 32 + li, n - 1);
+        acc[i][j][r] = A[(int64_t)gr * n + gc];
+      }
+  const float* pa[2];
+  const float* pb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    pa[i] = A + (int64_t)min(r0 + wm * 64 + i * 32 + li, n - 1) * n + 32 * g;
+    pb[i] = A + (int64_t)min(c0 + wn * 64 + i * 32 + li, n - 1) * n + 32 * g;
+  }
+  for (int pc = 0; pc < npan; ++pc) {
+    const int kc = kfrom + pc * NB;
+    float4 a[2][8], b[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        a[i][q] = *(const float4*)(pa[i] + kc + 4 * q);
+        b[i][q] = *(const float4*)(pb[i] + kc + 4 * q);
+      }
+    // all 32 loads in flight before the first MFMA (the scheduler would
+    // otherwise interleave them a few at a time, paying the latency 8 times)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float av[2], bv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          av[i] = -(&a[i][q].x)[e];
+          bv[i] = (&b[i][q].x)[e];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int gc = c0 + wn * 64 + j * 32 + li;
+        if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = acc[i][j][r];
+      }
+}
+
 // One step with look-ahead, given the finished panel at k0 (columns
 // k0..k0+63 of every row >= k0 hold L).  The trailing update is applied
 // lazily, several panels at a time: panels kfrom/64 .. k0/64 (npan of them)
@@ -525,6 +609,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void chol_step(T* __re
     return;
   }
   if ((int)blockIdx.x >= np) {
+    if constexpr (sizeof(T) == 4) {
+      if (n % 4 == 0 && ((uintptr_t)A & 15) == 0) {
+        trailing_tile_f32_reg(A, n, kfrom, npan, k0 + 2 * NB, blockIdx.x - np);
+        return;
+      }
+    }
     trailing_tile<T>(A, n, kfrom, npan, k0 + 2 * NB, blockIdx.x - np, smem);
     return;
   }

@@ -1,4 +1,6 @@
-// H (+)= 2 X X^T for calibration activations X [n, ntok] (tokens contiguous).
+// H (+)= 2 X X^T for calibration activations X, stored either channel-major
+// ([n, ntok], tokens contiguous) or token-major ([ntok, n], one row per
+// token with the channels contiguous, as activations are usually captured).
 //
 // "The Geometry of LLM Quantization: GPTQ as Babai's Nearest Plane
 // Algorithm", technical summary 2.1: the closest-vector lattice is generated
@@ -97,10 +99,26 @@ __device__ __forceinline__ uint4 load_vec(const XT* X, int64_t ldx, int row,
   return v;
 }
 
+// Token-major X: the same 16-byte vector (channel `row`, tokens k ..
+// k+VEC-1) gathered element by element; consecutive lanes take consecutive
+// channels, so every element load is coalesced across the wave.
+template <typename XT>
+__device__ __forceinline__ uint4 load_vec_tm(const XT* X, int64_t ldx, int row, int n,
+                                             int64_t k, int64_t kend) {
+  constexpr int VEC = SyrkCfg<XT>::VEC;
+  XT tmp[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e)
+    tmp[e] = (row < n && k + e < kend) ? X[(k + e) * ldx + row] : (XT)0;
+  uint4 v;
+  __builtin_memcpy(&v, tmp, sizeof(v));
+  return v;
+}
+
 // Work item = (split, tile position), split-major.  Workgroup w runs on XCD
 // w % 8 (round-robin dispatch); XCD x takes items [x Q, (x+1) Q), so with 8
 // splits each XCD owns one token range of every tile.
-template <typename XT>
+template <typename XT, bool TM>
 __global__ __launch_bounds__(NT) void syrk_tiles(
     const XT* __restrict__ X, int n, int64_t ntok, int64_t ldx, int64_t kps,
     int aligned, float* __restrict__ partial, float* __restrict__ H,
@@ -136,19 +154,29 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   uint4 ra[NV], rb[NV];
+  // vector v of a panel stage: channel row, token vector cv (channel-major:
+  // consecutive threads walk along the tokens of a row; token-major: along
+  // the channels)
+  auto vrow = [](int v) { return TM ? v % BM : v / VPR; };
+  auto vcol = [](int v) { return TM ? v / BM : v % VPR; };
   auto gload = [&](int stage) {
     const int64_t k0 = kbeg + (int64_t)stage * BK;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int v = tid + NT * i, row = v / VPR, cv = v % VPR;
-      ra[i] = load_vec<XT>(X, ldx, r0 + row, n, k0 + cv * VEC, kend, aligned);
-      if (!diag) rb[i] = load_vec<XT>(X, ldx, c0 + row, n, k0 + cv * VEC, kend, aligned);
+      const int v = tid + NT * i, row = vrow(v), cv = vcol(v);
+      if constexpr (TM) {
+        ra[i] = load_vec_tm<XT>(X, ldx, r0 + row, n, k0 + cv * VEC, kend);
+        if (!diag) rb[i] = load_vec_tm<XT>(X, ldx, c0 + row, n, k0 + cv * VEC, kend);
+      } else {
+        ra[i] = load_vec<XT>(X, ldx, r0 + row, n, k0 + cv * VEC, kend, aligned);
+        if (!diag) rb[i] = load_vec<XT>(X, ldx, c0 + row, n, k0 + cv * VEC, kend, aligned);
+      }
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int v = tid + NT * i, row = v / VPR, cv = v % VPR;
+      const int v = tid + NT * i, row = vrow(v), cv = vcol(v);
       *(uint4*)&As[buf][row * LD + cv * VEC] = ra[i];
       if (!diag) *(uint4*)&Bs[buf][row * LD + cv * VEC] = rb[i];
     }
@@ -249,9 +277,64 @@ constexpr int NTL = 64 * NWL;  // threads
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
+// Token-major X: an LDS panel stage is 32 token rows of 512 B (256 channels,
+// 32 chunks of 16 B); logical chunk c of token row r is stored at chunk
+// c ^ tm_swz(r).  The MFMA operands (8 consecutive tokens of one channel per
+// lane) come from pairs of ds_read_b64_tr_b16: within each 16-lane group,
+// lane i receives element i % 4 of the 8 bytes addressed by lane
+// 4 j + i / 4 as its element j.  When source lane 4 j + a addresses token
+// row t0 + j, channels f0 + 4a .. f0 + 4a + 3, lane i therefore receives
+// tokens t0 .. t0 + 3 of channel f0 + i.  A group reads 4 consecutive token
+// rows at the same channels; the swizzle moves those rows' 32-byte pieces
+// to distinct banks.
+#ifndef PWQ_TM_SWZ
+#define PWQ_TM_SWZ 4
+#endif
+__device__ __forceinline__ int tm_swz(int r) { return PWQ_TM_SWZ * (r & 3); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Six MFMA operands (8 consecutive tokens t0 .. t0 + 7 of channel f0 +
+// lane % 16 each) from the LDS addresses p[0..5]: two transposed reads 4
+// token rows (2048 B) apart per operand.  The reads are issued together and
+// waited for (lgkmcnt(0)) inside the same asm block, so every output is
+// complete when the block ends.  (Written as asm because the compiler, not
+// seeing which LDS bytes the builtin reads, would otherwise wait for every
+// LDS copy still in flight before the first read.)
+__device__ __forceinline__ void tr_operands6(const uint32_t (&p)[6], bf16x8_t (&out)[6]) {
+  v4i16 lo[6], hi[6];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %13\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %17\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+        "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5])
+      : "memory");
+#pragma unroll
+  for (int t = 0; t < 6; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[t][e] = lo[t][e];
+      out[t][4 + e] = hi[t][e];
+    }
+}
+
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= v and lgkmcnt = 0.
 constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
 
+template <bool TM>
 __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     const uint16_t* __restrict__ X, int n, int64_t ntok, int64_t ldx, int64_t kps,
     int aligned, float* __restrict__ partial, float* __restrict__ H, int direct,
@@ -286,22 +369,47 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // DMA: each stage and panel is 16 wave-chunks of 1 KB (64 lanes x 16 B);
-  // wave w fills chunks CPW w .. CPW w + CPW-1.  Lane l of chunk q fills LDS
-  // unit u = 64 q + l = row u/4, physical chunk u%4, i.e. logical chunk
-  // (u%4) ^ ((row>>2)&3).  Rows past n read row n-1 (those products only
-  // reach outputs >= n, which are never stored).
+  // wave w fills chunks CPW w .. CPW w + CPW-1, and lane l of chunk q fills
+  // LDS unit u = 64 q + l.
+  // Channel-major: unit u = channel row u/4, physical chunk u%4, i.e.
+  // logical chunk (u%4) ^ ((row>>2)&3) of 8 tokens.  Rows past n read row
+  // n-1 (those products only reach outputs >= n, which are never stored).
+  // Token-major: unit u = token row u/32, physical chunk u%32, logical chunk
+  // (u%32) ^ tm_swz(row) of 8 channels; channels past n read channels n-8 ..
+  // n-1 (n is a multiple of 8 on this path), again only reaching outputs
+  // that are never stored.
   const uint16_t* ga[CPW];
   const uint16_t* gb[CPW];
 #pragma unroll
   for (int q = 0; q < CPW; ++q) {
-    const int u = (CPW * wave + q) * 64 + lane, r = u >> 2;
-    const int c = (u & 3) ^ ((r >> 2) & 3);
-    ga[q] = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
-    gb[q] = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
+    const int u = (CPW * wave + q) * 64 + lane;
+    if constexpr (TM) {
+      const int t = u >> 5, c = (u & 31) ^ tm_swz(u >> 5);
+      ga[q] = X + (kbeg + t) * ldx + min(r0 + 8 * c, n - 8);
+      gb[q] = X + (kbeg + t) * ldx + min(c0 + 8 * c, n - 8);
+    } else {
+      const int r = u >> 2, c = (u & 3) ^ ((r >> 2) & 3);
+      ga[q] = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
+      gb[q] = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
+    }
+  }
+  const int64_t kstep = TM ? (int64_t)BKL * ldx : (int64_t)BKL;   // elements per stage
+  // token-major operand reads: lane-constant byte offsets of the A (t < TI)
+  // and B (t >= TI) fragments within a slot, for tokens 8 (lane/32) .. + 3
+  // of the stage's first 16 (the other reads add constant row offsets)
+  int toff[TM ? TI + 4 : 1];
+  if constexpr (TM) {
+    const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+#pragma unroll
+    for (int t = 0; t < TI + 4; ++t) {
+      const int f = (t < TI ? wm * WR + 32 * t : wn * 128 + 32 * (t - TI)) + 16 * (g & 1) + 4 * a;
+      toff[t] = (t < TI ? 0 : BL * 64) + (8 * (g >> 1) + j) * 512 +
+                (((f >> 3) ^ tm_swz(j)) << 4) + 2 * (f & 7);
+    }
   }
   auto issue = [&](int stage) {
     const int slot = stage % NSLOT;
-    const int64_t ko = (int64_t)stage * BKL;
+    const int64_t ko = (int64_t)stage * kstep;
 #pragma unroll
     for (int q = 0; q < CPW; ++q) {
       __builtin_amdgcn_global_load_lds(
@@ -318,16 +426,31 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     if (skip) return;
     const uint4* A = Ls[slot][0];
     const uint4* B = Ls[slot][1];
+    const lds_char* S = (const lds_char*)&Ls[slot][0][0];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = 2 * ks + (lane >> 5);
       bf16x8_t a[TI], b[4];
+      if constexpr (TM) {
+        static_assert(TI + 4 == 6, "six operands per token step");
+        const uint32_t sb = (uint32_t)(uintptr_t)S + ks * 16 * 512;
+        uint32_t p[6];
+        bf16x8_t o[6];
 #pragma unroll
-      for (int t = 0; t < TI; ++t)
-        a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * WR + 32 * t + (lane & 31), c)]);
+        for (int t = 0; t < 6; ++t) p[t] = sb + toff[t];
+        tr_operands6(p, o);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
+        for (int t = 0; t < TI; ++t) a[t] = o[t];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = o[TI + t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < TI; ++t)
+          a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * WR + 32 * t + (lane & 31), c)]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
+      }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -371,10 +494,21 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     const int64_t k0 = kbeg + (int64_t)nfull * BKL;
 #pragma unroll
     for (int i = 0; i < 1024 / NTL; ++i) {
-      const int row = (tid >> 2) + (NTL / 4) * i;
-      const int64_t kk = k0 + (tid & 3) * 8;
-      Ls[slot][0][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, r0 + row, n, kk, kend, aligned);
-      Ls[slot][1][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, c0 + row, n, kk, kend, aligned);
+      if constexpr (TM) {
+        const int u = tid + NTL * i, t = u >> 5, c = (u & 31) ^ tm_swz(t);
+        uint4 va = make_uint4(0, 0, 0, 0), vb = va;
+        if (k0 + t < kend) {
+          va = *(const uint4*)(X + (k0 + t) * ldx + min(r0 + 8 * c, n - 8));
+          vb = *(const uint4*)(X + (k0 + t) * ldx + min(c0 + 8 * c, n - 8));
+        }
+        Ls[slot][0][u] = va;
+        Ls[slot][1][u] = vb;
+      } else {
+        const int row = (tid >> 2) + (NTL / 4) * i;
+        const int64_t kk = k0 + (tid & 3) * 8;
+        Ls[slot][0][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, r0 + row, n, kk, kend, aligned);
+        Ls[slot][1][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, c0 + row, n, kk, kend, aligned);
+      }
     }
     __syncthreads();
     compute(slot);
@@ -467,13 +601,18 @@ __global__ __launch_bounds__(256) void syrk_reduce(
 
 }  // namespace
 
-bool syrk_aligned(const void* X, int64_t ldx, int32_t xdtype) {
-  return ((uintptr_t)X % 16 == 0) && ((ldx * (xdtype == 1 ? 2 : 4)) % 16 == 0);
+bool syrk_aligned(const void* X, int64_t n, int64_t ldx, int32_t xdtype) {
+  const int64_t es = (xdtype & kXTypeMask) == 1 ? 2 : 4;
+  // token-major rows are read in 16-byte pieces of channels, so n must fill
+  // whole pieces as well
+  const bool tm = (xdtype & kXTokenMajor) != 0;
+  return ((uintptr_t)X % 16 == 0) && ((ldx * es) % 16 == 0) && (!tm || (n * es) % 16 == 0);
 }
 
 void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* p) {
   // bf16 inputs on layers of >= 1024 channels (16-byte aligned rows) use the
   // 256x256 tile
+  xdtype &= kXTypeMask;
   const bool big = xdtype == 1 && n >= 1024 && aligned;
   const int te = big ? BL : BM;
   const int bk = big ? BKL : (xdtype == 1 ? SyrkCfg<uint16_t>::BK : SyrkCfg<float>::BK);
@@ -516,7 +655,9 @@ void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* 
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
                           int64_t ntok, int64_t ldx, int32_t accumulate,
                           const SyrkPlan& p, void* partial, hipStream_t st) {
-  const bool aligned = syrk_aligned(X, ldx, xdtype);
+  const bool aligned = syrk_aligned(X, n, ldx, xdtype);
+  const bool tm = (xdtype & kXTokenMajor) != 0;
+  xdtype &= kXTypeMask;
   const int direct = p.nsplit == 1;
   const int64_t items = p.ntiles * p.nsplit;
   const int per_xcd = (int)((items + 7) / 8);
@@ -527,20 +668,28 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
     const hipError_t e = hipEventRecord(g_timer_hessian_tiles.starts[ti], st);
     if (e != hipSuccess) return e;
   }
-  if (p.tile == BL)
-    syrk_tiles256<<<grid, NTL, 0, st>>>((const uint16_t*)X, (int)n, ntok, ldx, p.kps, aligned,
-                                       (float*)partial, H, direct, accumulate, (int)p.ntiles,
-                                       (int)p.nsplit, per_xcd);
+  const float* Xf = (const float*)X;
+  const uint16_t* Xh = (const uint16_t*)X;
+  float* P = (float*)partial;
+  const int nti = (int)p.ntiles, nsp = (int)p.nsplit;
+  if (p.tile == BL && tm)
+    syrk_tiles256<true><<<grid, NTL, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P, H,
+                                              direct, accumulate, nti, nsp, per_xcd);
+  else if (p.tile == BL)
+    syrk_tiles256<false><<<grid, NTL, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P, H,
+                                               direct, accumulate, nti, nsp, per_xcd);
+  else if (xdtype == 1 && tm)
+    syrk_tiles<uint16_t, true><<<grid, NT, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P,
+                                                    H, direct, accumulate, nti, nsp, per_xcd);
   else if (xdtype == 1)
-    syrk_tiles<uint16_t><<<grid, NT, 0, st>>>((const uint16_t*)X, (int)n, ntok, ldx,
-                                              p.kps, aligned, (float*)partial, H,
-                                              direct, accumulate, (int)p.ntiles,
-                                              (int)p.nsplit, per_xcd);
+    syrk_tiles<uint16_t, false><<<grid, NT, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P,
+                                                     H, direct, accumulate, nti, nsp, per_xcd);
+  else if (tm)
+    syrk_tiles<float, true><<<grid, NT, 0, st>>>(Xf, (int)n, ntok, ldx, p.kps, aligned, P, H,
+                                                 direct, accumulate, nti, nsp, per_xcd);
   else
-    syrk_tiles<float><<<grid, NT, 0, st>>>((const float*)X, (int)n, ntok, ldx, p.kps,
-                                           aligned, (float*)partial, H, direct,
-                                           accumulate, (int)p.ntiles, (int)p.nsplit,
-                                           per_xcd);
+    syrk_tiles<float, false><<<grid, NT, 0, st>>>(Xf, (int)n, ntok, ldx, p.kps, aligned, P, H,
+                                                  direct, accumulate, nti, nsp, per_xcd);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ti >= 0) e = hipEventRecord(g_timer_hessian_tiles.stops[ti], st);
   if (e != hipSuccess || direct) return e;

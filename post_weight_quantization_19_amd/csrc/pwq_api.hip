@@ -159,6 +159,21 @@ const char* pwq_last_error(void) { return g_last_error.c_str(); }
 
 // ------------------------------------------------------------------ Hessian
 
+// Element type and layout of X (xdtype = PWQ_BF16 / PWQ_F32, optionally
+// | PWQ_X_TOKEN_MAJOR) and its row stride.
+static pwq_status check_x(int64_t n, int64_t ntok, int32_t xdtype, int64_t ldx) {
+  const int32_t el = xdtype & ~PWQ_X_TOKEN_MAJOR;
+  if (el != PWQ_BF16 && el != PWQ_F32)
+    return fail(PWQ_ERR_INVALID_ARG,
+                "X dtype must be PWQ_BF16 or PWQ_F32 (optionally | PWQ_X_TOKEN_MAJOR)");
+  if (xdtype & PWQ_X_TOKEN_MAJOR) {
+    if (ldx < n) return fail(PWQ_ERR_INVALID_ARG, "token-major X needs ldx >= n");
+  } else if (ldx < ntok) {
+    return fail(PWQ_ERR_INVALID_ARG, "ldx < ntok");
+  }
+  return PWQ_OK;
+}
+
 size_t pwq_hessian_workspace_size(int64_t n, int64_t ntok) {
   if (n <= 0 || ntok < 0) return 0;
   size_t need = 0;
@@ -178,12 +193,11 @@ pwq_status pwq_hessian_accum(float* H, int64_t n, const void* X, int32_t xdtype,
   if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
   if (ntok < 0) return fail(PWQ_ERR_INVALID_ARG, "ntok must be >= 0");
   if (ntok > 0 && !X) return fail(PWQ_ERR_INVALID_ARG, "X is NULL");
-  if (xdtype != PWQ_BF16 && xdtype != PWQ_F32)
-    return fail(PWQ_ERR_INVALID_ARG, "X dtype must be PWQ_BF16 or PWQ_F32");
-  if (ldx < ntok) return fail(PWQ_ERR_INVALID_ARG, "ldx < ntok");
+  pwq_status s = check_x(n, ntok, xdtype, ldx);
+  if (s != PWQ_OK) return s;
   SyrkPlan p;
-  syrk_plan(n, ntok, xdtype, syrk_aligned(X, ldx, xdtype), &p);
-  pwq_status s = check_ws(ws, ws_bytes, p.partial_bytes);
+  syrk_plan(n, ntok, xdtype, syrk_aligned(X, n, ldx, xdtype), &p);
+  s = check_ws(ws, ws_bytes, p.partial_bytes);
   if (s != PWQ_OK) return s;
   hipError_t e = launch_hessian(H, n, X, xdtype, ntok, ldx, accumulate, p, ws,
                                 (hipStream_t)stream);
@@ -349,9 +363,9 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   const bool has_x = X != nullptr;
   if (has_x == (H != nullptr)) return fail(PWQ_ERR_INVALID_ARG, "give exactly one of X and H");
   if (has_x) {
-    if (xdtype != PWQ_BF16 && xdtype != PWQ_F32)
-      return fail(PWQ_ERR_INVALID_ARG, "X dtype must be PWQ_BF16 or PWQ_F32");
-    if (ntok < 0 || ldx < ntok) return fail(PWQ_ERR_INVALID_ARG, "bad ntok / ldx");
+    if (ntok < 0) return fail(PWQ_ERR_INVALID_ARG, "ntok must be >= 0");
+    s = check_x(n, ntok, xdtype, ldx);
+    if (s != PWQ_OK) return s;
   } else if (H_out) {
     return fail(PWQ_ERR_INVALID_ARG, "H_out is only produced when X is given");
   }
@@ -363,7 +377,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
 
   const bool need_h = has_x && !H_out;
   const bool need_l = !L_out;
-  const bool xal = has_x && syrk_aligned(X, ldx, xdtype);
+  const bool xal = has_x && syrk_aligned(X, n, ldx, xdtype);
   Carver measure(nullptr);
   LayerWs w;
   carve_layer(measure, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, &w);

@@ -18,7 +18,11 @@ struct SyrkPlan {
   size_t partial_bytes;  // 0 when a single split writes H directly
 };
 
-bool syrk_aligned(const void* X, int64_t ldx, int32_t xdtype);
+// xdtype as at the boundary: element type in the low bits, kXTokenMajor
+// when X is stored ntok x n.
+constexpr int32_t kXTypeMask = 0xff;
+constexpr int32_t kXTokenMajor = 0x100;
+bool syrk_aligned(const void* X, int64_t n, int64_t ldx, int32_t xdtype);
 void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* p);
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype, int64_t ntok,
                           int64_t ldx, int32_t accumulate, const SyrkPlan& p, void* partial,

@@ -45,6 +45,12 @@ def test_hessian_validation():
     assert L.pwq_hessian_accum(FAKE, 8, FAKE, 7, 16, 16, 0, None, 0, None) == INVALID
     assert L.pwq_hessian_accum(FAKE, 8, FAKE, 1, 16, 8, 0, None, 0, None) == INVALID
     assert L.pwq_hessian_accum(FAKE, 8, None, 1, 16, 16, 0, None, 0, None) == INVALID
+    # token-major layout: ldx is checked against n, not ntok; unknown flag bits fail
+    TM = B.PWQ_X_TOKEN_MAJOR
+    assert L.pwq_hessian_accum(FAKE, 8, FAKE, 1 | TM, 16, 4, 0, None, 0, None) == INVALID
+    assert L.pwq_hessian_accum(FAKE, 8, FAKE, 1 | 0x200, 16, 16, 0, None, 0, None) == INVALID
+    assert L.pwq_hessian_accum(FAKE, 8, FAKE, 2 | TM, 16, 16, 0, None, 0, None) == INVALID
+    assert L.pwq_hessian_accum(FAKE, 4096, FAKE, 1 | TM, 131072, 4096, 0, None, 0, None) == WS
     # a long token axis needs split-K partials: workspace checks
     need = L.pwq_hessian_workspace_size(4096, 131072)
     assert need > 0
@@ -117,6 +123,10 @@ def test_quant_layer_validation():
     assert call(grid=_grid(1, 4, 0)) == INVALID           # ASYM without zeros
     assert call(grid=_grid(0, 17, 0)) == INVALID
     assert call(X=None, H=FAKE, Hout=FAKE) == INVALID     # H_out needs X
+    TM = B.PWQ_X_TOKEN_MAJOR
+    assert call(xdt=1 | TM, ldx=100) == INVALID            # token-major: ldx >= n
+    assert call(xdt=1 | TM, ldx=128) == WS                 # valid, fails on workspace only
+    assert call(xdt=1 | 0x400) == INVALID
     assert call() == WS                                   # no workspace
     need = L.pwq_quant_layer_workspace_size(64, 128, 256, 1, 0, 32, 0)
     assert need > 0
