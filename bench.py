@@ -14,6 +14,14 @@ Prints ONE JSON line.  `roofline` is for the dominant kernel (the Hessian
 SYRK tiles): algorithmic flops n(n+1)N per launch over its average duration,
 measured with HIP events that the library records around each launch of that
 kernel during the timed steps, on the stream it launches on.
+`stage_rooflines` gives the same for the other stages: the lazy block
+updates (m n (n - 128) flop against the fp32 or fp64 MFMA peak) and the
+column sweeps (14 bytes per weight against HBM), both from the library's HIP
+events around each of their launches in the timed steps, and the Cholesky
+(n^3/3 flop, stage time).  Each carries the published peak and the
+achievable one measured on the device by the peak probe
+(post_weight_quantization_19_amd/peak_probe, dense MFMA from registers and a
+1 GiB copy), run in its own process first.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -43,6 +51,8 @@ def parse():
                     help="storage of the activations: token-major [ntok, n] (one row per "
                          "token, as a layer's inputs are captured; the default) or [n, ntok]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probe (MFMA and copy microbenchmarks)")
     ap.add_argument("--cpu-token-fraction", type=int, default=8,
                     help="oracle Hessian is timed on 1/k of the tokens, scaled by k")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -126,6 +136,53 @@ def cpu_baseline(lay, cfg, frac):
     }
 
 
+def sweep_launches(n, B):
+    """(sweep-block launches, lazy updates, update flops / m) of one sweep, in
+    the order the library issues them (blocks from the back, sub-blocks of at
+    most 128 columns, an in-block update after every sub-block but the
+    block's first column group, a block update for every block above 0)."""
+    bi = min(B, 128)
+    nsweep = nupd = 0
+    flops_per_row = 0.0
+    for jb0 in range(((n - 1) // B) * B, -1, -B):
+        jb1 = min(n, jb0 + B)
+        nsub = (jb1 - jb0 + bi - 1) // bi
+        for s in range(nsub - 1, -1, -1):
+            js0 = jb0 + s * bi
+            nsweep += 1
+            if s > 0:
+                nupd += 1
+                flops_per_row += 2.0 * min(jb1 - js0, bi) * (js0 - jb0)
+        if jb0 > 0:
+            nupd += 1
+            flops_per_row += 2.0 * (jb1 - jb0) * jb0
+    return nsweep, nupd, flops_per_row
+
+
+def measure_peaks():
+    """Achievable peaks from the committed probe (a separate process, run
+    before this one touches the GPU), or None."""
+    import subprocess
+    exe = os.path.join(ROOT, "post_weight_quantization_19_amd", "peak_probe")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        return None
+    if r.returncode != 0:
+        print(f"[bench] peak probe failed: {r.stderr.strip()}", file=sys.stderr)
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def stage_roofline(achieved, peak, achievable, unit, bound, work, how):
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "achievable": achievable,
+            "frac_of_achievable": (achieved / achievable) if achievable else None,
+            "work_per_step": work, "timed_by": how}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -140,6 +197,10 @@ def main():
     import post_weight_quantization_19_amd as P
     import synth
 
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] achievable peaks (probe)", file=sys.stderr, flush=True)
+        peaks = measure_peaks()
     cfg = synth.config(args.config)
     m, n, N = cfg.m, cfg.n, cfg.ntok
     print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
@@ -202,6 +263,18 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    # the lazy updates and block sweeps are timed in a separate pass of as
+    # many steps (their 2 x 63 event records per step would perturb the
+    # headline timing above)
+    nsweep, nupd, upd_flops_row = sweep_launches(n, cfg.block)
+    t_upd = P.KernelTimer("lazy_update", args.steps * nupd)
+    t_swp = P.KernelTimer("sweep_block", args.steps * nsweep)
+    torch.cuda.synchronize()
+    with t_upd, t_swp:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+
     # stage breakdown (same library calls, separately)
     def timed(fn, r=3):
         fn()
@@ -223,8 +296,6 @@ def main():
     s, z = (None, None) if cfg.grid_kind == "colspacing" else P.grid_steps(W, grid)
     t_chol = timed(lambda: P.damp_cholesky(H, damp=cfg.damp, prec=prec))
     t_sweep = timed(lambda: P.babai_sweep(W, Lf, grid, scales=s, zeros=z, block=cfg.block))
-    flops_upd = float(m) * n * (n - cfg.block)
-    peak_upd = PEAK_F32_TFLOPS if prec == "f32" else PEAK_F64_TFLOPS
     if has_x:
         stored = "stored token-major [ntok, n]" if xl == "tokens" else "stored [n, ntok]"
         inputs = (f"X {n}x{N} bf16 {stored} " + ("Student-t(4)" if cfg.x_kind == "student_t" else
@@ -234,6 +305,35 @@ def main():
     else:
         inputs = f"H {n}x{n} fp32 = L0 diag(k^-1.2) L0^T"
         grid_txt = f"column spacing c/l_kk, c = {grid.c:.6g}"
+
+    # per-stage rooflines (SURVEY 8d style): SYRK and lazy update against
+    # their MFMA peaks, Cholesky n^3/3 against its MFMA peak (stage time),
+    # the sweep's ~14 bytes per weight against HBM
+    pk = peaks or {}
+    mf_peak, mf_key = (PEAK_F32_TFLOPS, "mfma_f32_tflops") if prec == "f32" else \
+        (PEAK_F64_TFLOPS, "mfma_f64_tflops")
+    upd_ms = sum(t_upd.durations_ms()) / args.steps
+    swp_ms = sum(t_swp.durations_ms()) / args.steps
+    upd_flops = m * upd_flops_row
+    stages = {
+        "cholesky": stage_roofline(n ** 3 / 3.0 / (t_chol / 1e3) / 1e12, mf_peak, pk.get(mf_key),
+                                   "TFLOP/s", "mfma", n ** 3 / 3.0,
+                                   "stage time (damp + factor), CUDA events"),
+        "lazy_update": stage_roofline(upd_flops / (upd_ms / 1e3) / 1e12, mf_peak,
+                                      pk.get(mf_key), "TFLOP/s", "mfma", upd_flops,
+                                      f"library HIP events around each of the {nupd} updates "
+                                      "of a step (separate pass)"),
+        "sweep": stage_roofline(14.0 * m * n / (swp_ms / 1e3) / 1e9, PEAK_HBM_GBS,
+                                pk.get("copy_gbs"), "GB/s", "hbm (latency: serial columns)",
+                                14.0 * m * n,
+                                f"library HIP events around each of the {nsweep} block sweeps "
+                                "of a step (separate pass)"),
+    }
+    if roofline is not None:
+        stages["hessian_tiles"] = stage_roofline(
+            roofline["achieved"], PEAK_BF16_TFLOPS, pk.get("mfma_bf16_tflops"), "TFLOP/s",
+            "mfma", roofline["flops_per_launch"], "library HIP events around each launch")
+        roofline["achievable"] = pk.get("mfma_bf16_tflops")
 
     line = {
         "metric": METRIC,
@@ -255,8 +355,10 @@ def main():
                    "layer_quantize_time_s": dt},
         "roofline": roofline,
         "stages_ms": {"hessian_accum": t_hess, "damp_cholesky": t_chol,
-                      "sweep_and_update": t_sweep},
-        "update_mfma_util_upper": (flops_upd / (t_sweep / 1e3) / 1e12) / peak_upd,
+                      "sweep_and_update": t_sweep, "lazy_updates_in_step": upd_ms,
+                      "block_sweeps_in_step": swp_ms},
+        "stage_rooflines": stages,
+        "achievable_peaks": peaks,
         "loss": res0["loss"], "bound": res0["bound"],
     }
     if not args.no_cpu_baseline:

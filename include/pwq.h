@@ -257,16 +257,27 @@ pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_
  * the stream it is launched on; later launches are not recorded.
  *   kernel   : PWQ_TIMER_HESSIAN_TILES = the Hessian product kernel (the
  *              bf16/fp32 SYRK tiles of pwq_hessian_accum and of
- *              pwq_quant_layer, without the split-K reduction).
+ *              pwq_quant_layer, without the split-K reduction);
+ *              PWQ_TIMER_LAZY_UPDATE = one lazy block update of the sweep
+ *              (acc[:, cols] += E[:, blk] L[blk, cols]; one pair per update,
+ *              which may be several launches of the update kernel);
+ *              PWQ_TIMER_SWEEP_BLOCK = one launch of the column sweep of a
+ *              block (at most 128 columns) over all rows.
  *   capacity : number of event pairs; 0 (with NULL arrays) detaches.
+ * The kernels are timed independently; several may be attached at once.
  * The arrays must stay valid until detach.  Process-wide state, not
  * thread safe: attach, run, synchronise, detach from one thread.
- * pwq_kernel_timer_count returns the pairs recorded since the last attach.
+ * pwq_kernel_timer_count returns the pairs recorded for `kernel` since its
+ * last attach (-1 for an unknown kernel).
  * ---------------------------------------------------------------------- */
-typedef enum { PWQ_TIMER_HESSIAN_TILES = 0 } pwq_timed_kernel;
+typedef enum {
+  PWQ_TIMER_HESSIAN_TILES = 0,
+  PWQ_TIMER_LAZY_UPDATE = 1,
+  PWQ_TIMER_SWEEP_BLOCK = 2
+} pwq_timed_kernel;
 pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* const* stops,
                                    int64_t capacity);
-int64_t pwq_kernel_timer_count(void);
+int64_t pwq_kernel_timer_count(int32_t kernel);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ from . import _lib
 from ._lib import PwqError, check, lib, make_grid, parse_result
 
 __all__ = ["Grid", "hessian_accum", "damp_cholesky", "grid_steps", "babai_sweep",
-           "quant_layer", "column_entropy", "read_result", "PwqError", "HessianTileTimer"]
+           "quant_layer", "column_entropy", "read_result", "PwqError", "KernelTimer",
+           "HessianTileTimer"]
 
 
 @dataclass(frozen=True)
@@ -237,12 +238,15 @@ def column_entropy(codes: torch.Tensor, huffman: bool = False):
     return (bits, mean, huff) if huffman else (bits, mean)
 
 
-class HessianTileTimer:
-    """Times the Hessian product kernel itself (pwq_kernel_timer_attach):
+class KernelTimer:
+    """Times one of the library's kernels (pwq_kernel_timer_attach):
     inside the ``with`` block, its first ``capacity`` launches record a pair
-    of HIP events on the stream they run on.  Measurement only."""
+    of HIP events on the stream they run on.  ``kernel`` is "hessian_tiles"
+    (the SYRK tiles), "lazy_update" (one lazy block update of the sweep) or
+    "sweep_block" (one block of the column sweep).  Measurement only."""
 
-    def __init__(self, capacity: int):
+    def __init__(self, kernel: str, capacity: int):
+        self.kernel = _lib.TIMED_KERNELS[kernel]
         self.starts = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
         self.stops = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
         for e in self.starts + self.stops:
@@ -254,13 +258,12 @@ class HessianTileTimer:
         self.count = 0
 
     def __enter__(self):
-        check(lib().pwq_kernel_timer_attach(_lib.PWQ_TIMER_HESSIAN_TILES, self._s, self._e,
-                                            self.capacity))
+        check(lib().pwq_kernel_timer_attach(self.kernel, self._s, self._e, self.capacity))
         return self
 
     def __exit__(self, *exc):
-        self.count = int(lib().pwq_kernel_timer_count())
-        check(lib().pwq_kernel_timer_attach(_lib.PWQ_TIMER_HESSIAN_TILES, None, None, 0))
+        self.count = int(lib().pwq_kernel_timer_count(self.kernel))
+        check(lib().pwq_kernel_timer_attach(self.kernel, None, None, 0))
         return False
 
     def durations_ms(self):
@@ -268,3 +271,10 @@ class HessianTileTimer:
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in zip(self.starts[:self.count],
                                                   self.stops[:self.count])]
+
+
+class HessianTileTimer(KernelTimer):
+    """KernelTimer of the Hessian product kernel."""
+
+    def __init__(self, capacity: int):
+        super().__init__("hessian_tiles", capacity)

@@ -28,7 +28,9 @@ EXPORTS = [
     "pwq_rate_workspace_size", "pwq_column_entropy",
     "pwq_kernel_timer_attach", "pwq_kernel_timer_count",
 ]
-PWQ_TIMER_HESSIAN_TILES = 0
+PWQ_TIMER_HESSIAN_TILES, PWQ_TIMER_LAZY_UPDATE, PWQ_TIMER_SWEEP_BLOCK = 0, 1, 2
+TIMED_KERNELS = {"hessian_tiles": PWQ_TIMER_HESSIAN_TILES, "lazy_update": PWQ_TIMER_LAZY_UPDATE,
+                 "sweep_block": PWQ_TIMER_SWEEP_BLOCK}
 
 
 class PwqGrid(ctypes.Structure):
@@ -71,7 +73,7 @@ _SIGS = {
     "pwq_rate_workspace_size": (_sz, [_i64]),
     "pwq_column_entropy": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_kernel_timer_attach": (_i32, [_i32, _vp, _vp, _i64]),
-    "pwq_kernel_timer_count": (_i64, []),
+    "pwq_kernel_timer_count": (_i64, [_i32]),
 }
 
 

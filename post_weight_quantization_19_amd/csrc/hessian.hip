@@ -663,11 +663,10 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
   const int per_xcd = (int)((items + 7) / 8);
   const unsigned grid = (unsigned)(8 * per_xcd);
   if (p.tile == BL && !aligned) return hipErrorInvalidValue;  // checked by the caller
-  const int64_t ti = g_timer_hessian_tiles.next();
-  if (ti >= 0) {
-    const hipError_t e = hipEventRecord(g_timer_hessian_tiles.starts[ti], st);
-    if (e != hipSuccess) return e;
-  }
+  KernelTimer& timer = g_timers[PWQ_TIMER_HESSIAN_TILES];
+  hipError_t te = hipSuccess;
+  const int64_t ti = timer.begin(st, &te);
+  if (te != hipSuccess) return te;
   const float* Xf = (const float*)X;
   const uint16_t* Xh = (const uint16_t*)X;
   float* P = (float*)partial;
@@ -691,7 +690,7 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
     syrk_tiles<float, false><<<grid, NT, 0, st>>>(Xf, (int)n, ntok, ldx, p.kps, aligned, P, H,
                                                   direct, accumulate, nti, nsp, per_xcd);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ti >= 0) e = hipEventRecord(g_timer_hessian_tiles.stops[ti], st);
+  if (e == hipSuccess) e = timer.end(ti, st);
   if (e != hipSuccess || direct) return e;
   if (p.tile == BL)
     syrk_reduce<BL><<<(unsigned)(p.ntiles * 16), 256, 0, st>>>(

@@ -11,7 +11,7 @@
 using namespace pwq;
 
 namespace pwq {
-KernelTimer g_timer_hessian_tiles;
+KernelTimer g_timers[kNumTimers];
 }
 
 namespace {
@@ -454,12 +454,12 @@ pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_
 
 pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* const* stops,
                                    int64_t capacity) {
-  if (kernel != PWQ_TIMER_HESSIAN_TILES)
+  if (kernel < 0 || kernel >= kNumTimers)
     return fail(PWQ_ERR_INVALID_ARG, "unknown timed kernel %d", kernel);
   if (capacity < 0) return fail(PWQ_ERR_INVALID_ARG, "capacity must be >= 0");
   if (capacity > 0 && (!starts || !stops))
     return fail(PWQ_ERR_INVALID_ARG, "event arrays are NULL");
-  KernelTimer& t = g_timer_hessian_tiles;
+  KernelTimer& t = g_timers[kernel];
   t.starts = capacity ? (hipEvent_t*)starts : nullptr;
   t.stops = capacity ? (hipEvent_t*)stops : nullptr;
   t.capacity = capacity;
@@ -467,6 +467,8 @@ pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* co
   return ok();
 }
 
-int64_t pwq_kernel_timer_count(void) { return g_timer_hessian_tiles.used; }
+int64_t pwq_kernel_timer_count(int32_t kernel) {
+  return (kernel >= 0 && kernel < kNumTimers) ? g_timers[kernel].used : -1;
+}
 
 }  // extern "C"

@@ -84,7 +84,18 @@ struct KernelTimer {
   int64_t used = 0;
   // Returns the pair index to record, or -1 when not attached / full.
   int64_t next() { return used < capacity ? used++ : -1; }
+  // Start event of the next pair on `st` (if attached); returns its index.
+  int64_t begin(hipStream_t st, hipError_t* err) {
+    const int64_t i = next();
+    if (i >= 0) *err = hipEventRecord(starts[i], st);
+    return i;
+  }
+  hipError_t end(int64_t i, hipStream_t st) {
+    return i >= 0 ? hipEventRecord(stops[i], st) : hipSuccess;
+  }
 };
-extern KernelTimer g_timer_hessian_tiles;
+// indexed by pwq_timed_kernel
+constexpr int kNumTimers = 3;
+extern KernelTimer g_timers[kNumTimers];
 
 }  // namespace pwq

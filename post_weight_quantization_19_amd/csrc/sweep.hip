@@ -628,23 +628,40 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
   const int nblk = (n + B - 1) / B;
   const unsigned nwg = (unsigned)((m + 15) / 16);
   int part = 0;
+  KernelTimer& tsweep = g_timers[PWQ_TIMER_SWEEP_BLOCK];
+  KernelTimer& tupd = g_timers[PWQ_TIMER_LAZY_UPDATE];
   for (int b = nblk - 1; b >= 0 && nwg > 0; --b) {
     const int jb0 = b * B, jb1 = (n < jb0 + B) ? n : jb0 + B;
     const int nsub = (jb1 - jb0 + Bi - 1) / Bi;
     for (int s = nsub - 1; s >= 0; --s) {
       const int js0 = jb0 + s * Bi;
       const int first_sub = (b == nblk - 1) && (s == nsub - 1);
+      hipError_t te = hipSuccess;
+      int64_t ti = tsweep.begin(st, &te);
+      if (te != hipSuccess) return te;
       sweep_block<T, Bi><<<nwg, 256, 0, st>>>(a, js0, B, js0 - jb0, first_sub, part++);
+      te = tsweep.end(ti, st);
+      if (te != hipSuccess) return te;
       if (s > 0) {
         // the sub-block's errors reach the open columns of its own block
         const int kb = (jb1 - js0 < Bi) ? jb1 - js0 : Bi;
+        ti = tupd.begin(st, &te);
+        if (te != hipSuccess) return te;
         update_launch<T>((const T*)sl.E, B, js0 - jb0, kb, (const T*)sl.L, n, js0, jb0, js0, m,
                          (T*)sl.acc, first_sub, sl.flags, st);
+        te = tupd.end(ti, st);
+        if (te != hipSuccess) return te;
       }
     }
-    if (jb0 > 0)   // the block's errors reach every earlier column
+    if (jb0 > 0) {   // the block's errors reach every earlier column
+      hipError_t te = hipSuccess;
+      const int64_t ti = tupd.begin(st, &te);
+      if (te != hipSuccess) return te;
       update_launch<T>((const T*)sl.E, B, 0, jb1 - jb0, (const T*)sl.L, n, jb0, 0, jb0, m,
                        (T*)sl.acc, b == nblk - 1, sl.flags, st);
+      te = tupd.end(ti, st);
+      if (te != hipSuccess) return te;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -147,10 +147,17 @@ def test_workspace_sizes_grow_with_the_problem():
 def test_kernel_timer_validation():
     L = B.lib()
     assert L.pwq_kernel_timer_attach(5, None, None, 0) == INVALID
+    assert L.pwq_kernel_timer_attach(3, None, None, 0) == INVALID
+    assert L.pwq_kernel_timer_attach(-1, None, None, 0) == INVALID
+    assert L.pwq_kernel_timer_count(3) == -1
+    for k in (B.PWQ_TIMER_LAZY_UPDATE, B.PWQ_TIMER_SWEEP_BLOCK):
+        assert L.pwq_kernel_timer_attach(k, None, None, 2) == INVALID
+        assert L.pwq_kernel_timer_attach(k, None, None, 0) == OK
+        assert L.pwq_kernel_timer_count(k) == 0
     assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, -1) == INVALID
     assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, 4) == INVALID
     assert L.pwq_kernel_timer_attach(B.PWQ_TIMER_HESSIAN_TILES, None, None, 0) == OK
-    assert L.pwq_kernel_timer_count() == 0
+    assert L.pwq_kernel_timer_count(B.PWQ_TIMER_HESSIAN_TILES) == 0
 
 
 def test_rate_validation():

@@ -1,5 +1,5 @@
-"""The kernel timing hook: event pairs are recorded around the Hessian tile
-kernel only while attached, up to the capacity, and the product is unchanged."""
+"""The kernel timing hook: event pairs are recorded around the timed kernels
+only while attached, up to the capacity, and the results are unchanged."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +23,30 @@ def test_hessian_tile_timer_records_pairs():
     assert len(d) == 2 and all(x > 0 for x in d)
     H4 = P.hessian_accum(X)          # detached: nothing more is recorded
     torch.cuda.synchronize()
-    assert P.lib().pwq_kernel_timer_count() == 0
+    assert P.lib().pwq_kernel_timer_count(0) == 0
     for Hk in (H1, H2, H3, H4):
         assert torch.equal(Hk, H0)
     assert np.isfinite(H0.cpu().numpy()).all()
+
+
+def test_sweep_and_update_timers_count_launches():
+    """One sweep pair per sub-block of at most 128 columns, one update pair per
+    lazy update (every block but the first, plus the in-block sub-block
+    updates), for block 256 (two sub-blocks per block) on 640 columns."""
+    g = torch.Generator().manual_seed(3)
+    m, n, ntok, B = 64, 640, 2048, 256
+    W = (0.02 * torch.randn((m, n), generator=g)).to(torch.bfloat16).cuda()
+    X = torch.randn((n, ntok), generator=g).to(torch.bfloat16).cuda()
+    grid = P.Grid("sym", 4, 128)
+    ref = P.quant_layer(W, X=X, grid=grid, block=B)
+    ts = P.KernelTimer("sweep_block", 64)
+    tu = P.KernelTimer("lazy_update", 64)
+    with ts, tu:
+        out = P.quant_layer(W, X=X, grid=grid, block=B)
+    torch.cuda.synchronize()
+    # blocks [512, 640), [256, 512), [0, 256): sub-blocks 1 + 2 + 2
+    assert ts.count == 5
+    # in-block updates: 0 + 1 + 1; block updates: 2 (every block above column 0)
+    assert tu.count == 4
+    assert all(d > 0 for d in ts.durations_ms() + tu.durations_ms())
+    assert torch.equal(out["codes"], ref["codes"])
