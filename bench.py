@@ -65,10 +65,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_tiles256_qproj_4096x4096_tra
 KERNEL_SOURCE = os.path.join(ROOT, "post_weight_quantization_19_amd", "csrc", "hessian.hip")
 
 
-def measured_traffic():
+def measured_traffic(x_layout):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, or None if the kernel source has changed since
-    the counters were taken."""
+    the counters were taken or they were taken for the other X layout."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -77,7 +77,7 @@ def measured_traffic():
             h = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if t.get("kernel_source_sha256") != h:
+    if t.get("kernel_source_sha256") != h or t.get("x_layout") != x_layout:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -257,7 +257,7 @@ def main():
                     "kernel": "syrk_tiles256 (bf16 SYRK tiles of H = 2 X X^T)",
                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / PEAK_BF16_TFLOPS,
-                    "traffic": measured_traffic() if args.config == 2 else None,
+                    "traffic": measured_traffic(xl) if args.config == 2 else None,
                     "avg_launch_ms": t_tiles * 1e3, "launches_timed": len(tiles_ms),
                     "flops_per_launch": flops_h}
 

@@ -111,7 +111,7 @@ def counter_per_dispatch(d, counter):
 
 
 def traffic(fetch_dir, write_dir, kernel, algorithmic_bytes, source, commands, title,
-            workload):
+            workload, x_layout=None):
     fv = counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     wv = counter_per_dispatch(write_dir, "WRITE_SIZE")
 
@@ -131,7 +131,8 @@ def traffic(fetch_dir, write_dir, kernel, algorithmic_bytes, source, commands, t
     with open(source, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     return {
-        "title": title, "kernel": kernel, "workload": workload, "commands": commands,
+        "title": title, "kernel": kernel, "workload": workload, "x_layout": x_layout,
+        "commands": commands,
         "fetch_size_kib_per_dispatch": fkib, "fetch_dispatches": len(kf),
         "write_size_kib_per_dispatch": wkib, "write_dispatches": len(kw),
         "calibration": {"kernel": "1 GiB device-to-device copy (bench.py --copy-calibration)",
@@ -163,13 +164,14 @@ def main(argv=None):
     t.add_argument("--command", action="append", required=True)
     t.add_argument("--title", default="HBM traffic per launch")
     t.add_argument("--workload", default="")
+    t.add_argument("--x-layout", default=None, help="X layout the counters were taken with")
     t.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         txt = stats_markdown(a.dir, a.command, a.title, a.launches, a.bench_log)
     else:
         txt = json.dumps(traffic(a.fetch, a.write, a.kernel, a.algorithmic_bytes, a.source,
-                                 a.command, a.title, a.workload), indent=1) + "\n"
+                                 a.command, a.title, a.workload, a.x_layout), indent=1) + "\n"
     with open(a.out, "w") as f:
         f.write(txt)
     sys.stdout.write(txt)
