@@ -34,17 +34,19 @@ __device__ __forceinline__ T load_w(const void* W, int32_t wdtype, int64_t idx) 
 }
 
 // Broadcast lane q of every 16-lane row to the whole row (DPP row_newbcast).
+// Every lane is written (all rows and banks enabled), so the "old" operand
+// is the value itself: no separate register has to be cleared first.
 template <int Q>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                         0x150 + Q, 0xF, 0xF, false));
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x150 + Q, 0xF, 0xF, false));
 }
 template <int Q>
 __device__ __forceinline__ double row_bcast(double v) {
   long long b = __builtin_bit_cast(long long, v);
-  int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), 0x150 + Q, 0xF, 0xF, false);
-  int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), 0x150 + Q, 0xF, 0xF, false);
+  const int l0 = (int)(b & 0xffffffffll), h0 = (int)(b >> 32);
+  int lo = __builtin_amdgcn_update_dpp(l0, l0, 0x150 + Q, 0xF, 0xF, false);
+  int hi = __builtin_amdgcn_update_dpp(h0, h0, 0x150 + Q, 0xF, 0xF, false);
   return __builtin_bit_cast(double, (long long)(((unsigned long long)(unsigned)hi << 32) |
                                                 (unsigned long long)(unsigned)lo));
 }

@@ -125,17 +125,69 @@ struct SweepArgs {
   const DevFlags* flags;
 };
 
+// 16-byte vector of T (4 floats or 2 doubles).
+template <typename T> struct Vec16;
+template <> struct Vec16<float> { typedef float4 type; };
+template <> struct Vec16<double> { typedef double2 type; };
+
+// Rows cb .. cb + CH - 1 of the block's strictly-lower part of L, stored
+// transposed: Lt[i * LP + r] = L[j0 + cb + r][j0 + i] for i < cb + r (zero
+// elsewhere and for rows past n), so the coefficients of one column i for
+// consecutive rows are contiguous.  Thread t takes row r = t % CH and the
+// column range (t / CH) of the block; consecutive lanes write consecutive
+// LDS words.  `vec`: 16-byte loads (whole block inside the matrix, rows
+// 16-byte aligned).
+template <typename T, int B, int CH, int LP>
+__device__ __forceinline__ void stage_lt(T* __restrict__ Lt, const T* __restrict__ L, int n,
+                                         int j0, int cb, bool vec) {
+  constexpr int VW = 16 / (int)sizeof(T);
+  constexpr int PARTS = 256 / CH, CW = B / PARTS;
+  static_assert(256 % CH == 0 && B % PARTS == 0 && CW % VW == 0, "staging shape");
+  typedef typename Vec16<T>::type V;
+  const int r = threadIdx.x % CH, part = threadIdx.x / CH;
+  const int kr = cb + r;
+  const bool rowok = j0 + kr < n;
+  const T* src = L + (int64_t)(rowok ? j0 + kr : 0) * n + j0 + part * CW;
+  // all of the thread's loads first, then the LDS writes (one wait)
+  T v[CW];
+  if (vec) {
+    // uniform: the whole block lies inside the matrix, every row is valid
+#pragma unroll
+    for (int c = 0; c < CW; c += VW) {
+      const V x = *(const V*)(src + c);
+      __builtin_memcpy(&v[c], &x, sizeof(x));
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int i = part * CW + c;
+      v[c] = (rowok && i < kr) ? src[c] : (T)0;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const int i = part * CW + c;
+    Lt[i * LP + r] = (rowok && i < kr) ? v[c] : (T)0;
+  }
+}
+
 // One sub-block of Bi columns [j0, j0 + Bi) of every row.  E (leading
 // dimension ldE) receives the sub-block's errors at column offset e_off.
 template <typename T, int B>
 __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int ldE, int e_off,
                                                   int first, int part) {
   constexpr int P = 16, S = B / P;
-  // rows of L staged per LDS pass (64 KB of the CU's 160 KB)
+  // rows of L staged per LDS pass (about 64 KB of the CU's 160 KB)
   constexpr int CH0 = 65536 / (B * (int)sizeof(T));
   constexpr int CH = CH0 < 8 ? 8 : (CH0 > B ? B : CH0);
   static_assert(B % CH == 0, "chunk must divide block");
-  __shared__ T Ls[CH * B];
+  // L is read VW rows (columns of the sweep) at a time: one 16-byte LDS read
+  // per slot covers the next VW columns
+  constexpr int VW = 16 / (int)sizeof(T);
+  constexpr int LP = CH + VW;           // padded: 16 lanes hit distinct banks
+  static_assert(CH % VW == 0, "groups inside a chunk");
+  typedef typename Vec16<T>::type V;
+  __shared__ __attribute__((aligned(16))) T Lt[B * LP];
   __shared__ double red[4][4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -146,61 +198,133 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int l
 
   T acc[S], av[S], bv[S], sv[S], wv[S], dv[S];
   int ocv[S], zpv[S];
+  // Every slot's loads are issued together, from indices clamped into the
+  // arrays (row 0 / column 0 for slots outside the matrix), and the values
+  // selected afterwards: no per-slot branch serializes their latencies.
+  const int rowc = rok ? row : 0;
+  int colc[S];
+  bool okv[S];
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const int col = j0 + q + P * t;
-    const bool ok = rok && col < n;
-    T w = (T)0, s = (T)1, il = (T)0, ac = (T)0, d = (T)0;
-    int oc = -1, zp = 0;
-    if (ok) {
-      oc = a.colmap ? a.colmap[col] : col;
-      w = load_w<T>(a.W, a.wdtype, (int64_t)row * a.ldw + oc);
-      if (a.dead && a.dead[oc]) w = (T)0;
-      s = a.alpha ? a.alpha[col] : (T)a.scales[(int64_t)row * a.ng + oc / a.G];
-      if (a.zeros) zp = a.zeros[(int64_t)row * a.ng + oc / a.G];
-      il = a.invd[col];
-      d = a.dg[col];
-      if (!first) ac = a.acc[(int64_t)row * n + col];
-    }
+    okv[t] = rok && col < n;
+    colc[t] = okv[t] ? col : 0;
+    ocv[t] = colc[t];
+  }
+  if (a.colmap) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) ocv[t] = a.colmap[colc[t]];
+  }
+  // (uniform branches outside the slot loops, raw bits kept until every
+  // load is in flight, so that no conversion forces an early wait)
+  uint32_t wraw[S];
+  int dd[S], zl[S];
+  float sraw[S];
+  T al0[S], il0[S], dl0[S], acl[S];
+  int64_t gi[S];
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    gi[t] = (int64_t)rowc * a.ng + ocv[t] / a.G;
+    dd[t] = 0;
+    zl[t] = 0;
+    sraw[t] = 1.0f;
+    al0[t] = (T)1;
+    acl[t] = (T)0;
+  }
+  if (a.wdtype == 1) {
+    const uint16_t* W16 = (const uint16_t*)a.W + (int64_t)rowc * a.ldw;
+#pragma unroll
+    for (int t = 0; t < S; ++t) wraw[t] = W16[ocv[t]];
+  } else {
+    const uint32_t* W32 = (const uint32_t*)a.W + (int64_t)rowc * a.ldw;
+#pragma unroll
+    for (int t = 0; t < S; ++t) wraw[t] = W32[ocv[t]];
+  }
+  if (a.dead) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) dd[t] = a.dead[ocv[t]];
+  }
+  if (a.alpha) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) al0[t] = a.alpha[colc[t]];
+  } else {
+#pragma unroll
+    for (int t = 0; t < S; ++t) sraw[t] = a.scales[gi[t]];
+  }
+  if (a.zeros) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) zl[t] = a.zeros[gi[t]];
+  }
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    il0[t] = a.invd[colc[t]];
+    dl0[t] = a.dg[colc[t]];
+  }
+  if (!first) {
+    const T* accr = a.acc + (int64_t)rowc * n;
+#pragma unroll
+    for (int t = 0; t < S; ++t) acl[t] = accr[colc[t]];
+  }
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const bool ok = okv[t];
+    const T wl = a.wdtype == 1 ? (T)bf16_to_f32((uint16_t)wraw[t]) : (T)__uint_as_float(wraw[t]);
+    const T sl = a.alpha ? al0[t] : (T)sraw[t];
+    const T w = (ok && !dd[t]) ? wl : (T)0;
+    const T s = ok ? sl : (T)1;
+    const T il = ok ? il0[t] : (T)0;
+    const T d = ok ? dl0[t] : (T)0;
+    const T ac = ok ? acl[t] : (T)0;
+    const int zp = ok ? zl[t] : 0;
+    ocv[t] = ok ? ocv[t] : -1;
     // true (correctly rounded) quotients: with no feedback yet the coordinate
     // is exactly w / s, so an exact tie is rounded to even as on paper
     acc[t] = ac;
     av[t] = il / s;
     bv[t] = w / s;
+    // computed here, off the column chain (the compiler would otherwise
+    // sink each division to the first column that uses it)
+    pin(av[t]);
+    pin(bv[t]);
     sv[t] = s;
     wv[t] = w;
     dv[t] = d;
-    ocv[t] = oc;
     zpv[t] = zp;
   }
   int32_t* codes_row = a.codes + (int64_t)(rok ? row : 0) * n;
   T* e_row = a.E + (int64_t)(rok ? row : 0) * ldE + e_off;
 
   double loss_d = 0.0, bound = 0.0, dsq = 0.0;
-  T lc[S], ln[S];  // coefficients l_kj of the current / next column
+  // coefficients l_kj of the current and the next group of VW columns (k),
+  // for the lane's columns j = q + 16 t (one 16-byte LDS read per slot)
+  V cur[S], nxt[S];
 #pragma unroll
-  for (int t = 0; t < S; ++t) lc[t] = ln[t] = (T)0;
+  for (int t = 0; t < S; ++t) {
+    __builtin_memset(&cur[t], 0, sizeof(V));
+    __builtin_memset(&nxt[t], 0, sizeof(V));
+  }
+  const bool vec = j0 + B <= n && n % VW == 0 && ((uintptr_t)a.L % 16) == 0;
 
   static_for_down<B - 1>([&](auto KK) {
     constexpr int kk = decltype(KK)::value;
     constexpr int t = kk / P, qk = kk % P;
+    constexpr int pos = kk % VW;          // position in its group (VW-1 first)
     if constexpr (kk % CH == CH - 1) {
       // stage rows j0+kk-CH+1 .. j0+kk of L (strictly-lower part of the block)
       constexpr int cb = kk - CH + 1;
       __syncthreads();
-      tile_to_lds<T, CH, B, 256, B>(Ls, tid, [&](int rr, int i) {
-        const int kr = cb + rr;
-        return (i < kr && j0 + kr < n) ? a.L[(int64_t)(j0 + kr) * n + j0 + i] : (T)0;
-      });
+      stage_lt<T, B, CH, LP>(Lt, a.L, n, j0, cb, vec);
       __syncthreads();
 #pragma unroll
-      for (int t2 = 0; t2 <= t; ++t2) lc[t2] = Ls[(kk % CH) * B + q + P * t2];
+      for (int t2 = 0; t2 <= t; ++t2)
+        cur[t2] = *(const V*)&Lt[(q + P * t2) * LP + (kk % CH) - (VW - 1)];
     }
-    // prefetch the next column's coefficients when they are already staged
-    if constexpr (kk > 0 && (kk - 1) % CH != CH - 1) {
-      constexpr int tn = (kk - 1) / P;
+    // the next group's coefficients, one group ahead, when already staged
+    if constexpr (pos == VW - 1 && kk >= VW && (kk - VW) % CH != CH - 1) {
+      constexpr int kn = kk - VW, tn = kn / P;
 #pragma unroll
-      for (int t2 = 0; t2 <= tn; ++t2) ln[t2] = Ls[((kk - 1) % CH) * B + q + P * t2];
+      for (int t2 = 0; t2 <= tn; ++t2)
+        nxt[t2] = *(const V*)&Lt[(q + P * t2) * LP + (kn % CH) - (VW - 1)];
     }
     const T c = acc[t] * av[t] + bv[t];
     const T z = rint_t(c);
@@ -208,34 +332,40 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int l
     const T eb = row_bcast<qk>(e);
 #pragma unroll
     for (int t2 = 0; t2 <= t; ++t2) {
-      acc[t2] += eb * lc[t2];
+      acc[t2] += eb * (&cur[t2].x)[pos];
       // materialise the update here: without this the compiler sinks the
       // updates toward their distant use and keeps every broadcast alive
       pin(acc[t2]);
     }
-    if constexpr (qk == 0) {
-      // every lane's slot t is final now: record its decision
-      const T cc = acc[t] * av[t] + bv[t];
-      const T zz = rint_t(cc);
-      const T rho = cc - zz;
-      const T ee = wv[t] - sv[t] * zz;
-      if (ocv[t] >= 0) {
-        codes_row[ocv[t]] = (int32_t)zz + zpv[t];
-        e_row[q + P * t] = ee;
-        const double sl = (double)sv[t] * (double)dv[t];
-        loss_d += (double)rho * (double)rho * sl * sl;
-        bound += sl * sl;
-        dsq += (double)ee * (double)ee;
-      } else if (rok) {
-        e_row[q + P * t] = (T)0;
-      }
-    }
+    if constexpr (pos == 0) {
 #pragma unroll
-    for (int t2 = 0; t2 < S; ++t2) lc[t2] = ln[t2];
+      for (int t2 = 0; t2 < S; ++t2) cur[t2] = nxt[t2];
+    }
     // one column per scheduling region: bounded live ranges
     __builtin_amdgcn_sched_barrier(0);
   });
 
+  // Record the decisions.  Slot t of every lane is final once column 16 t
+  // has been swept (later columns add only the zero upper-triangle
+  // coefficients to it), so the running target here is the one each column
+  // was rounded at; done after the column chain to keep it short.
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const T cc = acc[t] * av[t] + bv[t];
+    const T zz = rint_t(cc);
+    const T rho = cc - zz;
+    const T ee = wv[t] - sv[t] * zz;
+    if (ocv[t] >= 0) {
+      codes_row[ocv[t]] = (int32_t)zz + zpv[t];
+      e_row[q + P * t] = ee;
+      const double sl = (double)sv[t] * (double)dv[t];
+      loss_d += (double)rho * (double)rho * sl * sl;
+      bound += sl * sl;
+      dsq += (double)ee * (double)ee;
+    } else if (rok) {
+      e_row[q + P * t] = (T)0;
+    }
+  }
   loss_d = wave_sum(loss_d);
   bound = wave_sum(bound);
   dsq = wave_sum(dsq);
