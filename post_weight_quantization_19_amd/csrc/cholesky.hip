@@ -147,11 +147,17 @@ __device__ __forceinline__ void panel_factor_store(T* __restrict__ A, int n, int
                                                    T (*gbuf)[2][4][NB], int* fail_col,
                                                    T* __restrict__ dbuf, DevFlags* flags,
                                                    pwq_result* res) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: "wave >= owner" below is then a scalar branch
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = min(NB, n - k0);
   const int row1 = k0 + NB * b + lane;
   const bool has1 = b > 0 && row1 < n;
-  if (tid == 0) *fail_col = -1;
+  if (tid == 0) *fail_col = NB;
+  // first bad pivot this wave owns (columns are factored in order, so the
+  // smallest over the waves is the first bad one); kept in a register and
+  // published once after the loop, off the column chain
+  int my_fail = NB;
   __syncthreads();
   static_for_up<NB / 4>([&](auto G) {
     constexpr int g = decltype(G)::value;
@@ -162,7 +168,7 @@ __device__ __forceinline__ void panel_factor_store(T* __restrict__ A, int n, int
         constexpr int j = j0 + u, jl = jl0 + u;
         const T piv = readlane_t(d0[jl], j);
         const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
-        if (bad && lane == 0 && *fail_col < 0) *fail_col = j;
+        if (bad && my_fail == NB) my_fail = j;
         T d, inv;
         pivot_ops(piv, d, inv);
         d0[jl] = (lane == j) ? d : d0[jl] * inv;
@@ -199,9 +205,10 @@ __device__ __forceinline__ void panel_factor_store(T* __restrict__ A, int n, int
       }
     }
   });
+  if (lane == 0 && my_fail < NB) atomicMin(fail_col, my_fail);
   __syncthreads();
   const int fc = *fail_col;
-  if (fc >= 0 && fc < nb) {
+  if (fc < nb) {
     if (b == 0 && tid == 0) {
       flags->info = k0 + fc + 1;
       res->info = k0 + fc + 1;
@@ -237,6 +244,24 @@ __device__ __forceinline__ void panel_load(const T* __restrict__ A, int n, int k
   const bool has1 = b > 0 && row1 < n;
   const T* src0 = A + (int64_t)(k0 + min(lane, nb - 1)) * n + k0 + 16 * wave;
   const T* src1 = A + (int64_t)(has1 ? row1 : k0) * n + k0 + 16 * wave;
+  if constexpr (sizeof(T) == 4) {
+    // a whole fp32 panel with 16-byte aligned rows: 16-byte loads, masks after
+    if (nb == NB && n % 4 == 0 && ((uintptr_t)A & 15) == 0) {
+      float4 a[4], b4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *(const float4*)(src0 + 4 * i);
+        b4[i] = *(const float4*)(src1 + 4 * i);
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int col = 16 * wave + c;
+        d0[c] = col <= lane ? (&a[c >> 2].x)[c & 3] : 0.0f;
+        d1[c] = has1 ? (&b4[c >> 2].x)[c & 3] : 0.0f;
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
     const int col = 16 * wave + c;
@@ -576,6 +601,32 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
       }
 }
 
+// 64 rows r0 .. r0+63, columns kc .. kc+63 of fp32 A into LDS (row pitch
+// NB + 1), for 16-byte aligned rows: four 16-byte loads per thread from rows
+// clamped into the matrix, rows past n stored as zeros.
+template <typename T>
+__device__ __forceinline__ void rows_to_lds_vec(T* __restrict__ dst, const T* __restrict__ A,
+                                                int n, int r0, int kc, int tid) {
+  if constexpr (sizeof(T) == 4) {
+    constexpr int LD = NB + 1;
+    float4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i, r = e >> 4, c4 = (e & 15) * 4;
+      v[i] = *(const float4*)(A + (int64_t)min(r0 + r, n - 1) * n + kc + c4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i, r = e >> 4, c4 = (e & 15) * 4;
+      const bool ok = r0 + r < n;
+      dst[r * LD + c4 + 0] = ok ? v[i].x : 0.0f;
+      dst[r * LD + c4 + 1] = ok ? v[i].y : 0.0f;
+      dst[r * LD + c4 + 2] = ok ? v[i].z : 0.0f;
+      dst[r * LD + c4 + 3] = ok ? v[i].w : 0.0f;
+    }
+  }
+}
+
 // One step with look-ahead, given the finished panel at k0 (columns
 // k0..k0+63 of every row >= k0 hold L).  The trailing update is applied
 // lazily, several panels at a time: panels kfrom/64 .. k0/64 (npan of them)
@@ -628,17 +679,26 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void chol_step(T* __re
   Mfma64<T> u0, u1;
   u0.zero();
   u1.zero();
+  // fp32 rows of 16-byte multiples: the pending-panel rows come in with
+  // 16-byte loads from rows clamped into the matrix (rows past n are zeroed
+  // after the load)
+  const bool vec = sizeof(T) == 4 && n % 4 == 0 && ((uintptr_t)A & 15) == 0;
   for (int pc = 0; pc < npan; ++pc) {
     const int kc = kfrom + pc * NB;
     if (pc > 0) __syncthreads();   // the previous chunk's LDS reads are done
-    tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
-      return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + kc + k] : (T)0;
-    });
-    if (b > 0)
-      tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
-        const int row = p1 + NB * b + r;
-        return (row < n) ? A[(int64_t)row * n + kc + k] : (T)0;
+    if (vec) {
+      rows_to_lds_vec(Q, A, n, p1, kc, tid);
+      if (b > 0) rows_to_lds_vec(S, A, n, p1 + NB * b, kc, tid);
+    } else {
+      tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
+        return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + kc + k] : (T)0;
       });
+      if (b > 0)
+        tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
+          const int row = p1 + NB * b + r;
+          return (row < n) ? A[(int64_t)row * n + kc + k] : (T)0;
+        });
+    }
     __syncthreads();
     u0.add(Q, Q);
     if (b > 0) u1.add(S, Q);
