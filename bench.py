@@ -306,9 +306,9 @@ def main():
         inputs = f"H {n}x{n} fp32 = L0 diag(k^-1.2) L0^T"
         grid_txt = f"column spacing c/l_kk, c = {grid.c:.6g}"
 
-    # per-stage rooflines (SURVEY 8d style): SYRK and lazy update against
-    # their MFMA peaks, Cholesky n^3/3 against its MFMA peak (stage time),
-    # the sweep's ~14 bytes per weight against HBM
+    # per-stage rooflines: SYRK and lazy update against their MFMA peaks,
+    # Cholesky n^3/3 against its MFMA peak (stage time), the sweep's
+    # ~14 bytes per weight against HBM
     pk = peaks or {}
     mf_peak, mf_key = (PEAK_F32_TFLOPS, "mfma_f32_tflops") if prec == "f32" else \
         (PEAK_F64_TFLOPS, "mfma_f64_tflops")
