@@ -295,35 +295,51 @@ __device__ __forceinline__ int tm_swz(int r) { return PWQ_TM_SWZ * (r & 3); }
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Six MFMA operands (8 consecutive tokens t0 .. t0 + 7 of channel f0 +
-// lane % 16 each) from the LDS addresses p[0..5]: two transposed reads 4
-// token rows (2048 B) apart per operand.  The reads are issued together and
-// waited for (lgkmcnt(0)) inside the same asm block, so every output is
-// complete when the block ends.  (Written as asm because the compiler, not
-// seeing which LDS bytes the builtin reads, would otherwise wait for every
-// LDS copy still in flight before the first read.)
-__device__ __forceinline__ void tr_operands6(const uint32_t (&p)[6], bf16x8_t (&out)[6]) {
-  v4i16 lo[6], hi[6];
+// The twelve MFMA operands of one stage (two token steps of 16; each
+// operand is 8 consecutive tokens t0 .. t0 + 7 of channel f0 + lane % 16)
+// from the LDS addresses p[0..5] of the first step: two transposed reads 4
+// token rows (2048 B) apart per operand, the second step 16 rows (8192 B)
+// further.  All 24 reads are issued together and waited for (lgkmcnt(0))
+// inside the same asm block, so every output is complete when the block
+// ends.  (Written as asm because the compiler, not seeing which LDS bytes
+// the builtin reads, would otherwise wait for every LDS copy still in
+// flight before the first read.)
+__device__ __forceinline__ void tr_operands12(const uint32_t (&p)[6], bf16x8_t (&out)[12]) {
+  v4i16 lo[12], hi[12];
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %12\n\t"
-      "ds_read_b64_tr_b16 %1, %12 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %2, %13\n\t"
-      "ds_read_b64_tr_b16 %3, %13 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %4, %14\n\t"
-      "ds_read_b64_tr_b16 %5, %14 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %6, %15\n\t"
-      "ds_read_b64_tr_b16 %7, %15 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %8, %16\n\t"
-      "ds_read_b64_tr_b16 %9, %16 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %10, %17\n\t"
-      "ds_read_b64_tr_b16 %11, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %0, %24\n\t"
+      "ds_read_b64_tr_b16 %1, %24 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %25\n\t"
+      "ds_read_b64_tr_b16 %3, %25 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %26\n\t"
+      "ds_read_b64_tr_b16 %5, %26 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %27\n\t"
+      "ds_read_b64_tr_b16 %7, %27 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %28\n\t"
+      "ds_read_b64_tr_b16 %9, %28 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %29\n\t"
+      "ds_read_b64_tr_b16 %11, %29 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %12, %24 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %13, %24 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %14, %25 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %15, %25 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %16, %26 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %17, %26 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %18, %27 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %19, %27 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %20, %28 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %21, %28 offset:10240\n\t"
+      "ds_read_b64_tr_b16 %22, %29 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %23, %29 offset:10240\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
-        "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5])
+        "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
+        "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7]), "=&v"(lo[8]), "=&v"(hi[8]),
+        "=&v"(lo[9]), "=&v"(hi[9]), "=&v"(lo[10]), "=&v"(hi[10]), "=&v"(lo[11]), "=&v"(hi[11])
       : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5])
       : "memory");
 #pragma unroll
-  for (int t = 0; t < 6; ++t)
+  for (int t = 0; t < 12; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       out[t][e] = lo[t][e];
@@ -426,31 +442,35 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     if (skip) return;
     const uint4* A = Ls[slot][0];
     const uint4* B = Ls[slot][1];
-    const lds_char* S = (const lds_char*)&Ls[slot][0][0];
+    if constexpr (TM) {
+      // both token steps' operands in one block of transposed reads
+      static_assert(TI + 4 == 6, "six operands per token step");
+      const uint32_t sb = (uint32_t)(uintptr_t)(const lds_char*)&Ls[slot][0][0];
+      uint32_t p[6];
+      bf16x8_t o[12];
+#pragma unroll
+      for (int t = 0; t < 6; ++t) p[t] = sb + toff[t];
+      tr_operands12(p, o);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[6 * ks + i], o[6 * ks + TI + j],
+                                                                acc[i][j], 0, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = 2 * ks + (lane >> 5);
       bf16x8_t a[TI], b[4];
-      if constexpr (TM) {
-        static_assert(TI + 4 == 6, "six operands per token step");
-        const uint32_t sb = (uint32_t)(uintptr_t)S + ks * 16 * 512;
-        uint32_t p[6];
-        bf16x8_t o[6];
 #pragma unroll
-        for (int t = 0; t < 6; ++t) p[t] = sb + toff[t];
-        tr_operands6(p, o);
+      for (int t = 0; t < TI; ++t)
+        a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * WR + 32 * t + (lane & 31), c)]);
 #pragma unroll
-        for (int t = 0; t < TI; ++t) a[t] = o[t];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = o[TI + t];
-      } else {
-#pragma unroll
-        for (int t = 0; t < TI; ++t)
-          a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * WR + 32 * t + (lane & 31), c)]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
-      }
+      for (int t = 0; t < 4; ++t)
+        b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
