@@ -26,6 +26,9 @@ CASES = {
     "zsic_small": (synth.config(5).resized(m=48, n=512), "f64", 0.001),
     # n % 4 != 0: rows of L are not 16-byte aligned (generic update kernel)
     "tiny_unaligned": (synth.config(1).resized(m=40, n=130, ntok=1000), "f32", None),
+    # n % 4 == 0 but n % 64 != 0: 16-byte rows with a ragged last panel and
+    # block (clamped rows in the vector loads of the factor and the sweep)
+    "tiny_ragged_aligned": (synth.config(1).resized(m=72, n=200, ntok=2048), "f32", None),
 }
 
 
