@@ -12,3 +12,4 @@ from .babai_oracle import (babai_bound, babai_gram_schmidt, certificate,
                            gamma_ratio, gptq_obs_sweep, grid_steps, hessian,
                            nearest_plane_sweep, nearest_plane_sweep_blocked,
                            order_permutation, proxy_loss, quant_layer)
+from .babai_oracle import code_range, overflow_entries, ssqr_search

@@ -437,3 +437,87 @@ def test_perm_with_grouped_and_column_steps(grid_kind, group):
     for r in range(m):
         zg = O.babai_gram_schmidt(Ap, W[r, p], S_pos[r])
         np.testing.assert_array_equal(res["Z"][r, p], zg)
+
+
+# ---------------------------------------------------------------- SSQR (GEOM 3)
+
+def test_ssqr_step_scale_and_code_range():
+    rng = np.random.default_rng(41)
+    W = rng.standard_normal((6, 32)).astype(np.float32).astype(np.float64)
+    for kind, bits in (("sym", 4), ("asym", 3)):
+        s1, z1 = O.grid_steps(W, kind, bits, 16)
+        s2, z2 = O.grid_steps(W, kind, bits, 16, step_scale=0.5)
+        assert np.array_equal(s2, s1 * 0.5)          # a power of two scales exactly
+        if kind == "asym":
+            lo = np.minimum(W.reshape(6, 2, 16).min(axis=2), 0).astype(np.float32)
+            assert np.array_equal(z2, np.rint(-lo / (s1 * 0.5).astype(np.float32)).astype(np.int64))
+    assert O.code_range("sym", 4) == (-8, 7)
+    assert O.code_range("asym", 2) == (0, 3)
+
+
+def test_ssqr_overflow_split_reconstructs_the_dequantized_weights():
+    rng = np.random.default_rng(42)
+    m, n, G = 5, 24, 8
+    scales = rng.uniform(0.01, 0.1, (m, n // G)).astype(np.float32).astype(np.float64)
+    zeros = rng.integers(0, 16, (m, n // G))
+    codes = rng.integers(-20, 36, (m, n))
+    rows, cols, vals = O.overflow_entries(codes, scales, zeros, "asym", 4)
+    lo, hi = O.code_range("asym", 4)
+    inside = (codes >= lo) & (codes <= hi)
+    assert len(rows) == int(np.sum(~inside))
+    order = rows * n + cols
+    assert np.all(np.diff(order) > 0)                 # row-major, no repeats
+    assert not np.any(inside[rows, cols])
+    S = np.repeat(scales, G, axis=1).astype(np.float32)
+    Z = (codes - np.repeat(zeros, G, axis=1)).astype(np.float32)
+    full = S * Z
+    recon = np.where(inside, full, np.float32(0))
+    recon[rows, cols] = vals
+    assert np.array_equal(recon, full)
+
+
+def _rtn_count(W0, kind, bits, group, kappa):
+    """Outliers of plain round-to-nearest at steps s * kappa (no sweep)."""
+    s, z = O.grid_steps(W0, kind, bits, group, step_scale=kappa)
+    S = O.expand_group_steps(s, W0.shape[1])
+    codes = np.rint(W0 / S).astype(np.int64)
+    if z is not None:
+        codes = codes + O.expand_group_steps(z.astype(np.float64), W0.shape[1]).astype(np.int64)
+    lo, hi = O.code_range(kind, bits)
+    return int(np.sum((codes < lo) | (codes > hi)))
+
+
+def test_ssqr_search_on_a_diagonal_hessian_equals_brute_force():
+    """A diagonal H makes the sweep plain rounding, whose outlier count never
+    increases with kappa: the bisection must land on the smallest point of
+    its dyadic grid that meets the target."""
+    rng = np.random.default_rng(43)
+    m, n = 12, 64
+    W = (0.02 * rng.standard_t(3, (m, n))).astype(np.float32).astype(np.float64)
+    H = np.diag(rng.uniform(0.5, 2.0, n))
+    iters, lo = 6, -4.0
+    for kind, bits, group, density in (("sym", 3, 32, 0.05), ("asym", 2, 16, 0.10)):
+        def count_at(k):
+            r = O.quant_layer(W, H=H, grid_kind=kind, bits=bits, group=group, damp=0.0,
+                              step_scale=k)
+            rows, _, _ = O.overflow_entries(r["codes"], r["scales"], r["zeros"], kind, bits)
+            assert len(rows) == _rtn_count(W, kind, bits, group, k)
+            return len(rows)
+        kappa, evals = O.ssqr_search(count_at, m, n, density, iters=iters, log2_lo=lo)
+        target = int(np.floor(density * m * n))
+        grid = [lo + (0.0 - lo) * k / 2 ** iters for k in range(2 ** iters + 1)]
+        best = min(x for x in grid
+                   if _rtn_count(W, kind, bits, group, float(np.float32(2.0 ** x))) <= target)
+        assert kappa == float(np.float32(2.0 ** best))
+        assert len(evals) == iters + 2
+
+
+def test_ssqr_search_edges():
+    calls = []
+
+    def always(c):
+        return lambda k: (calls.append(k), c)[1]
+    k, ev = O.ssqr_search(always(0), 4, 4, 0.0, iters=5, log2_lo=-3.0)
+    assert k == 0.125 and len(ev) == 2                # the lower end already meets it
+    k, ev = O.ssqr_search(always(100), 4, 4, 0.5, iters=5, log2_lo=-3.0)
+    assert k == 1.0 and len(ev) == 1                  # unreachable: kappa stays 1
