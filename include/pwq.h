@@ -83,7 +83,11 @@ typedef struct {
   int32_t bits;
   int32_t group_size;  /* 0 = one step per row; must divide n otherwise  */
   int32_t reserved;
-  double c;            /* COLSPACING constant                            */
+  double c;            /* COLSPACING: alpha_k = c / l_kk.  SYM / ASYM:   */
+                       /* a multiplier kappa on every step, applied after */
+                       /* the step rule (the asymmetric zero point uses   */
+                       /* the scaled step); 0 means none.  [GEOM 3: SSQR  */
+                       /* adjusts the scale]                              */
 } pwq_grid;
 
 /* Processing order.  Position k of the permuted problem holds original
@@ -248,6 +252,57 @@ size_t pwq_rate_workspace_size(int64_t n);
 pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
                               double* bits, double* mean, int64_t* huff, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- *
+ * Overflow-tolerant steps (SSQR) [GEOM 3: a few outlier weights are kept at
+ * full precision as sparse floating-point values, the rest quantized at
+ * low bit width; a binary search adjusts the scale to meet a target outlier
+ * density].  Reading: the sweep never clips [GEOM 2.3], so a stored code
+ * may fall outside the b-bit range (SYM: -2^(b-1) .. 2^(b-1)-1, ASYM:
+ * 0 .. 2^b-1); those entries are the outliers, listed as (row, column,
+ * value = float32(step * (code - zero point))) sorted by row, then column.
+ *
+ * pwq_overflow_entries: the list for given codes.
+ *   codes   : m x n int32, row stride ldc >= n; scales / zeros as written by
+ *             pwq_grid_steps or pwq_quant_layer for `grid` (SYM or ASYM).
+ *   rows, cols, vals : device arrays of max_out entries; the first
+ *             min(count, max_out) entries of the list are written.
+ *   count   : device int64: the number of outliers (may exceed max_out).
+ *   ws      : pwq_overflow_workspace_size(m) bytes.
+ *
+ * pwq_ssqr_quant_layer: the whole layer with the scale search.  H (from X
+ * once, or given) is quantized as by pwq_quant_layer (back-to-front) at
+ * step multiplier kappa (pwq_grid.c), and log2 kappa is bisected in
+ * [log2_lo, 0]: kappa = 1 is tried first (if its outlier count already
+ * exceeds floor(density m n) it is kept), then 2^log2_lo (kept if it meets
+ * the target), then `iters` halvings of the bracket; the result is the
+ * upper end of the final bracket (kappa = float32(2^x)).  On return codes,
+ * scales, zeros and result hold the quantization at that kappa and
+ * rows / cols / vals its outliers (as above).
+ *   density : target fraction of outliers, in [0, 1].
+ *   n_out   : host int64: the number of outliers at the chosen kappa.
+ *   kappa   : host double: the chosen multiplier.
+ *   ws      : pwq_ssqr_workspace_size(m, n, ntok, X != NULL, block, prec).
+ * Synchronous: the stream is synchronised after every quantization (the
+ * search needs each count on the host).  A failed factorization stops the
+ * search with kappa = 1, n_out = 0 and result->info set.
+ * ---------------------------------------------------------------------- */
+size_t pwq_overflow_workspace_size(int64_t m);
+pwq_status pwq_overflow_entries(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                                const pwq_grid* grid, const float* scales,
+                                const int32_t* zeros, int64_t max_out, int32_t* rows,
+                                int32_t* cols, float* vals, int64_t* count, void* ws,
+                                size_t ws_bytes, void* stream);
+size_t pwq_ssqr_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_t has_x,
+                               int32_t block, int32_t prec);
+pwq_status pwq_ssqr_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                                int64_t ldw, const void* X, int32_t xdtype, int64_t ntok,
+                                int64_t ldx, const float* H, const pwq_grid* grid, double damp,
+                                int32_t block, int32_t prec, double density, int32_t iters,
+                                double log2_lo, int32_t* codes, float* scales, int32_t* zeros,
+                                pwq_result* result, int64_t max_out, int32_t* rows,
+                                int32_t* cols, float* vals, int64_t* n_out, double* kappa,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- *
  * Kernel timing hook (measurement only; no effect on any result).

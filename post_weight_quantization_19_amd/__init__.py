@@ -20,7 +20,7 @@ from ._lib import PwqError, check, lib, make_grid, parse_result
 
 __all__ = ["Grid", "hessian_accum", "damp_cholesky", "grid_steps", "babai_sweep",
            "quant_layer", "column_entropy", "read_result", "PwqError", "KernelTimer",
-           "HessianTileTimer"]
+           "HessianTileTimer", "overflow_entries", "ssqr_quant_layer"]
 
 
 @dataclass(frozen=True)
@@ -278,3 +278,73 @@ class HessianTileTimer(KernelTimer):
 
     def __init__(self, capacity: int):
         super().__init__("hessian_tiles", capacity)
+
+
+def overflow_entries(codes: torch.Tensor, scales: torch.Tensor, grid: Grid,
+                     zeros: Optional[torch.Tensor] = None, max_out: Optional[int] = None):
+    """Overflow entries of int32 codes [m, n] for a SYM/ASYM grid (SSQR):
+    (rows, cols, vals, count) -- the first min(count, max_out) entries of the
+    (row, column)-sorted list, and the device int64 count."""
+    _require_cuda(codes, scales, zeros)
+    m, n = codes.shape
+    ldc = _row_major(codes) if m > 0 else n
+    cap = m * n if max_out is None else int(max_out)
+    dev = codes.device
+    rows = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    cols = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    vals = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    count = torch.zeros((), dtype=torch.int64, device=dev)
+    L_ = lib()
+    ws = _workspace(L_.pwq_overflow_workspace_size(m), dev)
+    g = grid.c_struct()
+    check(L_.pwq_overflow_entries(codes.data_ptr(), m, n, ldc, g, scales.data_ptr(),
+                                  _ptr(zeros), cap, rows.data_ptr(), cols.data_ptr(),
+                                  vals.data_ptr(), count.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream()))
+    return rows, cols, vals, count
+
+
+def ssqr_quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
+                     H: Optional[torch.Tensor] = None, grid: Grid = Grid(),
+                     damp: float = 0.01, block: int = 128, prec: str = "f32",
+                     density: float = 0.01, iters: int = 12, log2_lo: float = -8.0,
+                     max_outliers: Optional[int] = None, x_layout: str = "channels"):
+    """Overflow-tolerant quantization (SSQR): the step multiplier kappa is
+    bisected in log2 for at most ``density`` m n outlier codes.  Returns a
+    dict: codes, scales, zeros, result, kappa, n_outliers and the outlier
+    list rows / cols / vals (trimmed to min(n_outliers, max_outliers)).
+    Synchronous."""
+    _require_cuda(W, X, H)
+    m, n = W.shape
+    dev = W.device
+    ntok, ldx, xdt = 0, 0, 0
+    if X is not None:
+        nx, ntok, ldx, xdt = _x_args(X, x_layout)
+        if nx != n:
+            raise ValueError(f"X has {nx} channels, W has {n} columns")
+    G = grid.group or n
+    cap = m * n if max_outliers is None else int(max_outliers)
+    o = {"codes": torch.empty((m, n), dtype=torch.int32, device=dev),
+         "scales": torch.empty((m, n // G), dtype=torch.float32, device=dev),
+         "zeros": (torch.empty((m, n // G), dtype=torch.int32, device=dev)
+                   if grid.kind == "asym" else None),
+         "result": new_result(dev)}
+    rows = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    cols = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    vals = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    n_out = ctypes.c_int64(0)
+    kappa = ctypes.c_double(0.0)
+    L_ = lib()
+    ws = _workspace(L_.pwq_ssqr_workspace_size(m, n, ntok, int(X is not None), block,
+                                               _prec(prec)), dev)
+    g = grid.c_struct()
+    check(L_.pwq_ssqr_quant_layer(
+        W.data_ptr(), _dtype_code(W), m, n, _row_major(W), _ptr(X), xdt, ntok, ldx, _ptr(H),
+        g, float(damp), int(block), _prec(prec), float(density), int(iters), float(log2_lo),
+        o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o["zeros"]),
+        o["result"].data_ptr(), cap, rows.data_ptr(), cols.data_ptr(), vals.data_ptr(),
+        ctypes.byref(n_out), ctypes.byref(kappa), ws.data_ptr(), ws.numel(), _stream()))
+    k = min(int(n_out.value), cap)
+    o.update(kappa=float(kappa.value), n_outliers=int(n_out.value), rows=rows[:k],
+             cols=cols[:k], vals=vals[:k])
+    return o

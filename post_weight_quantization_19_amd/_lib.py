@@ -27,6 +27,8 @@ EXPORTS = [
     "pwq_quant_layer_workspace_size", "pwq_quant_layer",
     "pwq_rate_workspace_size", "pwq_column_entropy",
     "pwq_kernel_timer_attach", "pwq_kernel_timer_count",
+    "pwq_overflow_workspace_size", "pwq_overflow_entries",
+    "pwq_ssqr_workspace_size", "pwq_ssqr_quant_layer",
 ]
 PWQ_TIMER_HESSIAN_TILES, PWQ_TIMER_LAZY_UPDATE, PWQ_TIMER_SWEEP_BLOCK = 0, 1, 2
 TIMED_KERNELS = {"hessian_tiles": PWQ_TIMER_HESSIAN_TILES, "lazy_update": PWQ_TIMER_LAZY_UPDATE,
@@ -72,6 +74,15 @@ _SIGS = {
                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_rate_workspace_size": (_sz, [_i64]),
     "pwq_column_entropy": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_overflow_workspace_size": (_sz, [_i64]),
+    "pwq_overflow_entries": (_i32, [_vp, _i64, _i64, _i64, ctypes.POINTER(PwqGrid), _vp, _vp,
+                                    _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_ssqr_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+    "pwq_ssqr_quant_layer": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _i64, _i64, _vp,
+                                    ctypes.POINTER(PwqGrid), _f64, _i32, _i32, _f64, _i32, _f64,
+                                    _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                    ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_double), _vp, _sz, _vp]),
     "pwq_kernel_timer_attach": (_i32, [_i32, _vp, _vp, _i64]),
     "pwq_kernel_timer_count": (_i64, [_i32]),
 }

@@ -8,6 +8,8 @@
 
 #include "pwq_internal.h"
 
+#include <cmath>
+
 using namespace pwq;
 
 namespace pwq {
@@ -77,6 +79,8 @@ pwq_status check_grid(const pwq_grid* g, int64_t n, bool allow_colspacing) {
     if (g->group_size > 0 && n % g->group_size)
       return fail(PWQ_ERR_INVALID_ARG, "group_size %d does not divide n = %lld", g->group_size,
                   (long long)n);
+    if (!(g->c >= 0.0) || !(g->c < 1e30))
+      return fail(PWQ_ERR_INVALID_ARG, "the step multiplier c must be 0 (none) or finite > 0");
     return PWQ_OK;
   }
   if (g->kind == PWQ_GRID_COLSPACING) {
@@ -89,6 +93,9 @@ pwq_status check_grid(const pwq_grid* g, int64_t n, bool allow_colspacing) {
 }
 
 int group_of(const pwq_grid* g, int64_t n) { return g->group_size > 0 ? g->group_size : (int)n; }
+
+// SYM / ASYM: c is a multiplier on every step (0 means none).
+float step_multiplier(const pwq_grid* g) { return g->c > 0.0 ? (float)g->c : 1.0f; }
 
 // ---- workspace layouts (shared by sizing and carving)
 
@@ -256,7 +263,7 @@ pwq_status pwq_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, i
     return fail(PWQ_ERR_INVALID_ARG, "ASYM grid needs zeros");
   hipError_t e = launch_grid_steps(W, wdtype, m, n, ldw, dead, grid->kind, grid->bits,
                                    group_of(grid, n), scales, zeros, nullptr,
-                                   (hipStream_t)stream);
+                                   (hipStream_t)stream, step_multiplier(grid));
   if (e != hipSuccess) return hip_fail(e, "grid_steps launch");
   return ok();
 }
@@ -407,7 +414,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   const int G = colsp ? 1 : group_of(grid, n);
   if (e == hipSuccess && !colsp && m > 0)
     e = launch_grid_steps(W, wdtype, m, n, ldw, w.dead, grid->kind, grid->bits, G, scales,
-                          zeros, w.flags, st);
+                          zeros, w.flags, st, step_multiplier(grid));
   if (e == hipSuccess) {
     SweepLaunch sl{};
     sl.W = W; sl.wdtype = wdtype; sl.ldw = ldw; sl.m = m; sl.n = n; sl.prec = prec;
@@ -469,6 +476,169 @@ pwq_status pwq_kernel_timer_attach(int32_t kernel, void* const* starts, void* co
 
 int64_t pwq_kernel_timer_count(int32_t kernel) {
   return (kernel >= 0 && kernel < kNumTimers) ? g_timers[kernel].used : -1;
+}
+
+// ------------------------------------------------------------ SSQR outliers
+
+size_t pwq_overflow_workspace_size(int64_t m) {
+  if (m < 0) return 0;
+  Carver c(nullptr);
+  c.take((size_t)m * 4);
+  c.take((size_t)m * 8);
+  c.take(8);
+  return c.size();
+}
+
+pwq_status pwq_overflow_entries(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                                const pwq_grid* grid, const float* scales,
+                                const int32_t* zeros, int64_t max_out, int32_t* rows,
+                                int32_t* cols, float* vals, int64_t* count, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (m < 0 || n <= 0 || m > INT32_MAX || n > INT32_MAX)
+    return fail(PWQ_ERR_INVALID_ARG, "bad m / n");
+  if (m > 0 && (!codes || !scales)) return fail(PWQ_ERR_INVALID_ARG, "codes / scales NULL");
+  if (m > 0 && ldc < n) return fail(PWQ_ERR_INVALID_ARG, "ldc < n");
+  if (!count) return fail(PWQ_ERR_INVALID_ARG, "count is NULL");
+  if (max_out < 0) return fail(PWQ_ERR_INVALID_ARG, "max_out must be >= 0");
+  if (max_out > 0 && (!rows || !cols || !vals))
+    return fail(PWQ_ERR_INVALID_ARG, "rows / cols / vals NULL");
+  pwq_status s = check_grid(grid, n, false);
+  if (s != PWQ_OK) return s;
+  if (grid->kind == PWQ_GRID_ASYM && !zeros)
+    return fail(PWQ_ERR_INVALID_ARG, "ASYM grid needs zeros");
+  s = check_ws(ws, ws_bytes, pwq_overflow_workspace_size(m));
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  int32_t* rc = (int32_t*)c.take((size_t)m * 4);
+  int64_t* ro = (int64_t*)c.take((size_t)m * 8);
+  (void)c.take(8);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_overflow_count(codes, m, n, ldc, grid->kind, grid->bits, rc, ro, count, st);
+  if (e == hipSuccess)
+    e = launch_overflow_write(codes, m, n, ldc, grid->kind, grid->bits, scales,
+                              grid->kind == PWQ_GRID_ASYM ? zeros : nullptr, group_of(grid, n),
+                              ro, max_out, rows, cols, vals, st);
+  if (e != hipSuccess) return hip_fail(e, "overflow launch");
+  return ok();
+}
+
+size_t pwq_ssqr_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_t has_x, int32_t block,
+                               int32_t prec) {
+  if (m < 0 || n <= 0 || !valid_block(block)) return 0;
+  Carver c(nullptr);
+  if (has_x) c.take((size_t)n * n * 4);                               // H
+  size_t inner = pwq_quant_layer_workspace_size(m, n, 0, 0, PWQ_ORDER_BACK_TO_FRONT, block, prec);
+  if (has_x) {
+    const size_t h = pwq_hessian_workspace_size(n, ntok);
+    if (h > inner) inner = h;
+  }
+  c.take(inner);
+  c.take(pwq_overflow_workspace_size(m));
+  return c.size();
+}
+
+pwq_status pwq_ssqr_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                                int64_t ldw, const void* X, int32_t xdtype, int64_t ntok,
+                                int64_t ldx, const float* H, const pwq_grid* grid, double damp,
+                                int32_t block, int32_t prec, double density, int32_t iters,
+                                double log2_lo, int32_t* codes, float* scales, int32_t* zeros,
+                                pwq_result* result, int64_t max_out, int32_t* rows,
+                                int32_t* cols, float* vals, int64_t* n_out, double* kappa,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (!grid || (grid->kind != PWQ_GRID_SYM && grid->kind != PWQ_GRID_ASYM))
+    return fail(PWQ_ERR_INVALID_ARG, "SSQR needs a SYM or ASYM grid");
+  if (!(density >= 0.0) || !(density <= 1.0))
+    return fail(PWQ_ERR_INVALID_ARG, "density must be in [0, 1]");
+  if (iters < 0 || iters > 60) return fail(PWQ_ERR_INVALID_ARG, "iters must be in [0, 60]");
+  if (!(log2_lo < 0.0) || !(log2_lo >= -60.0))
+    return fail(PWQ_ERR_INVALID_ARG, "log2_lo must be in [-60, 0)");
+  if (!n_out || !kappa) return fail(PWQ_ERR_INVALID_ARG, "n_out / kappa NULL");
+  if (max_out < 0 || (max_out > 0 && (!rows || !cols || !vals)))
+    return fail(PWQ_ERR_INVALID_ARG, "bad outlier arrays");
+  const bool has_x = X != nullptr;
+  if (has_x == (H != nullptr)) return fail(PWQ_ERR_INVALID_ARG, "give exactly one of X and H");
+  if (m <= 0 || n <= 0) return fail(PWQ_ERR_INVALID_ARG, "m and n must be positive");
+  if (!valid_block(block)) return fail(PWQ_ERR_UNSUPPORTED, "block must be 32, 64, 128 or 256");
+  pwq_status s = check_ws(ws, ws_bytes, pwq_ssqr_workspace_size(m, n, ntok, has_x, block, prec));
+  if (s != PWQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  float* Hw = has_x ? (float*)c.take((size_t)n * n * 4) : nullptr;
+  size_t inner = pwq_quant_layer_workspace_size(m, n, 0, 0, PWQ_ORDER_BACK_TO_FRONT, block, prec);
+  if (has_x) {
+    const size_t h = pwq_hessian_workspace_size(n, ntok);
+    if (h > inner) inner = h;
+  }
+  void* qws = c.take(inner);
+  int32_t* rc = (int32_t*)c.take((size_t)m * 4);
+  int64_t* ro = (int64_t*)c.take((size_t)m * 8);
+  int64_t* tot = (int64_t*)c.take(8);
+  if (has_x) {
+    s = pwq_hessian_accum(Hw, n, X, xdtype, ntok, ldx, 0, qws, inner, stream);
+    if (s != PWQ_OK) return s;
+  }
+  const float* Hm = has_x ? Hw : H;
+  const int64_t target = (int64_t)std::floor(density * (double)m * (double)n);
+  // one whole quantization at step multiplier k; returns its outlier count,
+  // or -1 when the factorization failed (result->info)
+  double last = -1.0;
+  auto evaluate = [&](double k, int64_t* cnt) -> pwq_status {
+    pwq_grid g = *grid;
+    g.c = k;
+    pwq_status q = pwq_quant_layer(W, wdtype, m, n, ldw, nullptr, 0, 0, 0, Hm, &g,
+                                   PWQ_ORDER_BACK_TO_FRONT, nullptr, damp, block, prec, codes,
+                                   scales, zeros, result, nullptr, nullptr, qws, inner, stream);
+    if (q != PWQ_OK) return q;
+    hipError_t e = launch_overflow_count(codes, m, n, n, grid->kind, grid->bits, rc, ro, tot, st);
+    pwq_result r;
+    int64_t t = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&t, tot, 8, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(&r, result, sizeof(r), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "ssqr evaluation");
+    last = k;
+    *cnt = r.info != 0 ? -1 : t;
+    return PWQ_OK;
+  };
+  // the multiplier as float32 of 2^x (what the step kernel multiplies by)
+  auto kap = [](double x) { return (double)(float)std::exp2(x); };
+  int64_t cnt = 0;
+  double lo = log2_lo, hi = 0.0, res_k = 1.0;
+  s = evaluate(kap(hi), &cnt);
+  if (s != PWQ_OK) return s;
+  if (cnt < 0) {                    // the factorization failed: result->info says where
+    *n_out = 0;
+    *kappa = 1.0;
+    return ok();
+  }
+  if (cnt <= target) {
+    s = evaluate(kap(lo), &cnt);
+    if (s != PWQ_OK) return s;
+    if (cnt <= target) {
+      res_k = kap(lo);
+    } else {
+      for (int i = 0; i < iters; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        s = evaluate(kap(mid), &cnt);
+        if (s != PWQ_OK) return s;
+        if (cnt <= target) hi = mid;
+        else lo = mid;
+      }
+      res_k = kap(hi);
+    }
+  }
+  if (last != res_k) {              // leave the outputs at the chosen multiplier
+    s = evaluate(res_k, &cnt);
+    if (s != PWQ_OK) return s;
+  }
+  hipError_t e = launch_overflow_write(codes, m, n, n, grid->kind, grid->bits, scales,
+                                       grid->kind == PWQ_GRID_ASYM ? zeros : nullptr,
+                                       group_of(grid, n), ro, max_out, rows, cols, vals, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "ssqr outliers");
+  *n_out = cnt;
+  *kappa = res_k;
+  return ok();
 }
 
 }  // extern "C"

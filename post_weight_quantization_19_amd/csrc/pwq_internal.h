@@ -18,6 +18,16 @@ struct SyrkPlan {
   size_t partial_bytes;  // 0 when a single split writes H directly
 };
 
+// Overflow entries (SSQR): per-row counts, offsets and total; the sorted
+// (row, column, value) list.
+hipError_t launch_overflow_count(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                                 int kind, int bits, int32_t* row_count, int64_t* row_off,
+                                 int64_t* total, hipStream_t st);
+hipError_t launch_overflow_write(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,
+                                 int kind, int bits, const float* scales, const int32_t* zeros,
+                                 int G, const int64_t* row_off, int64_t max_out,
+                                 int32_t* rows, int32_t* cols, float* vals, hipStream_t st);
+
 // xdtype as at the boundary: element type in the low bits, kXTokenMajor
 // when X is stored ntok x n.
 constexpr int32_t kXTypeMask = 0xff;
@@ -36,7 +46,8 @@ hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t 
 
 hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
                              const int32_t* dead, int kind, int bits, int G, float* scales,
-                             int32_t* zeros, const DevFlags* flags, hipStream_t st);
+                             int32_t* zeros, const DevFlags* flags, hipStream_t st,
+                             float kappa = 1.0f);
 
 struct SweepLaunch {
   const void* W;

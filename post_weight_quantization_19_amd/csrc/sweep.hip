@@ -41,7 +41,7 @@ namespace {
 // One 16-lane quarter of a wave per (row, group): 16 groups per workgroup.
 __global__ __launch_bounds__(256) void grid_steps_kernel(
     const void* __restrict__ W, int32_t wdtype, int m, int n, int64_t ldw,
-    const int32_t* __restrict__ dead, int kind, int bits, int G,
+    const int32_t* __restrict__ dead, int kind, int bits, int G, float kappa,
     float* __restrict__ scales, int32_t* __restrict__ zeros,
     const DevFlags* flags) {
   if (flags && flags->info != 0) return;
@@ -67,14 +67,18 @@ __global__ __launch_bounds__(256) void grid_steps_kernel(
     amax = fmaxf(amax, __shfl_xor(amax, o, 16));
   }
   if (!live || sub != 0) return;
+  // kappa: one multiplier on every step (1 by default), applied after the
+  // zero-step rule; the asymmetric zero point follows the scaled step
   if (kind == PWQ_GRID_SYM) {
     float s = amax / (float)((1 << (bits - 1)) - 1);
     if (s == 0.0f) s = 1.0f;
+    s *= kappa;
     scales[(int64_t)r * ng + g] = s;
   } else {
     const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
     float s = (hi - lo) / (float)((1 << bits) - 1);
     if (s == 0.0f) s = 1.0f;
+    s *= kappa;
     scales[(int64_t)r * ng + g] = s;
     zeros[(int64_t)r * ng + g] = (int32_t)rintf(-lo / s);
   }
@@ -803,10 +807,10 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
 
 hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
                              const int32_t* dead, int kind, int bits, int G, float* scales,
-                             int32_t* zeros, const DevFlags* flags, hipStream_t st) {
+                             int32_t* zeros, const DevFlags* flags, hipStream_t st, float kappa) {
   const int64_t groups = m * (n / G);
   grid_steps_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, st>>>(
-      W, wdtype, (int)m, (int)n, ldw, dead, kind, bits, G, scales, zeros, flags);
+      W, wdtype, (int)m, (int)n, ldw, dead, kind, bits, G, kappa, scales, zeros, flags);
   return hipGetLastError();
 }
 

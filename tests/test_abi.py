@@ -25,7 +25,7 @@ def header_functions():
 def test_exports_match_header():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 19
     assert sorted(B.EXPORTS) == names
     for nm in names:
         assert getattr(L, nm) is not None
@@ -169,3 +169,46 @@ def test_rate_validation():
     assert L.pwq_column_entropy(None, 4, 8, 8, FAKE, None, None, None, 0, None) == INVALID
     assert L.pwq_column_entropy(FAKE, 4, 8, 8, None, None, None, None, 0, None) == INVALID
     assert L.pwq_column_entropy(FAKE, 4, 8, 8, FAKE, None, None, None, 0, None) == WS
+
+
+def test_ssqr_validation():
+    L = B.lib()
+    g = _grid(0, 4, 0)
+    n_out = ctypes.c_int64(0)
+    kap = ctypes.c_double(0.0)
+    # overflow list
+    assert L.pwq_overflow_entries(FAKE, 4, 8, 4, g, FAKE, None, 0, None, None, None, FAKE,
+                                  FAKE, 4096, None) == INVALID          # ldc < n
+    assert L.pwq_overflow_entries(FAKE, 4, 8, 8, g, FAKE, None, 4, None, None, None, FAKE,
+                                  FAKE, 4096, None) == INVALID          # no output arrays
+    assert L.pwq_overflow_entries(FAKE, 4, 8, 8, _grid(1, 4, 0), FAKE, None, 0, None, None,
+                                  None, FAKE, FAKE, 4096, None) == INVALID   # ASYM, no zeros
+    assert L.pwq_overflow_entries(FAKE, 4, 8, 8, g, FAKE, None, 0, None, None, None, FAKE,
+                                  None, 0, None) == WS
+    assert L.pwq_overflow_workspace_size(4) > 0
+
+    def call(**kw):
+        a = dict(X=FAKE, H=None, grid=g, density=0.01, iters=8, lo=-6.0, block=32,
+                 nout=ctypes.byref(n_out), kap=ctypes.byref(kap), ws=None, wsb=0)
+        a.update(kw)
+        return L.pwq_ssqr_quant_layer(FAKE, 1, 64, 128, 128, a["X"], 1, 256, 256, a["H"],
+                                      a["grid"], 0.01, a["block"], 0, a["density"], a["iters"],
+                                      a["lo"], FAKE, FAKE, None, FAKE, 0, None, None, None,
+                                      a["nout"], a["kap"], a["ws"], a["wsb"], None)
+    assert call(grid=_grid(2, 0, 0)) == INVALID       # COLSPACING has no b-bit range
+    assert call(density=1.5) == INVALID
+    assert call(iters=-1) == INVALID
+    assert call(lo=0.0) == INVALID
+    assert call(H=FAKE) == INVALID                    # both X and H
+    assert call(nout=None) == INVALID
+    assert call(block=100) == UNSUP
+    assert call() == WS
+    assert L.pwq_ssqr_workspace_size(64, 128, 256, 1, 32, 0) > \
+        L.pwq_ssqr_workspace_size(64, 128, 0, 0, 32, 0)
+
+
+def test_grid_step_multiplier_validation():
+    L = B.lib()
+    g = _grid(0, 4, 0)
+    g.c = -1.0
+    assert L.pwq_grid_steps(FAKE, 1, 4, 8, 8, None, g, FAKE, None, None) == INVALID
