@@ -51,6 +51,10 @@ def parse():
                     help="storage of the activations: token-major [ntok, n] (one row per "
                          "token, as a layer's inputs are captured; the default) or [n, ntok]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ssqr", type=float, default=None, metavar="DENSITY",
+                    help="time the overflow-tolerant layer (SSQR: scale search for this "
+                         "outlier density) instead of the plain one")
+    ap.add_argument("--ssqr-iters", type=int, default=12)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the achievable-peak probe (MFMA and copy microbenchmarks)")
     ap.add_argument("--cpu-token-fraction", type=int, default=8,
@@ -183,8 +187,79 @@ def stage_roofline(achieved, peak, achievable, unit, bound, work, how):
             "work_per_step": work, "timed_by": how}
 
 
+def ssqr_bench(args):
+    """The overflow-tolerant layer (SSQR): one call = the Hessian once, then
+    iters + 2 (or 3) quantizations of the bisection of the step multiplier,
+    and the outlier list.  Prints one JSON line of its own."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_19_amd as P
+    import synth
+
+    cfg = synth.config(args.config)
+    if cfg.grid_kind not in ("sym", "asym"):
+        raise SystemExit("SSQR needs a layer with a SYM or ASYM grid (--config 2, 3 or 4)")
+    m, n, N = cfg.m, cfg.n, cfg.ntok
+    print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
+          flush=True)
+    lay = synth.make_layer(cfg, keep_x_f32=False)
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xl = args.x_layout
+    if xl == "tokens":
+        X = X.t().contiguous()
+    grid = P.Grid(cfg.grid_kind, cfg.bits, cfg.group)
+
+    def call():
+        return P.ssqr_quant_layer(W, X=X, grid=grid, damp=cfg.damp, block=cfg.block,
+                                  density=args.ssqr, iters=args.ssqr_iters, x_layout=xl)
+    out = call()                                   # warm-up (synchronous)
+    reps = max(1, args.steps // 5)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        out = call()
+    dt = (time.perf_counter() - t0) / reps
+    # the outlier list alone (two passes over the codes: 8 bytes per weight)
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    P.overflow_entries(out["codes"], out["scales"], grid, out["zeros"])
+    a.record(stream)
+    for _ in range(5):
+        P.overflow_entries(out["codes"], out["scales"], grid, out["zeros"])
+    b.record(stream)
+    torch.cuda.synchronize()
+    t_list = a.elapsed_time(b) / 5 / 1e3
+    gbs = 8.0 * m * n / t_list / 1e9
+    nq = args.ssqr_iters + 2
+    line = {
+        "metric": "SSQR layer time (scale search) & weights quantized/s",
+        "value": m * n / dt, "unit": "weights/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 products, f32 accumulate/factor/sweep",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{cfg.name} (SSQR, outlier density {args.ssqr}, "
+                               f"{args.ssqr_iters} halvings of log2 kappa in [-8, 0])",
+                   "m": m, "n": n, "ntok": N, "x_layout": xl},
+        "ssqr": {"kappa": out["kappa"], "n_outliers": out["n_outliers"],
+                 "density": out["n_outliers"] / (m * n),
+                 "quantizations_per_call": f"{nq} or {nq + 1}",
+                 "ms_per_quantization": dt * 1e3 / nq},
+        "roofline": {"bound": "hbm", "kernel": "overflow_rows + overflow_scan + "
+                     "overflow_write (the outlier list)", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "avg_launch_ms": t_list * 1e3, "bytes_per_launch": 8.0 * m * n},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.ssqr is not None and args.gpus == 1:
+        ssqr_bench(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the "
               "quantizer's rows are independent, and a multi-GPU run would shard them "

@@ -270,9 +270,10 @@ pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_
  *   count   : device int64: the number of outliers (may exceed max_out).
  *   ws      : pwq_overflow_workspace_size(m) bytes.
  *
- * pwq_ssqr_quant_layer: the whole layer with the scale search.  H (from X
- * once, or given) is quantized as by pwq_quant_layer (back-to-front) at
- * step multiplier kappa (pwq_grid.c), and log2 kappa is bisected in
+ * pwq_ssqr_quant_layer: the whole layer with the scale search.  H (from X,
+ * or given), the damping and the factor are computed once; the layer is
+ * then quantized as by pwq_quant_layer (back-to-front) at step multiplier
+ * kappa (pwq_grid.c: steps, then the sweep), and log2 kappa is bisected in
  * [log2_lo, 0]: kappa = 1 is tried first (if its outlier count already
  * exceeds floor(density m n) it is kept), then 2^log2_lo (kept if it meets
  * the target), then `iters` halvings of the bracket; the result is the

@@ -8,6 +8,7 @@
 
 #include "pwq_internal.h"
 
+#include <algorithm>
 #include <cmath>
 
 using namespace pwq;
@@ -527,11 +528,11 @@ size_t pwq_ssqr_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_t has_x
   if (m < 0 || n <= 0 || !valid_block(block)) return 0;
   Carver c(nullptr);
   if (has_x) c.take((size_t)n * n * 4);                               // H
-  size_t inner = pwq_quant_layer_workspace_size(m, n, 0, 0, PWQ_ORDER_BACK_TO_FRONT, block, prec);
-  if (has_x) {
-    const size_t h = pwq_hessian_workspace_size(n, ntok);
-    if (h > inner) inner = h;
-  }
+  c.take((size_t)n * n * elem(prec));                                 // L
+  c.take((size_t)n * 4);                                              // dead flags
+  size_t inner = pwq_sweep_workspace_size(m, n, block, prec);
+  inner = std::max(inner, pwq_cholesky_workspace_size(n, prec));
+  if (has_x) inner = std::max(inner, pwq_hessian_workspace_size(n, ntok));
   c.take(inner);
   c.take(pwq_overflow_workspace_size(m));
   return c.size();
@@ -564,40 +565,49 @@ pwq_status pwq_ssqr_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_
   hipStream_t st = (hipStream_t)stream;
   Carver c(ws);
   float* Hw = has_x ? (float*)c.take((size_t)n * n * 4) : nullptr;
-  size_t inner = pwq_quant_layer_workspace_size(m, n, 0, 0, PWQ_ORDER_BACK_TO_FRONT, block, prec);
-  if (has_x) {
-    const size_t h = pwq_hessian_workspace_size(n, ntok);
-    if (h > inner) inner = h;
-  }
-  void* qws = c.take(inner);
+  void* L = c.take((size_t)n * n * elem(prec));
+  int32_t* dead = (int32_t*)c.take((size_t)n * 4);
+  size_t inner = pwq_sweep_workspace_size(m, n, block, prec);
+  inner = std::max(inner, pwq_cholesky_workspace_size(n, prec));
+  if (has_x) inner = std::max(inner, pwq_hessian_workspace_size(n, ntok));
+  void* iws = c.take(inner);
   int32_t* rc = (int32_t*)c.take((size_t)m * 4);
   int64_t* ro = (int64_t*)c.take((size_t)m * 8);
   int64_t* tot = (int64_t*)c.take(8);
+  // The Hessian and its factor do not depend on the steps: once.
   if (has_x) {
-    s = pwq_hessian_accum(Hw, n, X, xdtype, ntok, ldx, 0, qws, inner, stream);
+    s = pwq_hessian_accum(Hw, n, X, xdtype, ntok, ldx, 0, iws, inner, stream);
     if (s != PWQ_OK) return s;
   }
-  const float* Hm = has_x ? Hw : H;
+  s = pwq_damp_cholesky(has_x ? Hw : H, n, damp, prec, L, dead, result, iws, inner, stream);
+  if (s != PWQ_OK) return s;
+  pwq_result r0;
+  hipError_t e = hipMemcpyAsync(&r0, result, sizeof(r0), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "ssqr factor");
+  if (r0.info != 0) {               // the factorization failed: result->info says where
+    *n_out = 0;
+    *kappa = 1.0;
+    return ok();
+  }
   const int64_t target = (int64_t)std::floor(density * (double)m * (double)n);
-  // one whole quantization at step multiplier k; returns its outlier count,
-  // or -1 when the factorization failed (result->info)
+  // steps at multiplier k, the sweep, and its outlier count (on the host)
   double last = -1.0;
   auto evaluate = [&](double k, int64_t* cnt) -> pwq_status {
     pwq_grid g = *grid;
     g.c = k;
-    pwq_status q = pwq_quant_layer(W, wdtype, m, n, ldw, nullptr, 0, 0, 0, Hm, &g,
-                                   PWQ_ORDER_BACK_TO_FRONT, nullptr, damp, block, prec, codes,
-                                   scales, zeros, result, nullptr, nullptr, qws, inner, stream);
+    pwq_status q = pwq_grid_steps(W, wdtype, m, n, ldw, dead, &g, scales, zeros, stream);
     if (q != PWQ_OK) return q;
-    hipError_t e = launch_overflow_count(codes, m, n, n, grid->kind, grid->bits, rc, ro, tot, st);
-    pwq_result r;
+    q = pwq_babai_sweep(W, wdtype, m, n, ldw, L, prec, dead, &g, scales, zeros, block, codes,
+                        result, iws, inner, stream);
+    if (q != PWQ_OK) return q;
+    hipError_t he = launch_overflow_count(codes, m, n, n, grid->kind, grid->bits, rc, ro, tot, st);
     int64_t t = 0;
-    if (e == hipSuccess) e = hipMemcpyAsync(&t, tot, 8, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipMemcpyAsync(&r, result, sizeof(r), hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "ssqr evaluation");
+    if (he == hipSuccess) he = hipMemcpyAsync(&t, tot, 8, hipMemcpyDeviceToHost, st);
+    if (he == hipSuccess) he = hipStreamSynchronize(st);
+    if (he != hipSuccess) return hip_fail(he, "ssqr evaluation");
     last = k;
-    *cnt = r.info != 0 ? -1 : t;
+    *cnt = t;
     return PWQ_OK;
   };
   // the multiplier as float32 of 2^x (what the step kernel multiplies by)
@@ -606,11 +616,6 @@ pwq_status pwq_ssqr_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_
   double lo = log2_lo, hi = 0.0, res_k = 1.0;
   s = evaluate(kap(hi), &cnt);
   if (s != PWQ_OK) return s;
-  if (cnt < 0) {                    // the factorization failed: result->info says where
-    *n_out = 0;
-    *kappa = 1.0;
-    return ok();
-  }
   if (cnt <= target) {
     s = evaluate(kap(lo), &cnt);
     if (s != PWQ_OK) return s;
@@ -631,9 +636,9 @@ pwq_status pwq_ssqr_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_
     s = evaluate(res_k, &cnt);
     if (s != PWQ_OK) return s;
   }
-  hipError_t e = launch_overflow_write(codes, m, n, n, grid->kind, grid->bits, scales,
-                                       grid->kind == PWQ_GRID_ASYM ? zeros : nullptr,
-                                       group_of(grid, n), ro, max_out, rows, cols, vals, st);
+  e = launch_overflow_write(codes, m, n, n, grid->kind, grid->bits, scales,
+                            grid->kind == PWQ_GRID_ASYM ? zeros : nullptr, group_of(grid, n),
+                            ro, max_out, rows, cols, vals, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "ssqr outliers");
   *n_out = cnt;
