@@ -11,5 +11,6 @@ from .babai_oracle import (babai_bound, babai_gram_schmidt, certificate,
                            expand_group_steps, fix_dead_and_damp,
                            gamma_ratio, gptq_obs_sweep, grid_steps, hessian,
                            nearest_plane_sweep, nearest_plane_sweep_blocked,
-                           order_permutation, proxy_loss, quant_layer)
+                           min_pivot_order, order_permutation, proxy_loss,
+                           quant_layer)
 from .babai_oracle import code_range, overflow_entries, ssqr_search

@@ -341,6 +341,96 @@ def test_act_order_processes_largest_diagonal_first():
     assert list(p[::-1]) == [1, 3, 2, 0]
 
 
+def test_min_pivot_on_a_diagonal_matrix_sorts_ascending():
+    """[GEOM 2.3] min-pivot order on a diagonal H: the Schur complement never
+    changes, so the pivots are the diagonal in increasing order (ties by the
+    lower index) and the largest entry is processed first."""
+    H = np.diag([3.0, 1.0, 2.0, 1.0, 5.0])
+    pi, piv, info = O.min_pivot_order(H)
+    assert info == 0
+    assert list(pi) == [1, 3, 2, 0, 4]
+    np.testing.assert_array_equal(piv, [1.0, 1.0, 2.0, 3.0, 5.0])
+    np.testing.assert_array_equal(O.order_permutation("min_pivot", 5, H), pi)
+
+
+def test_min_pivot_matches_greedy_determinant_ratios():
+    """Brute force: the Schur-complement diagonal of candidate i after the
+    chosen set S is det H[S+i] / det H[S] (a ratio of principal minors), so
+    the greedy order and its pivots follow from determinants alone."""
+    rng = np.random.default_rng(31)
+    for n in (2, 3, 5, 7):
+        _, X = _rand_problem(rng, 1, n, 3 * n, spread=0.8)
+        H = O.hessian(X)
+        chosen, ratios = [], []
+        for _ in range(n):
+            base = np.linalg.det(H[np.ix_(chosen, chosen)]) if chosen else 1.0
+            cand = [(np.linalg.det(H[np.ix_(chosen + [i], chosen + [i])]) / base, i)
+                    for i in range(n) if i not in chosen]
+            r, q = min(cand)
+            chosen.append(q)
+            ratios.append(r)
+        pi, piv, info = O.min_pivot_order(H)
+        assert info == 0
+        assert list(pi) == chosen, n
+        np.testing.assert_allclose(piv, ratios, rtol=1e-9)
+
+
+def test_min_pivot_pivots_are_the_permuted_factor():
+    """The pivots are D of the LDL^T of the permuted Hessian, i.e. the squared
+    diagonal of its Cholesky factor (numpy's), and each is the smallest
+    Schur diagonal among the columns still open at its step."""
+    rng = np.random.default_rng(32)
+    _, X = _rand_problem(rng, 1, 40, 160, spread=0.7, outl=3)
+    H = O.hessian(X)
+    pi, piv, info = O.min_pivot_order(H)
+    assert info == 0 and sorted(pi) == list(range(40))
+    Lp = np.linalg.cholesky(H[np.ix_(pi, pi)])
+    np.testing.assert_allclose(piv, np.diag(Lp) ** 2, rtol=1e-10)
+    # Schur diagonal of position i at step k = Hp_ii - sum_{p<k} L_ip^2
+    Hp = H[np.ix_(pi, pi)]
+    sq = np.cumsum(Lp ** 2, axis=1)
+    for k in range(40):
+        schur = np.diag(Hp)[k:] - (sq[k:, k - 1] if k else 0.0)
+        assert piv[k] <= schur.min() * (1 + 1e-12)
+
+
+def test_min_pivot_2x2_takes_the_smaller_trace():
+    """2 x 2 closed form: the trace of D is a + c - b^2 / (first pivot), so
+    the smaller diagonal entry must go first."""
+    a, b, c = 5.0, 1.5, 2.0
+    H = np.array([[a, b], [b, c]])
+    pi, piv, info = O.min_pivot_order(H)
+    assert list(pi) == [1, 0]
+    assert piv.sum() == pytest.approx(a + c - b * b / c, rel=1e-15)
+    assert piv.sum() < a + c - b * b / a
+
+
+def test_min_pivot_reports_the_failing_step():
+    """A pivot that is not positive stops the factorization: info = step + 1;
+    a NaN diagonal is taken first."""
+    pi, piv, info = O.min_pivot_order(np.diag([2.0, -1.0, 3.0]))
+    assert info == 1 and list(pi) == [1, 0, 2]
+    assert piv[0] == -1.0 and np.all(np.isnan(piv[1:]))
+    pi, piv, info = O.min_pivot_order(np.ones((2, 2)))
+    assert info == 2 and list(pi) == [0, 1] and piv[0] == 1.0
+    pi, _, info = O.min_pivot_order(np.diag([1.0, np.nan, 2.0]))
+    assert info == 1 and pi[0] == 1
+    # the layer's factor fails at the same leading minor
+    W = np.ones((2, 3))
+    out = O.quant_layer(W, H=np.diag([2.0, -1.0, 3.0]), order="min_pivot", damp=0.0)
+    assert out["info"] == 1
+
+
+def test_min_pivot_layer_is_the_layer_in_that_order():
+    rng = np.random.default_rng(33)
+    W, X = _rand_problem(rng, 8, 24, 96, outl=2)
+    a = O.quant_layer(W, X=X, grid_kind="asym", bits=3, group=8, order="min_pivot")
+    pi, _, _ = O.min_pivot_order(a["Hd"])
+    b = O.quant_layer(W, X=X, grid_kind="asym", bits=3, group=8, order="perm", perm=pi)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(a["pi"], pi)
+
+
 def test_dead_feature_is_erased():
     """[WSIC 2]: a zero-variance input is erased: its code is 0 and the other
     columns are quantized as if it were absent (damp 0 keeps lambda equal)."""
