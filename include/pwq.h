@@ -96,12 +96,15 @@ typedef struct {
  *   FRONT_TO_BACK : perm = reversal (standard GPTQ order)
  *   PERM          : caller's device int32 permutation of 0..n-1
  *   ACT_ORDER     : largest diag(H) processed first, ties by lower index
- *                   [GEOM 2.3] */
+ *                   [GEOM 2.3]
+ *   MIN_PIVOT     : the min-pivot order of the damped Hessian (see
+ *                   pwq_min_pivot_order) [GEOM 2.3] */
 typedef enum {
   PWQ_ORDER_BACK_TO_FRONT = 0,
   PWQ_ORDER_FRONT_TO_BACK = 1,
   PWQ_ORDER_PERM = 2,
-  PWQ_ORDER_ACT = 3
+  PWQ_ORDER_ACT = 3,
+  PWQ_ORDER_MIN_PIVOT = 4
 } pwq_order_kind;
 
 /* Device-resident result record (read after a stream synchronisation).
@@ -213,6 +216,8 @@ pwq_status pwq_babai_sweep(const void* W, int32_t wdtype, int64_t m, int64_t n,
  *   H_out      : optional n x n float32 copy of H = 2 X X^T (X given only).
  *   L_out      : optional n x n factor (precision prec) of the PERMUTED
  *                damped Hessian.
+ *   The workspace depends on order_kind: MIN_PIVOT adds the n x n fp64
+ *   matrix of pwq_min_pivot_order.
  * ---------------------------------------------------------------------- */
 size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok,
                                       int32_t has_x, int32_t order_kind,
@@ -225,6 +230,31 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
                            int32_t prec, int32_t* codes, float* scales,
                            int32_t* zeros, pwq_result* result, float* H_out,
                            void* L_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- *
+ * Min-pivot order [GEOM 2.3: the Theorem 5 bound is (1/4) s^T D s with D
+ * the LDL pivots of the permuted Hessian; taking the smallest diagonal
+ * entry at each LDL step lowers trace D].  A diagonally pivoted LDL^T of
+ * H_d = H' + lambda I, H' = H with erased inputs (H_ii = 0) set to 1,
+ * lambda = damp * mean(diag H') (the damped matrix of pwq_quant_layer):
+ * step k takes the column not yet chosen whose Schur-complement diagonal
+ * is smallest (ties: lower column index; NaN counts as smallest) and puts
+ * it at position k, so position 0 is processed LAST by the back-to-front
+ * sweep.  Computed in float64.
+ *   H      : n x n float32 device, lower triangle read.
+ *   perm   : n int32 device out: perm[k] = column of position k.
+ *   pivots : optional n float64 device out: D_kk (NULL to skip).
+ *   result : device; info = 0, or k + 1 when pivot k is not positive (then
+ *            perm and pivots are undefined from position k on); lambda and
+ *            ndead written; the other fields untouched.
+ *   ws     : pwq_min_pivot_workspace_size(n) bytes (n x n float64 inside).
+ * One launch per pivot: the time grows with n launches.
+ * ---------------------------------------------------------------------- */
+size_t pwq_min_pivot_workspace_size(int64_t n);
+pwq_status pwq_min_pivot_order(const float* H, int64_t n, double damp,
+                               int32_t* perm, double* pivots,
+                               pwq_result* result, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* ---------------------------------------------------------------------- *
  * Rate: the empirical Shannon entropy of each column's codes, in bits

@@ -127,6 +127,24 @@ def damp_cholesky(H: torch.Tensor, damp: float = 0.01, prec: str = "f32"):
     return Lt, dead, res
 
 
+def min_pivot_order(H: torch.Tensor, damp: float = 0.01, want_pivots: bool = False):
+    """Min-pivot order of H_d = H' + lambda I: (perm, pivots or None, result).
+    perm[k] (int32) is the column at position k (position 0 is processed
+    last); pivots (float64) are the LDL pivots D_kk of the permuted matrix."""
+    _require_cuda(H)
+    n = H.shape[0]
+    if H.dim() != 2 or H.shape[1] != n or H.dtype != torch.float32 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [n, n] tensor")
+    L_ = lib()
+    perm = torch.empty(n, dtype=torch.int32, device=H.device)
+    piv = torch.empty(n, dtype=torch.float64, device=H.device) if want_pivots else None
+    res = new_result(H.device)
+    ws = _workspace(L_.pwq_min_pivot_workspace_size(n), H.device)
+    check(L_.pwq_min_pivot_order(H.data_ptr(), n, float(damp), perm.data_ptr(), _ptr(piv),
+                                 res.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return perm, piv, res
+
+
 def grid_steps(W: torch.Tensor, grid: Grid, dead: Optional[torch.Tensor] = None):
     """(scales [m, n/G], zeros [m, n/G] or None) for SYM / ASYM grids."""
     _require_cuda(W, dead)

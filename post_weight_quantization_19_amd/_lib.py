@@ -15,7 +15,7 @@ PWQ_OK, PWQ_ERR_INVALID_ARG, PWQ_ERR_UNSUPPORTED, PWQ_ERR_WORKSPACE, PWQ_ERR_HIP
 PWQ_F32, PWQ_BF16, PWQ_F64 = 0, 1, 2
 PWQ_X_TOKEN_MAJOR = 0x100     # X stored ntok x n (one row per token)
 GRID_KINDS = {"sym": 0, "asym": 1, "colspacing": 2}
-ORDERS = {"back_to_front": 0, "front_to_back": 1, "perm": 2, "act_order": 3}
+ORDERS = {"back_to_front": 0, "front_to_back": 1, "perm": 2, "act_order": 3, "min_pivot": 4}
 
 # every symbol include/pwq.h declares
 EXPORTS = [
@@ -29,6 +29,7 @@ EXPORTS = [
     "pwq_kernel_timer_attach", "pwq_kernel_timer_count",
     "pwq_overflow_workspace_size", "pwq_overflow_entries",
     "pwq_ssqr_workspace_size", "pwq_ssqr_quant_layer",
+    "pwq_min_pivot_workspace_size", "pwq_min_pivot_order",
 ]
 PWQ_TIMER_HESSIAN_TILES, PWQ_TIMER_LAZY_UPDATE, PWQ_TIMER_SWEEP_BLOCK = 0, 1, 2
 TIMED_KERNELS = {"hessian_tiles": PWQ_TIMER_HESSIAN_TILES, "lazy_update": PWQ_TIMER_LAZY_UPDATE,
@@ -77,6 +78,8 @@ _SIGS = {
     "pwq_overflow_workspace_size": (_sz, [_i64]),
     "pwq_overflow_entries": (_i32, [_vp, _i64, _i64, _i64, ctypes.POINTER(PwqGrid), _vp, _vp,
                                     _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_min_pivot_workspace_size": (_sz, [_i64]),
+    "pwq_min_pivot_order": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_ssqr_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
     "pwq_ssqr_quant_layer": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _i64, _i64, _vp,
                                     ctypes.POINTER(PwqGrid), _f64, _i32, _i32, _f64, _i32, _f64,

@@ -748,6 +748,12 @@ hipError_t factor_impl(T* A, int n, T* dbuf, DevFlags* flags, pwq_result* res,
 
 }  // namespace
 
+hipError_t launch_damp_lambda(const float* H, int64_t n, double damp, int32_t* dead,
+                              pwq_result* res, DevFlags* flags, double* lam, hipStream_t st) {
+  damp_prep<<<1, 256, 0, st>>>(H, (int)n, damp, dead, res, flags, lam);
+  return hipGetLastError();
+}
+
 hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                                 const int32_t* perm, void* L, int32_t* dead,
                                 pwq_result* res, DevFlags* flags, double* lam, void* dscratch,

@@ -115,6 +115,17 @@ void carve_sweep(Carver& c, int64_t m, int64_t n, int32_t block, int32_t prec, S
   w->partials = (double*)c.take(sweep_partials_bytes(m, n, block, prec));
 }
 
+void carve_min_pivot(Carver& c, int64_t n, MinPivotWs* w) {
+  const int64_t g = (n + 255) / 256;
+  w->A = (double*)c.take((size_t)n * n * sizeof(double));
+  w->P = (double*)c.take((size_t)n * kMinPivotPanel * sizeof(double));
+  w->d = (double*)c.take((size_t)n * sizeof(double));
+  w->pos = (int32_t*)c.take((size_t)n * 4);
+  w->rem = (int32_t*)c.take((size_t)n * 4);
+  w->part_v = (double*)c.take((size_t)2 * g * sizeof(double));
+  w->part_i = (int32_t*)c.take((size_t)2 * g * 4);
+}
+
 struct LayerWs {
   DevFlags* flags;
   double* lam;
@@ -126,11 +137,12 @@ struct LayerWs {
   void* L;
   void* dscratch;
   SweepWs sw;
+  MinPivotWs mp;
 };
 
 void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool need_h,
                  bool need_l, int32_t xdtype, bool x_aligned, int32_t block, int32_t prec,
-                 LayerWs* w) {
+                 bool min_pivot, LayerWs* w) {
   w->flags = (DevFlags*)c.take(sizeof(DevFlags));
   w->lam = (double*)c.take(sizeof(double));
   w->perm = (int32_t*)c.take((size_t)n * 4);
@@ -146,6 +158,8 @@ void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool
   w->L = need_l ? c.take((size_t)n * n * elem(prec)) : nullptr;
   w->dscratch = c.take(kCholScratchBytes);
   carve_sweep(c, m, n, block, prec, &w->sw);
+  w->mp = MinPivotWs{};
+  if (min_pivot) carve_min_pivot(c, n, &w->mp);
 }
 
 }  // namespace
@@ -342,8 +356,8 @@ pwq_status pwq_babai_sweep(const void* W, int32_t wdtype, int64_t m, int64_t n, 
 
 size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_t has_x,
                                       int32_t order_kind, int32_t block, int32_t prec) {
-  (void)order_kind;
   if (m < 0 || n <= 0 || !valid_block(block)) return 0;
+  const bool mp = order_kind == PWQ_ORDER_MIN_PIVOT;
   // size for the worst case: H and L kept in the workspace, any X dtype and
   // alignment
   size_t need = 0;
@@ -352,7 +366,7 @@ size_t pwq_quant_layer_workspace_size(int64_t m, int64_t n, int64_t ntok, int32_
       Carver c(nullptr);
       LayerWs w;
       carve_layer(c, m, n, ntok, has_x != 0, has_x != 0, true, dt == 0 ? PWQ_BF16 : PWQ_F32,
-                  al != 0, block, prec, &w);
+                  al != 0, block, prec, mp, &w);
       if (c.size() > need) need = c.size();
     }
   return need;
@@ -377,7 +391,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   } else if (H_out) {
     return fail(PWQ_ERR_INVALID_ARG, "H_out is only produced when X is given");
   }
-  if (order_kind < PWQ_ORDER_BACK_TO_FRONT || order_kind > PWQ_ORDER_ACT)
+  if (order_kind < PWQ_ORDER_BACK_TO_FRONT || order_kind > PWQ_ORDER_MIN_PIVOT)
     return fail(PWQ_ERR_INVALID_ARG, "unknown order %d", order_kind);
   if (order_kind == PWQ_ORDER_PERM && !perm)
     return fail(PWQ_ERR_INVALID_ARG, "PERM order needs perm");
@@ -388,11 +402,12 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   const bool xal = has_x && syrk_aligned(X, n, ldx, xdtype);
   Carver measure(nullptr);
   LayerWs w;
-  carve_layer(measure, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, &w);
+  const bool mp = order_kind == PWQ_ORDER_MIN_PIVOT;
+  carve_layer(measure, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, mp, &w);
   s = check_ws(ws, ws_bytes, measure.size());
   if (s != PWQ_OK) return s;
   Carver c(ws);
-  carve_layer(c, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, &w);
+  carve_layer(c, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, mp, &w);
   hipStream_t st = (hipStream_t)stream;
   float* Hm = has_x ? (H_out ? H_out : w.H) : (float*)H;
   void* Lm = L_out ? L_out : w.L;
@@ -404,7 +419,13 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
     e = launch_hessian(Hm, n, X, xdtype, ntok, ldx, 0, p, w.partial, st);
   }
   const int32_t* colmap = nullptr;
-  if (e == hipSuccess && order_kind != PWQ_ORDER_BACK_TO_FRONT) {
+  if (e == hipSuccess && mp) {
+    // the order is taken on the damped matrix: lambda first
+    e = launch_damp_lambda(Hm, n, damp, w.dead, result, w.flags, w.lam, st);
+    if (e == hipSuccess)
+      e = launch_min_pivot(Hm, n, w.lam, w.mp, w.perm, nullptr, w.flags, result, st);
+    colmap = w.perm;
+  } else if (e == hipSuccess && order_kind != PWQ_ORDER_BACK_TO_FRONT) {
     e = launch_order(order_kind, Hm, n, perm, w.perm, w.seen, result, w.flags, st);
     colmap = order_kind == PWQ_ORDER_PERM ? perm : w.perm;
   }
@@ -429,6 +450,38 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
     e = launch_sweep(sl, st);
   }
   if (e != hipSuccess) return hip_fail(e, "quant_layer launch");
+  return ok();
+}
+
+size_t pwq_min_pivot_workspace_size(int64_t n) {
+  if (n <= 0) return 0;
+  Carver c(nullptr);
+  c.take(sizeof(DevFlags));
+  c.take(sizeof(double));
+  MinPivotWs w;
+  carve_min_pivot(c, n, &w);
+  return c.size();
+}
+
+pwq_status pwq_min_pivot_order(const float* H, int64_t n, double damp, int32_t* perm,
+                               double* pivots, pwq_result* result, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (n <= 0 || n > INT32_MAX) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 2^31)");
+  if (!H || !perm || !result)
+    return fail(PWQ_ERR_INVALID_ARG, "H, perm and result must be non-NULL");
+  if (!(damp >= 0.0) || !(damp < 1e30)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
+  pwq_status s = check_ws(ws, ws_bytes, pwq_min_pivot_workspace_size(n));
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  DevFlags* flags = (DevFlags*)c.take(sizeof(DevFlags));
+  double* lam = (double*)c.take(sizeof(double));
+  MinPivotWs w;
+  carve_min_pivot(c, n, &w);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_init_flags(flags, result, 1, st);
+  if (e == hipSuccess) e = launch_damp_lambda(H, n, damp, nullptr, result, flags, lam, st);
+  if (e == hipSuccess) e = launch_min_pivot(H, n, lam, w, perm, pivots, flags, result, st);
+  if (e != hipSuccess) return hip_fail(e, "min_pivot_order launch");
   return ok();
 }
 

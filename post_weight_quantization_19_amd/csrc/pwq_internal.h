@@ -44,6 +44,11 @@ hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t 
                                 const int32_t* perm, void* L, int32_t* dead, pwq_result* res,
                                 DevFlags* flags, double* lam, void* dscratch, hipStream_t st);
 
+// Dead inputs and lambda = damp * mean(diag H after the dead fix), as the
+// first stage of launch_damp_cholesky (writes res->lambda, res->ndead).
+hipError_t launch_damp_lambda(const float* H, int64_t n, double damp, int32_t* dead,
+                              pwq_result* res, DevFlags* flags, double* lam, hipStream_t st);
+
 hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
                              const int32_t* dead, int kind, int bits, int G, float* scales,
                              int32_t* zeros, const DevFlags* flags, hipStream_t st,
@@ -81,6 +86,26 @@ hipError_t launch_order(int32_t order_kind, const float* H, int64_t n, const int
                         int32_t* perm_out, int32_t* seen, pwq_result* res, DevFlags* flags,
                         hipStream_t st);
 hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, hipStream_t st);
+
+// Min-pivot order (pivoted LDL^T in fp64).  Workspace: A n x n doubles,
+// P n x kMinPivotPanel doubles, d n doubles, pos and rem n int32 each, and
+// 2 ceil(n / 256) (double, int32) partial minima.
+constexpr int kMinPivotPanel = 32;
+struct MinPivotWs {
+  double* A;
+  double* P;
+  double* d;
+  int32_t* pos;
+  int32_t* rem;
+  double* part_v;
+  int32_t* part_i;
+};
+// perm[k] = column of position k; piv[k] = D_kk (may be NULL).  lam: the
+// damping (device double, from launch_damp_lambda).  A pivot that is not
+// positive sets flags->info = res->info = k + 1 and ends the work.
+hipError_t launch_min_pivot(const float* H, int64_t n, const double* lam, const MinPivotWs& w,
+                            int32_t* perm, double* piv, DevFlags* flags, pwq_result* res,
+                            hipStream_t st);
 
 // cmin / cmax: n int32 each of workspace.
 hipError_t launch_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_t ldc,

@@ -25,7 +25,7 @@ def header_functions():
 def test_exports_match_header():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     assert sorted(B.EXPORTS) == names
     for nm in names:
         assert getattr(L, nm) is not None
@@ -142,6 +142,23 @@ def test_workspace_sizes_grow_with_the_problem():
     assert 0 < a < b < c
     assert L.pwq_sweep_workspace_size(64, 128, 100, 0) == 0
     assert L.pwq_quant_layer_workspace_size(64, 0, 0, 0, 0, 128, 0) == 0
+
+
+def test_min_pivot_validation():
+    L = B.lib()
+    assert L.pwq_min_pivot_order(FAKE, 0, 0.01, FAKE, None, FAKE, FAKE, 4096, None) == INVALID
+    assert L.pwq_min_pivot_order(None, 8, 0.01, FAKE, None, FAKE, FAKE, 4096, None) == INVALID
+    assert L.pwq_min_pivot_order(FAKE, 8, 0.01, None, None, FAKE, FAKE, 4096, None) == INVALID
+    assert L.pwq_min_pivot_order(FAKE, 8, -1.0, FAKE, None, FAKE, FAKE, 4096, None) == INVALID
+    need = L.pwq_min_pivot_workspace_size(300)
+    assert need >= 300 * 300 * 8
+    assert L.pwq_min_pivot_order(FAKE, 300, 0.01, FAKE, None, FAKE, FAKE, need - 256,
+                                 None) == WS
+    assert L.pwq_min_pivot_workspace_size(0) == 0
+    # the layer's workspace grows by the fp64 matrix for this order only
+    a = L.pwq_quant_layer_workspace_size(64, 300, 0, 0, 3, 32, 0)
+    b = L.pwq_quant_layer_workspace_size(64, 300, 0, 0, 4, 32, 0)
+    assert b >= a + 300 * 300 * 8
 
 
 def test_kernel_timer_validation():
