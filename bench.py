@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--x-layout", choices=["channels", "tokens"], default="tokens",
                     help="storage of the activations: token-major [ntok, n] (one row per "
                          "token, as a layer's inputs are captured; the default) or [n, ntok]")
+    ap.add_argument("--order", default="back_to_front",
+                    choices=["back_to_front", "front_to_back", "act_order", "min_pivot"],
+                    help="processing order of the timed layer (the natural back-to-front "
+                         "order by default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ssqr", type=float, default=None, metavar="DENSITY",
                     help="time the overflow-tolerant layer (SSQR: scale search for this "
@@ -294,9 +298,10 @@ def main():
     else:
         grid = P.Grid(cfg.grid_kind, cfg.bits, cfg.group)
     prec = "f32" if has_x else "f64"     # the spectral layer is factored and swept in fp64
-    ws = P.workspace_for_layer(m, n, N, has_x, "back_to_front", cfg.block, prec, dev)
+    order = args.order
+    ws = P.workspace_for_layer(m, n, N, has_x, order, cfg.block, prec, dev)
     out = P.quant_layer(W, X=X, H=Hin, grid=grid, damp=cfg.damp, block=cfg.block, prec=prec,
-                        workspace=ws, x_layout=xl)
+                        workspace=ws, x_layout=xl, order=order)
     torch.cuda.synchronize()
     res0 = P.read_result(out["result"])
     if res0["info"] != 0:
@@ -304,7 +309,7 @@ def main():
 
     def step():
         P.quant_layer(W, X=X, H=Hin, grid=grid, damp=cfg.damp, block=cfg.block, prec=prec,
-                      workspace=ws, out=out, x_layout=xl)
+                      workspace=ws, out=out, x_layout=xl, order=order)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -371,6 +376,9 @@ def main():
     s, z = (None, None) if cfg.grid_kind == "colspacing" else P.grid_steps(W, grid)
     t_chol = timed(lambda: P.damp_cholesky(H, damp=cfg.damp, prec=prec))
     t_sweep = timed(lambda: P.babai_sweep(W, Lf, grid, scales=s, zeros=z, block=cfg.block))
+    t_order = None
+    if order == "min_pivot":
+        t_order = timed(lambda: P.min_pivot_order(H, damp=cfg.damp), r=2)
     if has_x:
         stored = "stored token-major [ntok, n]" if xl == "tokens" else "stored [n, ntok]"
         inputs = (f"X {n}x{N} bf16 {stored} " + ("Student-t(4)" if cfg.x_kind == "student_t" else
@@ -425,13 +433,15 @@ def main():
                   "f64 factor and sweep"),
         "data": "synthetic (seeded)",
         "config": {"workload": f"{cfg.name}: W {m}x{n} bf16, {inputs}; {grid_txt}, "
-                               f"block {cfg.block}, damp {cfg.damp}",
+                               f"block {cfg.block}, damp {cfg.damp}"
+                               + ("" if order == "back_to_front" else f", order {order}"),
                    "m": m, "n": n, "ntok": N, "x_layout": xl if has_x else None,
                    "layer_quantize_time_s": dt},
         "roofline": roofline,
         "stages_ms": {"hessian_accum": t_hess, "damp_cholesky": t_chol,
                       "sweep_and_update": t_sweep, "lazy_updates_in_step": upd_ms,
-                      "block_sweeps_in_step": swp_ms},
+                      "block_sweeps_in_step": swp_ms,
+                      **({"min_pivot_order": t_order} if t_order is not None else {})},
         "stage_rooflines": stages,
         "achievable_peaks": peaks,
         "loss": res0["loss"], "bound": res0["bound"],
