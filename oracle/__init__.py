@@ -14,3 +14,5 @@ from .babai_oracle import (babai_bound, babai_gram_schmidt, certificate,
                            min_pivot_order, order_permutation, proxy_loss,
                            quant_layer)
 from .babai_oracle import code_range, overflow_entries, ssqr_search
+from .babai_oracle import (oaem_blocks, oaem_estep, oaem_init, oaem_mstep,
+                           oaem_objective)

@@ -611,3 +611,114 @@ def test_ssqr_search_edges():
     assert k == 0.125 and len(ev) == 2                # the lower end already meets it
     k, ev = O.ssqr_search(always(100), 4, 4, 0.5, iters=5, log2_lo=-3.0)
     assert k == 1.0 and len(ev) == 1                  # unreachable: kappa stays 1
+
+
+# ---------------------------------------------------------------- OA-EM
+
+
+def _blobs(rng, K, per, g, spread=0.05):
+    means = rng.standard_normal((K, g)) * 3.0
+    pts = np.concatenate([mu + spread * rng.standard_normal((per, g)) for mu in means])
+    return pts[rng.permutation(len(pts))], means
+
+
+def _as_layer(pts, g, ng):
+    """Group vectors (in index order r * ng + i) as an m x (ng g) matrix."""
+    m = len(pts) // ng
+    return pts[:m * ng].reshape(m, ng * g)
+
+
+def _kmeans(X, C0, iters):
+    from sklearn.cluster import KMeans
+    km = KMeans(n_clusters=len(C0), init=C0, n_init=1, max_iter=iters, algorithm="lloyd",
+                tol=0.0).fit(X)
+    return km.cluster_centers_, km.labels_
+
+
+def test_oaem_identity_metric_is_lloyd_kmeans():
+    """[OAEM 3] with every H_i = I the Mahalanobis E-step is the nearest
+    centroid and the M-step the mean: Lloyd's k-means (scikit-learn's, from
+    the same initial centroids, on blobs where no cluster empties)."""
+    rng = np.random.default_rng(41)
+    g, ng, K = 4, 6, 5
+    pts, means = _blobs(rng, K, 24, g)
+    W = _as_layer(pts, g, ng)
+    m = W.shape[0]
+    vec = W.reshape(m * ng, g)
+    # one seed per blob: the group vector nearest to each blob centre
+    seeds = np.array([[int(np.argmin(np.linalg.norm(vec - mu, axis=1))) for mu in means]])
+    books, codes, objs, R = O.oaem_init(W, np.eye(ng * g), g, seeds, iters=6)
+    C_ref, lab_ref = _kmeans(vec, vec[seeds[0]], 6)
+    np.testing.assert_allclose(books[0], C_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_array_equal(codes[0].reshape(-1), lab_ref)
+
+
+def test_oaem_common_metric_is_kmeans_in_whitened_coordinates():
+    """With one metric H_0 = L L^T for every group, distances are Euclidean
+    in y = L^T w, so OA-EM is k-means on the whitened vectors."""
+    rng = np.random.default_rng(42)
+    g, ng, K = 3, 5, 4
+    pts, means = _blobs(rng, K, 20, g, spread=0.3)
+    W = _as_layer(pts, g, ng)
+    m = W.shape[0]
+    B = rng.standard_normal((g, g))
+    H0 = B @ B.T + 0.5 * np.eye(g)
+    Hd = np.kron(np.eye(ng), H0)
+    vec = W.reshape(m * ng, g)
+    seeds = np.array([[int(np.argmin(np.linalg.norm(vec - mu, axis=1))) for mu in means]])
+    books, codes, _, _ = O.oaem_init(W, Hd, g, seeds, iters=5)
+    L = np.linalg.cholesky(H0)
+    Y = vec @ L
+    Cy, lab = _kmeans(Y, Y[seeds[0]], 5)
+    np.testing.assert_array_equal(codes[0].reshape(-1), lab)
+    np.testing.assert_allclose(books[0] @ L, Cy, rtol=1e-9, atol=1e-12)
+
+
+def test_oaem_mstep_minimises_the_weighted_error():
+    """The M-step centroid of each cluster is the minimiser of
+    sum (w - c)^T H_i (w - c) over its groups (scipy's BFGS from zero)."""
+    from scipy.optimize import minimize
+    rng = np.random.default_rng(43)
+    g, ng, m, K = 4, 7, 9, 3
+    X = rng.standard_normal((ng * g, 200)) * rng.lognormal(0, 0.7, (ng * g, 1))
+    Hb = O.oaem_blocks(O.hessian(X), g)
+    R = rng.standard_normal((m, ng * g))
+    a = rng.integers(0, K, (m, ng))
+    a[0, 0] = 0
+    C0 = rng.standard_normal((K + 1, g))          # centroid K gets no group
+    C = O.oaem_mstep(R, Hb, a, C0)
+    np.testing.assert_array_equal(C[K], C0[K])
+    for k in range(K):
+        grp = [(r, i) for r in range(m) for i in range(ng) if a[r, i] == k]
+
+        def f(c):
+            return sum((R[r, i * g:(i + 1) * g] - c) @ Hb[i] @ (R[r, i * g:(i + 1) * g] - c)
+                       for r, i in grp)
+        opt = minimize(f, np.zeros(g), method="BFGS", options={"gtol": 1e-10})
+        np.testing.assert_allclose(C[k], opt.x, rtol=1e-5, atol=1e-6)
+        assert f(C[k]) <= opt.fun * (1 + 1e-12)
+
+
+def test_oaem_objective_falls_with_rounds_and_stages_reconstruct():
+    """E and M steps each minimise the same objective, so more rounds never
+    raise it; the residual is W minus every stage's chosen centroids."""
+    rng = np.random.default_rng(44)
+    g, ng, m, K = 4, 8, 12, 6
+    X = rng.standard_normal((ng * g, 300)) * rng.lognormal(0, 0.5, (ng * g, 1))
+    Hd, _, _, _ = O.fix_dead_and_damp(O.hessian(X), np.zeros((1, ng * g)), 0.01)
+    W = rng.standard_normal((m, ng * g)) * 0.02
+    seeds = np.stack([rng.choice(m * ng, K, replace=False) for _ in range(2)])
+    prev = np.inf
+    for it in range(5):
+        _, _, objs, _ = O.oaem_init(W, Hd, g, seeds[:1], iters=it)
+        assert objs[0] <= prev * (1 + 1e-12)
+        prev = objs[0]
+    books, codes, objs, R = O.oaem_init(W, Hd, g, seeds, iters=3)
+    rec = np.zeros_like(W)
+    for t in range(2):
+        for i in range(ng):
+            rec[:, i * g:(i + 1) * g] += books[t][codes[t][:, i]]
+    np.testing.assert_allclose(W - rec, R, atol=1e-14)
+    Hb = O.oaem_blocks(Hd, g)
+    assert objs[1] == pytest.approx(O.oaem_objective(R, Hb), rel=1e-12)
+    assert objs[1] < objs[0]
