@@ -257,6 +257,44 @@ pwq_status pwq_min_pivot_order(const float* H, int64_t n, double damp,
                                void* stream);
 
 /* ---------------------------------------------------------------------- *
+ * OA-EM codebook initialisation [OAEM 3: inside AQLM's residual framework
+ * each codebook is initialised by EM; the M-step moves the centroids to
+ * minimise the output reconstruction error weighted by
+ * H_i = X_i^T X_i + lambda I, the E-step reassigns every weight group to
+ * its nearest centroid in that Mahalanobis distance].
+ *   A weight group is g consecutive inputs of one output row,
+ *   w_{r,i} = W[r, i g .. i g + g), i < n / g; its metric H_i is the g x g
+ *   diagonal block of the damped Hessian H_d = H' + lambda I (erased inputs
+ *   and lambda as in pwq_quant_layer).  Stage t < M fits K centroids to the
+ *   residual left by stages 0..t-1: initial centroid k is the residual group
+ *   seeds[t K + k] (index r (n/g) + i, chosen by the caller); `iters` rounds
+ *   of E-step (argmin_k (w - c_k)^T H_i (w - c_k), ties to the lower k) and
+ *   M-step (c_k = (sum H_i)^{-1} sum H_i w over the groups assigned to k; a
+ *   centroid with no group keeps its value), then a final E-step gives the
+ *   stage's codes and the residual loses the chosen centroids.  float64.
+ *   W          : m x n float32 or bfloat16 (row stride ldw >= n), device.
+ *   H          : n x n float32 device, lower triangle read (undamped).
+ *   g, K       : 1 <= g <= 16 dividing n; K >= 1 with K (g + 1) <= 8192.
+ *   seeds      : M x K int64 device; an index outside [0, m n / g) sets
+ *                result->info = -1 (group 0 is used).
+ *   codebooks  : M x K x g float64 device out.
+ *   codes      : M x m x (n/g) int32 device out (codes[t][r][i]).
+ *   objective  : optional M float64 device out: sum over groups of
+ *                e^T H_i e for the residual e after each stage (NULL: skip).
+ *   result     : device; info = 0 or -1, lambda and ndead written.
+ *   ws         : pwq_oaem_workspace_size(m, n, g, K) bytes (0 for an
+ *                unsupported shape).
+ * ---------------------------------------------------------------------- */
+size_t pwq_oaem_workspace_size(int64_t m, int64_t n, int32_t g, int32_t K);
+pwq_status pwq_oaem_init(const void* W, int32_t wdtype, int64_t m, int64_t n,
+                         int64_t ldw, const float* H, double damp, int32_t g,
+                         int32_t K, int32_t M, int32_t iters,
+                         const int64_t* seeds, double* codebooks,
+                         int32_t* codes, double* objective,
+                         pwq_result* result, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ---------------------------------------------------------------------- *
  * Rate: the empirical Shannon entropy of each column's codes, in bits
  * [WSIC 2, items 1 and 3: columns get unequal rates and the unclipped codes
  * are entropy coded, so a column's rate is the entropy of its codes], and

@@ -145,6 +145,35 @@ def min_pivot_order(H: torch.Tensor, damp: float = 0.01, want_pivots: bool = Fal
     return perm, piv, res
 
 
+def oaem_init(W: torch.Tensor, H: torch.Tensor, seeds: torch.Tensor, g: int = 8,
+              iters: int = 10, damp: float = 0.01, want_objective: bool = True):
+    """OA-EM codebook initialisation.  seeds: int64 [M, K] group indices
+    r (n/g) + i.  Returns (codebooks float64 [M, K, g], codes int32
+    [M, m, n/g], objective float64 [M] or None, result)."""
+    _require_cuda(W, H, seeds)
+    m, n = W.shape
+    if H.shape != (n, n) or H.dtype != torch.float32 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [n, n] tensor")
+    if seeds.dim() != 2 or seeds.dtype != torch.int64 or not seeds.is_contiguous():
+        raise ValueError("seeds must be a contiguous int64 [M, K] tensor")
+    M, K = seeds.shape
+    if g <= 0 or n % g:
+        raise ValueError("g must divide n")
+    dev = W.device
+    L_ = lib()
+    books = torch.empty((M, K, g), dtype=torch.float64, device=dev)
+    codes = torch.empty((M, m, n // g), dtype=torch.int32, device=dev)
+    obj = torch.empty(M, dtype=torch.float64, device=dev) if want_objective else None
+    res = new_result(dev)
+    nb = L_.pwq_oaem_workspace_size(m, n, g, K)
+    ws = _workspace(nb, dev) if nb else None
+    check(L_.pwq_oaem_init(W.data_ptr(), _dtype_code(W), m, n, _row_major(W), H.data_ptr(),
+                           float(damp), int(g), int(K), int(M), int(iters), seeds.data_ptr(),
+                           books.data_ptr(), codes.data_ptr(), _ptr(obj), res.data_ptr(),
+                           _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return books, codes, obj, res
+
+
 def grid_steps(W: torch.Tensor, grid: Grid, dead: Optional[torch.Tensor] = None):
     """(scales [m, n/G], zeros [m, n/G] or None) for SYM / ASYM grids."""
     _require_cuda(W, dead)

@@ -30,6 +30,7 @@ EXPORTS = [
     "pwq_overflow_workspace_size", "pwq_overflow_entries",
     "pwq_ssqr_workspace_size", "pwq_ssqr_quant_layer",
     "pwq_min_pivot_workspace_size", "pwq_min_pivot_order",
+    "pwq_oaem_workspace_size", "pwq_oaem_init",
 ]
 PWQ_TIMER_HESSIAN_TILES, PWQ_TIMER_LAZY_UPDATE, PWQ_TIMER_SWEEP_BLOCK = 0, 1, 2
 TIMED_KERNELS = {"hessian_tiles": PWQ_TIMER_HESSIAN_TILES, "lazy_update": PWQ_TIMER_LAZY_UPDATE,
@@ -78,6 +79,9 @@ _SIGS = {
     "pwq_overflow_workspace_size": (_sz, [_i64]),
     "pwq_overflow_entries": (_i32, [_vp, _i64, _i64, _i64, ctypes.POINTER(PwqGrid), _vp, _vp,
                                     _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_oaem_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
+    "pwq_oaem_init": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, ctypes.c_double, _i32, _i32,
+                             _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_min_pivot_workspace_size": (_sz, [_i64]),
     "pwq_min_pivot_order": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pwq_ssqr_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),

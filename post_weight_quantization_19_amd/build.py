@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpwq.so")
 PROBE = os.path.join(HERE, "peak_probe")
 SOURCES = ["pwq_api.hip", "hessian.hip", "cholesky.hip", "sweep.hip", "order.hip", "rate.hip",
-           "ssqr.hip", "min_pivot.hip"]
+           "ssqr.hip", "min_pivot.hip", "oaem.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,342 @@
+// OA-EM: output-aware EM initialisation of additive codebooks.
+//
+// "Initialisation Determines the Basin: Efficient Codebook Optimisation for
+// Extreme LLM Quantization", section 3: inside AQLM's residual framework,
+// each codebook is initialised by EM.  The M-step moves each centroid to
+// minimise the output reconstruction error of its weight groups, weighted
+// by H_i = X_i^T X_i + lambda I; the E-step reassigns every group to the
+// nearest centroid in that Mahalanobis distance.
+//
+// Reading: a group is g consecutive inputs of one output row; H_i is the
+// g x g diagonal block of the damped Hessian (dead inputs and lambda as for
+// the layer); a stage's centroids start at the residual groups the caller
+// names; a stage runs `iters` E/M rounds and a final E-step, then the
+// residual loses the chosen centroids.  Ties go to the lower centroid; a
+// centroid without groups keeps its value.  Everything is float64.
+//
+// Kernels, per stage and round:
+//   oaem_qtable  Q[i][k] = c_k^T H_i c_k                     (ng x K)
+//   oaem_estep   one thread per row of a group column: h = H_i w, then
+//                argmin_k Q[i][k] - 2 h . c_k with the codebook in LDS
+//                (the same argmin as the distance, which differs from it
+//                by w^T H_i w)
+//   oaem_msums   per (group column, centroid): the sum of the assigned
+//                residual groups and their count, rows in increasing order
+//                (chunks of assignments and rows staged in LDS)
+//   oaem_msolve  one workgroup per centroid: A = sum_i cnt_ik H_i,
+//                b = sum_i H_i S_ik in a fixed order, then A c = b by
+//                Cholesky (g <= 16)
+//   oaem_apply / oaem_objective after the final E-step.
+#include "pwq_device.h"
+#include "pwq_internal.h"
+
+namespace pwq {
+
+namespace {
+
+constexpr int kMaxG = kOaemMaxG;
+
+__global__ __launch_bounds__(256) void oaem_blocks(const float* __restrict__ H, int n, int g,
+                                                   const double* __restrict__ lam_p,
+                                                   double* __restrict__ Hb) {
+  const int i = blockIdx.x;
+  const int t = threadIdx.x;
+  if (t >= g * g) return;
+  const int u = t / g, v = t % g;
+  const int a = i * g + (u > v ? u : v), b = i * g + (u > v ? v : u);
+  const float h = H[(int64_t)a * n + b];
+  double x = (double)h;
+  if (u == v) x = (h == 0.0f ? 1.0 : (double)h) + *lam_p;
+  Hb[(int64_t)i * g * g + t] = x;
+}
+
+__global__ __launch_bounds__(256) void oaem_load(const void* __restrict__ W, int wdtype,
+                                                 int n, int64_t ldw, double* __restrict__ R) {
+  const int r = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  double v;
+  if (wdtype == PWQ_BF16) {
+    const uint16_t b = ((const uint16_t*)W)[(int64_t)r * ldw + c];
+    v = (double)__uint_as_float((uint32_t)b << 16);
+  } else {
+    v = (double)((const float*)W)[(int64_t)r * ldw + c];
+  }
+  R[(int64_t)r * n + c] = v;
+}
+
+__global__ __launch_bounds__(256) void oaem_seed(const double* __restrict__ R, int m, int n,
+                                                 int g, const int64_t* __restrict__ seeds,
+                                                 int K, double* __restrict__ C,
+                                                 pwq_result* res) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  const int ng = n / g;
+  int64_t s = seeds[k];
+  if (s < 0 || s >= (int64_t)m * ng) {
+    res->info = -1;
+    s = 0;
+  }
+  const int r = (int)(s / ng), i = (int)(s % ng);
+  for (int e = 0; e < g; ++e) C[(int64_t)k * g + e] = R[(int64_t)r * n + i * g + e];
+}
+
+__global__ __launch_bounds__(256) void oaem_qtable(const double* __restrict__ Hb,
+                                                   const double* __restrict__ C, int K, int g,
+                                                   double* __restrict__ Q) {
+  __shared__ double h[kMaxG * kMaxG];
+  const int i = blockIdx.x;
+  for (int t = threadIdx.x; t < g * g; t += 256) h[t] = Hb[(int64_t)i * g * g + t];
+  __syncthreads();
+  for (int k = blockIdx.y * 256 + threadIdx.x; k < K; k += 256 * gridDim.y) {
+    double c[kMaxG];
+    for (int e = 0; e < g; ++e) c[e] = C[(int64_t)k * g + e];
+    double q = 0.0;
+    for (int u = 0; u < g; ++u) {
+      double hu = 0.0;
+      for (int v = 0; v < g; ++v) hu += h[u * g + v] * c[v];
+      q += c[u] * hu;
+    }
+    Q[(int64_t)i * K + k] = q;
+  }
+}
+
+// grid (ng, ceil(m / 256)); dynamic LDS: K g + K doubles.
+__global__ __launch_bounds__(256) void oaem_estep(const double* __restrict__ R, int m, int n,
+                                                  int g, const double* __restrict__ Hb,
+                                                  const double* __restrict__ C,
+                                                  const double* __restrict__ Q, int K,
+                                                  int32_t* __restrict__ a) {
+  extern __shared__ double lds[];
+  __shared__ double h[kMaxG * kMaxG];
+  double* cs = lds;             // K x g
+  double* qs = lds + K * g;     // K
+  const int i = blockIdx.x, ng = n / g;
+  for (int t = threadIdx.x; t < K * g; t += 256) cs[t] = C[t];
+  for (int t = threadIdx.x; t < K; t += 256) qs[t] = Q[(int64_t)i * K + t];
+  for (int t = threadIdx.x; t < g * g; t += 256) h[t] = Hb[(int64_t)i * g * g + t];
+  __syncthreads();
+  const int r = blockIdx.y * 256 + threadIdx.x;
+  if (r >= m) return;
+  double w[kMaxG], hw[kMaxG];
+  for (int e = 0; e < g; ++e) w[e] = R[(int64_t)r * n + i * g + e];
+  for (int u = 0; u < g; ++u) {
+    double s = 0.0;
+    for (int v = 0; v < g; ++v) s += h[u * g + v] * w[v];
+    hw[u] = 2.0 * s;
+  }
+  double best = INFINITY;
+  int bk = 0;
+  for (int k = 0; k < K; ++k) {
+    double dot = 0.0;
+    const double* ck = cs + k * g;
+    for (int e = 0; e < g; ++e) dot += hw[e] * ck[e];
+    const double sc = qs[k] - dot;
+    if (sc < best) {
+      best = sc;
+      bk = k;
+    }
+  }
+  a[(int64_t)r * ng + i] = bk;
+}
+
+// grid (ng, ceil(K / 256)): thread k sums the groups of column i assigned
+// to centroid k, rows in increasing order.
+__global__ __launch_bounds__(256) void oaem_msums(const double* __restrict__ R, int m, int n,
+                                                  int g, const int32_t* __restrict__ a, int K,
+                                                  double* __restrict__ S,
+                                                  int32_t* __restrict__ cnt) {
+  __shared__ int32_t ac[256];
+  __shared__ double rc[256 * kMaxG];
+  const int i = blockIdx.x, ng = n / g;
+  const int k = blockIdx.y * 256 + threadIdx.x;
+  double s[kMaxG];
+  for (int e = 0; e < kMaxG; ++e) s[e] = 0.0;
+  int c = 0;
+  for (int r0 = 0; r0 < m; r0 += 256) {
+    const int rr = r0 + threadIdx.x;
+    ac[threadIdx.x] = rr < m ? a[(int64_t)rr * ng + i] : -1;
+    for (int t = threadIdx.x; t < 256 * g; t += 256) {
+      const int row = r0 + t / g;
+      rc[t] = row < m ? R[(int64_t)row * n + i * g + t % g] : 0.0;
+    }
+    __syncthreads();
+    const int lim = m - r0 < 256 ? m - r0 : 256;
+    for (int t = 0; t < lim; ++t) {
+      if (ac[t] == k) {
+        ++c;
+        for (int e = 0; e < g; ++e) s[e] += rc[t * g + e];
+      }
+    }
+    __syncthreads();
+  }
+  if (k < K) {
+    const int64_t o = (int64_t)i * K + k;
+    cnt[o] = c;
+    for (int e = 0; e < g; ++e) S[o * g + e] = s[e];
+  }
+}
+
+// grid K: centroid k <- solve (sum_i cnt_ik H_i) c = sum_i H_i S_ik, or
+// unchanged when no group is assigned to it.
+__global__ __launch_bounds__(256) void oaem_msolve(const double* __restrict__ Hb, int ng, int g,
+                                                   const double* __restrict__ S,
+                                                   const int32_t* __restrict__ cnt, int K,
+                                                   double* __restrict__ C) {
+  __shared__ double A[kMaxG * kMaxG];
+  __shared__ double bsh[kMaxG];
+  __shared__ int64_t total;
+  const int k = blockIdx.x;
+  const int t = threadIdx.x;
+  for (int idx = t; idx < g * g; idx += 256) {
+    double acc = 0.0;
+    for (int i = 0; i < ng; ++i)
+      acc += (double)cnt[(int64_t)i * K + k] * Hb[(int64_t)i * g * g + idx];
+    A[idx] = acc;
+  }
+  if (t < g) {
+    double acc = 0.0;
+    for (int i = 0; i < ng; ++i) {
+      const double* h = Hb + (int64_t)i * g * g + t * g;
+      const double* sv = S + ((int64_t)i * K + k) * g;
+      double d = 0.0;
+      for (int v = 0; v < g; ++v) d += h[v] * sv[v];
+      acc += d;
+    }
+    bsh[t] = acc;
+  }
+  if (t == 0) {
+    int64_t c = 0;
+    for (int i = 0; i < ng; ++i) c += cnt[(int64_t)i * K + k];
+    total = c;
+  }
+  __syncthreads();
+  if (t != 0 || total == 0) return;
+  // Cholesky A = L L^T in place (lower), then forward / back substitution
+  for (int j = 0; j < g; ++j) {
+    double d = A[j * g + j];
+    for (int p = 0; p < j; ++p) d -= A[j * g + p] * A[j * g + p];
+    if (!(d > 0.0)) return;               // keep the centroid
+    const double ljj = sqrt(d);
+    A[j * g + j] = ljj;
+    for (int u = j + 1; u < g; ++u) {
+      double x = A[u * g + j];
+      for (int p = 0; p < j; ++p) x -= A[u * g + p] * A[j * g + p];
+      A[u * g + j] = x / ljj;
+    }
+  }
+  double y[kMaxG];
+  for (int u = 0; u < g; ++u) {
+    double x = bsh[u];
+    for (int p = 0; p < u; ++p) x -= A[u * g + p] * y[p];
+    y[u] = x / A[u * g + u];
+  }
+  for (int u = g - 1; u >= 0; --u) {
+    double x = y[u];
+    for (int p = u + 1; p < g; ++p) x -= A[p * g + u] * y[p];
+    y[u] = x / A[u * g + u];
+  }
+  for (int u = 0; u < g; ++u) C[(int64_t)k * g + u] = y[u];
+}
+
+__global__ __launch_bounds__(256) void oaem_apply(double* __restrict__ R, int n, int g,
+                                                  const int32_t* __restrict__ a,
+                                                  const double* __restrict__ C) {
+  const int r = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  const int ng = n / g, i = c / g, e = c % g;
+  const int k = a[(int64_t)r * ng + i];
+  R[(int64_t)r * n + c] -= C[(int64_t)k * g + e];
+}
+
+// Per-workgroup sums of e^T H_i e over 256 groups (index r ng + i), fixed
+// tree; the last launch of a stage sums the partials in order.
+__global__ __launch_bounds__(256) void oaem_objective(const double* __restrict__ R, int m,
+                                                      int n, int g,
+                                                      const double* __restrict__ Hb,
+                                                      double* __restrict__ part) {
+  __shared__ double red[256];
+  const int ng = n / g;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double val = 0.0;
+  if (q < (int64_t)m * ng) {
+    const int r = (int)(q / ng), i = (int)(q % ng);
+    double e[kMaxG];
+    for (int u = 0; u < g; ++u) e[u] = R[(int64_t)r * n + i * g + u];
+    const double* h = Hb + (int64_t)i * g * g;
+    for (int u = 0; u < g; ++u) {
+      double s = 0.0;
+      for (int v = 0; v < g; ++v) s += h[u * g + v] * e[v];
+      val += e[u] * s;
+    }
+  }
+  red[threadIdx.x] = val;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void oaem_objective_sum(const double* __restrict__ part,
+                                                          int np, double* __restrict__ out) {
+  __shared__ double red[256];
+  double v = 0.0;
+  for (int t = threadIdx.x; t < np; t += 256) v += part[t];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+}  // namespace
+
+int64_t oaem_objective_parts(int64_t m, int64_t n, int32_t g) {
+  return (m * (n / g) + 255) / 256;
+}
+
+hipError_t launch_oaem(const void* W, int32_t wdtype, int64_t m64, int64_t n64, int64_t ldw,
+                       const float* H, const double* lam, int32_t g, int32_t K, int32_t M,
+                       int32_t iters, const int64_t* seeds, double* books, int32_t* codes,
+                       double* obj, pwq_result* res, const OaemWs& w, hipStream_t st) {
+  const int m = (int)m64, n = (int)n64, ng = n / g;
+  oaem_blocks<<<ng, 256, 0, st>>>(H, n, g, lam, w.Hb);
+  oaem_load<<<dim3((unsigned)((n + 255) / 256), (unsigned)m), 256, 0, st>>>(W, wdtype, n, ldw,
+                                                                             w.R);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned kb = (unsigned)((K + 255) / 256);
+  const size_t lds = (size_t)(K * g + K) * sizeof(double);
+  const int64_t nparts = oaem_objective_parts(m, n, g);
+  for (int t = 0; t < M; ++t) {
+    double* C = books + (int64_t)t * K * g;
+    int32_t* a = codes + (int64_t)t * m * ng;
+    oaem_seed<<<kb, 256, 0, st>>>(w.R, m, n, g, seeds + (int64_t)t * K, K, C, res);
+    for (int it = 0; it <= iters; ++it) {
+      oaem_qtable<<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.Hb, C, K, g, w.Q);
+      oaem_estep<<<dim3((unsigned)ng, (unsigned)((m + 255) / 256)), 256, lds, st>>>(
+          w.R, m, n, g, w.Hb, C, w.Q, K, a);
+      if (it < iters) {
+        oaem_msums<<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
+        oaem_msolve<<<(unsigned)K, 256, 0, st>>>(w.Hb, ng, g, w.S, w.cnt, K, C);
+      }
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    oaem_apply<<<dim3((unsigned)((n + 255) / 256), (unsigned)m), 256, 0, st>>>(w.R, n, g, a, C);
+    if (obj) {
+      oaem_objective<<<(unsigned)nparts, 256, 0, st>>>(w.R, m, n, g, w.Hb, w.part);
+      oaem_objective_sum<<<1, 256, 0, st>>>(w.part, (int)nparts, obj + t);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pwq

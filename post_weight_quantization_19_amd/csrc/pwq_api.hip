@@ -485,6 +485,66 @@ pwq_status pwq_min_pivot_order(const float* H, int64_t n, double damp, int32_t* 
   return ok();
 }
 
+static void carve_oaem(Carver& c, int64_t m, int64_t n, int32_t g, int32_t K, OaemWs* w) {
+  const int64_t ng = n / g;
+  w->Hb = (double*)c.take((size_t)ng * g * g * sizeof(double));
+  w->R = (double*)c.take((size_t)m * n * sizeof(double));
+  w->Q = (double*)c.take((size_t)ng * K * sizeof(double));
+  w->S = (double*)c.take((size_t)ng * K * g * sizeof(double));
+  w->cnt = (int32_t*)c.take((size_t)ng * K * 4);
+  w->part = (double*)c.take((size_t)oaem_objective_parts(m, n, g) * sizeof(double));
+}
+
+static bool oaem_shape_ok(int64_t m, int64_t n, int32_t g, int32_t K) {
+  return m >= 1 && n >= 1 && m <= INT32_MAX && n <= INT32_MAX && g >= 1 && g <= kOaemMaxG &&
+         n % g == 0 && K >= 1 && (int64_t)K * (g + 1) <= kOaemMaxLds &&
+         m * (n / g) <= INT32_MAX;
+}
+
+size_t pwq_oaem_workspace_size(int64_t m, int64_t n, int32_t g, int32_t K) {
+  if (!oaem_shape_ok(m, n, g, K)) return 0;
+  Carver c(nullptr);
+  c.take(sizeof(DevFlags));
+  c.take(sizeof(double));
+  OaemWs w;
+  carve_oaem(c, m, n, g, K, &w);
+  return c.size();
+}
+
+pwq_status pwq_oaem_init(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
+                         const float* H, double damp, int32_t g, int32_t K, int32_t M,
+                         int32_t iters, const int64_t* seeds, double* codebooks, int32_t* codes,
+                         double* objective, pwq_result* result, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!W || !H || !seeds || !codebooks || !codes || !result)
+    return fail(PWQ_ERR_INVALID_ARG, "W, H, seeds, codebooks, codes and result must be non-NULL");
+  if (wdtype != PWQ_F32 && wdtype != PWQ_BF16)
+    return fail(PWQ_ERR_INVALID_ARG, "W dtype must be PWQ_F32 or PWQ_BF16");
+  if (!oaem_shape_ok(m, n, g, K))
+    return fail(PWQ_ERR_INVALID_ARG,
+                "need m, n >= 1, 1 <= g <= %d dividing n, K >= 1 with K (g + 1) <= %d "
+                "(got m %lld n %lld g %d K %d)", kOaemMaxG, kOaemMaxLds, (long long)m,
+                (long long)n, g, K);
+  if (ldw < n) return fail(PWQ_ERR_INVALID_ARG, "ldw < n");
+  if (M < 1 || iters < 0) return fail(PWQ_ERR_INVALID_ARG, "need M >= 1 and iters >= 0");
+  if (!(damp >= 0.0) || !(damp < 1e30)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
+  pwq_status s = check_ws(ws, ws_bytes, pwq_oaem_workspace_size(m, n, g, K));
+  if (s != PWQ_OK) return s;
+  Carver c(ws);
+  DevFlags* flags = (DevFlags*)c.take(sizeof(DevFlags));
+  double* lam = (double*)c.take(sizeof(double));
+  OaemWs w;
+  carve_oaem(c, m, n, g, K, &w);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_init_flags(flags, result, 1, st);
+  if (e == hipSuccess) e = launch_damp_lambda(H, n, damp, nullptr, result, flags, lam, st);
+  if (e == hipSuccess)
+    e = launch_oaem(W, wdtype, m, n, ldw, H, lam, g, K, M, iters, seeds, codebooks, codes,
+                    objective, result, w, st);
+  if (e != hipSuccess) return hip_fail(e, "oaem_init launch");
+  return ok();
+}
+
 size_t pwq_rate_workspace_size(int64_t n) {
   if (n <= 0) return 0;
   Carver c(nullptr);

@@ -44,6 +44,25 @@ hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t 
                                 const int32_t* perm, void* L, int32_t* dead, pwq_result* res,
                                 DevFlags* flags, double* lam, void* dscratch, hipStream_t st);
 
+// OA-EM codebook initialisation (all float64).  Workspace: Hb ng g g,
+// R m n, Q ng K, S ng K g doubles, cnt ng K int32, part
+// oaem_objective_parts(m, n, g) doubles.
+constexpr int kOaemMaxG = 16;
+constexpr int kOaemMaxLds = 8192;   // K (g + 1) doubles of codebook and norms in LDS
+struct OaemWs {
+  double* Hb;
+  double* R;
+  double* Q;
+  double* S;
+  int32_t* cnt;
+  double* part;
+};
+int64_t oaem_objective_parts(int64_t m, int64_t n, int32_t g);
+hipError_t launch_oaem(const void* W, int32_t wdtype, int64_t m, int64_t n, int64_t ldw,
+                       const float* H, const double* lam, int32_t g, int32_t K, int32_t M,
+                       int32_t iters, const int64_t* seeds, double* books, int32_t* codes,
+                       double* obj, pwq_result* res, const OaemWs& w, hipStream_t st);
+
 // Dead inputs and lambda = damp * mean(diag H after the dead fix), as the
 // first stage of launch_damp_cholesky (writes res->lambda, res->ndead).
 hipError_t launch_damp_lambda(const float* H, int64_t n, double damp, int32_t* dead,

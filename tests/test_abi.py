@@ -25,7 +25,7 @@ def header_functions():
 def test_exports_match_header():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     assert sorted(B.EXPORTS) == names
     for nm in names:
         assert getattr(L, nm) is not None
@@ -159,6 +159,29 @@ def test_min_pivot_validation():
     a = L.pwq_quant_layer_workspace_size(64, 300, 0, 0, 3, 32, 0)
     b = L.pwq_quant_layer_workspace_size(64, 300, 0, 0, 4, 32, 0)
     assert b >= a + 300 * 300 * 8
+
+
+def test_oaem_validation():
+    L = B.lib()
+
+    def call(m=16, n=64, g=8, K=16, M=1, iters=2, wdt=0, ldw=64, damp=0.01, ws=FAKE,
+             wsb=1 << 30, seeds=FAKE):
+        return L.pwq_oaem_init(FAKE, wdt, m, n, ldw, FAKE, damp, g, K, M, iters, seeds, FAKE,
+                               FAKE, None, FAKE, ws, wsb, None)
+    assert call(g=7) == INVALID                  # g does not divide n
+    assert call(g=32, n=64, ldw=64) == INVALID   # g above 16
+    assert call(K=0) == INVALID
+    assert call(K=1000) == INVALID               # codebook + norms above the LDS budget
+    assert call(M=0) == INVALID
+    assert call(iters=-1) == INVALID
+    assert call(wdt=2) == INVALID
+    assert call(ldw=32) == INVALID
+    assert call(damp=-1.0) == INVALID
+    assert call(seeds=None) == INVALID
+    need = L.pwq_oaem_workspace_size(16, 64, 8, 16)
+    assert need >= 16 * 64 * 8
+    assert call(wsb=need - 256) == WS
+    assert L.pwq_oaem_workspace_size(16, 64, 7, 16) == 0
 
 
 def test_kernel_timer_validation():
