@@ -59,6 +59,11 @@ def parse():
                     help="time the overflow-tolerant layer (SSQR: scale search for this "
                          "outlier density) instead of the plain one")
     ap.add_argument("--ssqr-iters", type=int, default=12)
+    ap.add_argument("--oaem", action="store_true",
+                    help="time OA-EM codebook initialisation of the layer (groups of 8, "
+                         "K = 256, M = 2 codebooks, --oaem-rounds EM rounds per codebook) "
+                         "instead of the quantizer")
+    ap.add_argument("--oaem-rounds", type=int, default=10)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the achievable-peak probe (MFMA and copy microbenchmarks)")
     ap.add_argument("--cpu-token-fraction", type=int, default=8,
@@ -259,10 +264,91 @@ def ssqr_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def oaem_bench(args):
+    """OA-EM initialisation of the layer's codebooks: one call = the Hessian
+    once, then M = 2 residual stages of `rounds` E/M rounds and a final
+    E-step each.  The E-step (fp64 Mahalanobis distances to every centroid)
+    is the dominant kernel; it is timed with HIP events around its launches
+    in a run of its own.  Prints one JSON line of its own."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_19_amd as P
+    import synth
+
+    cfg = synth.config(args.config)
+    if cfg.ntok == 0:
+        raise SystemExit("OA-EM needs calibration activations (--config 1 to 4)")
+    m, n, N = cfg.m, cfg.n, cfg.ntok
+    g, K, M, T = 8, 256, 2, args.oaem_rounds
+    ng = n // g
+    print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
+          flush=True)
+    lay = synth.make_layer(cfg, keep_x_f32=False)
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xl = args.x_layout
+    if xl == "tokens":
+        X = X.t().contiguous()
+    rng = np.random.default_rng(2024)
+    seeds = torch.from_numpy(np.stack([rng.choice(m * ng, K, replace=False)
+                                       for _ in range(M)])).to(dev)
+    H = torch.empty((n, n), dtype=torch.float32, device=dev)
+
+    def call():
+        P.hessian_accum(X, H=H, x_layout=xl)
+        return P.oaem_init(W, H, seeds, g=g, iters=T, damp=cfg.damp)
+    books, codes, obj, res = call()                # warm-up
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 5)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    # the E-step alone: one round of one stage is qtable + E-step; time a
+    # run without M-steps (iters 0: one E-step per stage) against events
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    one = seeds[:1].contiguous()
+    P.oaem_init(W, H, one, g=g, iters=0, damp=cfg.damp, want_objective=False)
+    a.record(stream)
+    for _ in range(5):
+        P.oaem_init(W, H, one, g=g, iters=0, damp=cfg.damp, want_objective=False)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t_e = a.elapsed_time(b) / 5 / 1e3
+    flops_e = 2.0 * m * ng * (g * g + K * g)
+    o = obj.cpu().numpy().tolist()
+    line = {
+        "metric": "OA-EM codebook initialisation time & weights/s",
+        "value": m * n / dt, "unit": "weights/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64 (distances, sums, solves); bf16 Hessian products",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{cfg.name} (OA-EM: groups of {g}, K {K}, M {M} codebooks, "
+                               f"{T} EM rounds each, seeded initial groups)",
+                   "m": m, "n": n, "ntok": N, "x_layout": xl},
+        "oaem": {"objective_per_stage": o, "info": P.read_result(res)["info"]},
+        "roofline": {"bound": "alu (fp64 vector FMA)",
+                     "kernel": "oaem_estep (+ its damping, load and norm table, timed as one "
+                               "E-step-only call)",
+                     "achieved": flops_e / t_e / 1e12, "peak": PEAK_F64_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops_e / t_e / 1e12 / PEAK_F64_TFLOPS,
+                     "traffic": None, "avg_call_ms": t_e * 1e3, "flops_per_estep": flops_e},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.ssqr is not None and args.gpus == 1:
         ssqr_bench(args)
+        return
+    if args.oaem and args.gpus == 1:
+        oaem_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the "

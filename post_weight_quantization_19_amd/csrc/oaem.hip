@@ -16,16 +16,16 @@
 //
 // Kernels, per stage and round:
 //   oaem_qtable  Q[i][k] = c_k^T H_i c_k                     (ng x K)
-//   oaem_estep   one thread per row of a group column: h = H_i w, then
-//                argmin_k Q[i][k] - 2 h . c_k with the codebook in LDS
-//                (the same argmin as the distance, which differs from it
-//                by w^T H_i w)
+//   oaem_estep   one thread per row (two for groups of 8) of a group
+//                column: h = H_i w, then argmin_k Q[i][k] - 2 h . c_k with
+//                the codebook in LDS (the same argmin as the distance,
+//                which differs from it by w^T H_i w)
 //   oaem_msums   per (group column, centroid): the sum of the assigned
 //                residual groups and their count, rows in increasing order
 //                (chunks of assignments and rows staged in LDS)
 //   oaem_msolve  one workgroup per centroid: A = sum_i cnt_ik H_i,
-//                b = sum_i H_i S_ik in a fixed order, then A c = b by
-//                Cholesky (g <= 16)
+//                b = sum_i H_i S_ik over fixed slices of i added in order,
+//                then A c = b by Cholesky (g <= 16)
 //   oaem_apply / oaem_objective after the final E-step.
 #include "pwq_device.h"
 #include "pwq_internal.h"
@@ -101,12 +101,17 @@ __global__ __launch_bounds__(256) void oaem_qtable(const double* __restrict__ Hb
   }
 }
 
-// grid (ng, ceil(m / 256)); dynamic LDS: K g + K doubles.
+// grid (ng, ceil(m / (256 RPT))); dynamic LDS: K g + K doubles.  GS is the
+// group size when known at compile time (0: the runtime g); each thread
+// takes RPT rows, so each centroid read from LDS serves RPT rows.
+template <int GS, int RPT>
 __global__ __launch_bounds__(256) void oaem_estep(const double* __restrict__ R, int m, int n,
-                                                  int g, const double* __restrict__ Hb,
+                                                  int g_rt, const double* __restrict__ Hb,
                                                   const double* __restrict__ C,
                                                   const double* __restrict__ Q, int K,
                                                   int32_t* __restrict__ a) {
+  constexpr int GM = GS > 0 ? GS : kMaxG;
+  const int g = GS > 0 ? GS : g_rt;
   extern __shared__ double lds[];
   __shared__ double h[kMaxG * kMaxG];
   double* cs = lds;             // K x g
@@ -116,56 +121,104 @@ __global__ __launch_bounds__(256) void oaem_estep(const double* __restrict__ R, 
   for (int t = threadIdx.x; t < K; t += 256) qs[t] = Q[(int64_t)i * K + t];
   for (int t = threadIdx.x; t < g * g; t += 256) h[t] = Hb[(int64_t)i * g * g + t];
   __syncthreads();
-  const int r = blockIdx.y * 256 + threadIdx.x;
-  if (r >= m) return;
-  double w[kMaxG], hw[kMaxG];
-  for (int e = 0; e < g; ++e) w[e] = R[(int64_t)r * n + i * g + e];
-  for (int u = 0; u < g; ++u) {
-    double s = 0.0;
-    for (int v = 0; v < g; ++v) s += h[u * g + v] * w[v];
-    hw[u] = 2.0 * s;
-  }
-  double best = INFINITY;
-  int bk = 0;
-  for (int k = 0; k < K; ++k) {
-    double dot = 0.0;
-    const double* ck = cs + k * g;
-    for (int e = 0; e < g; ++e) dot += hw[e] * ck[e];
-    const double sc = qs[k] - dot;
-    if (sc < best) {
-      best = sc;
-      bk = k;
+  const int r0 = blockIdx.y * 256 * RPT + threadIdx.x;
+  if (r0 >= m) return;
+  double hw[RPT][GM];
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int r = r0 + q * 256 < m ? r0 + q * 256 : r0;   // a clamped row is computed twice
+    double w[GM];
+#pragma unroll
+    for (int e = 0; e < GM; ++e) {
+      const double x = R[(int64_t)r * n + i * g + (e < g ? e : 0)];   // index kept in the row
+      w[e] = e < g ? x : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < GM; ++u) {
+      double acc = 0.0;
+#pragma unroll
+      for (int v = 0; v < GM; ++v)
+        if (u < g && v < g) acc += h[u * g + v] * w[v];
+      hw[q][u] = 2.0 * acc;
     }
   }
-  a[(int64_t)r * ng + i] = bk;
+  double best[RPT];
+  int bk[RPT];
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    best[q] = INFINITY;
+    bk[q] = 0;
+  }
+  for (int k = 0; k < K; ++k) {
+    const double* ck = cs + k * g;
+    double c[GM];
+#pragma unroll
+    for (int e = 0; e < GM; ++e) {
+      const double x = ck[e < g ? e : 0];
+      c[e] = e < g ? x : 0.0;
+    }
+    const double qk = qs[k];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      double dot = 0.0;
+#pragma unroll
+      for (int e = 0; e < GM; ++e)
+        if (e < g) dot += hw[q][e] * c[e];
+      const double sc = qk - dot;
+      if (sc < best[q]) {
+        best[q] = sc;
+        bk[q] = k;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int r = r0 + q * 256;
+    if (r < m) a[(int64_t)r * ng + i] = bk[q];
+  }
 }
 
 // grid (ng, ceil(K / 256)): thread k sums the groups of column i assigned
-// to centroid k, rows in increasing order.
+// to centroid k, rows in increasing order.  GS as for the E-step (the loops
+// over the group are unrolled to a compile-time bound so that the sums stay
+// in registers).
+template <int GS>
 __global__ __launch_bounds__(256) void oaem_msums(const double* __restrict__ R, int m, int n,
-                                                  int g, const int32_t* __restrict__ a, int K,
-                                                  double* __restrict__ S,
+                                                  int g_rt, const int32_t* __restrict__ a,
+                                                  int K, double* __restrict__ S,
                                                   int32_t* __restrict__ cnt) {
+  constexpr int GM = GS > 0 ? GS : kMaxG;
+  const int g = GS > 0 ? GS : g_rt;
   __shared__ int32_t ac[256];
-  __shared__ double rc[256 * kMaxG];
+  __shared__ double rc[256 * GM];
   const int i = blockIdx.x, ng = n / g;
   const int k = blockIdx.y * 256 + threadIdx.x;
-  double s[kMaxG];
-  for (int e = 0; e < kMaxG; ++e) s[e] = 0.0;
+  double s[GM];
+#pragma unroll
+  for (int e = 0; e < GM; ++e) s[e] = 0.0;
   int c = 0;
   for (int r0 = 0; r0 < m; r0 += 256) {
     const int rr = r0 + threadIdx.x;
     ac[threadIdx.x] = rr < m ? a[(int64_t)rr * ng + i] : -1;
-    for (int t = threadIdx.x; t < 256 * g; t += 256) {
-      const int row = r0 + t / g;
-      rc[t] = row < m ? R[(int64_t)row * n + i * g + t % g] : 0.0;
+#pragma unroll
+    for (int e = 0; e < GM; ++e) {
+      // row rr's group, stored at rc[threadIdx.x GM + e]
+      const double x = rr < m && e < g ? R[(int64_t)rr * n + i * g + e] : 0.0;
+      rc[threadIdx.x * GM + e] = x;
     }
     __syncthreads();
-    const int lim = m - r0 < 256 ? m - r0 : 256;
-    for (int t = 0; t < lim; ++t) {
-      if (ac[t] == k) {
-        ++c;
-        for (int e = 0; e < g; ++e) s[e] += rc[t * g + e];
+    // rows past m hold -1 and never match; eight assignments per pass
+    for (int t0 = 0; t0 < 256; t0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ac[t0 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (v[u] == k) {
+          ++c;
+#pragma unroll
+          for (int e = 0; e < GM; ++e) s[e] += rc[(t0 + u) * GM + e];
+        }
       }
     }
     __syncthreads();
@@ -173,44 +226,72 @@ __global__ __launch_bounds__(256) void oaem_msums(const double* __restrict__ R, 
   if (k < K) {
     const int64_t o = (int64_t)i * K + k;
     cnt[o] = c;
-    for (int e = 0; e < g; ++e) S[o * g + e] = s[e];
+#pragma unroll
+    for (int e = 0; e < GM; ++e)
+      if (e < g) S[o * g + e] = s[e];
   }
 }
 
 // grid K: centroid k <- solve (sum_i cnt_ik H_i) c = sum_i H_i S_ik, or
-// unchanged when no group is assigned to it.
+// unchanged when no group is assigned to it.  The sums over the group
+// columns i are split into fixed slices (i = s, s + nslices, ...) over all
+// 256 threads and the slices are added in order, so the result does not
+// depend on timing.
 __global__ __launch_bounds__(256) void oaem_msolve(const double* __restrict__ Hb, int ng, int g,
                                                    const double* __restrict__ S,
                                                    const int32_t* __restrict__ cnt, int K,
                                                    double* __restrict__ C) {
+  __shared__ double part[256];
   __shared__ double A[kMaxG * kMaxG];
   __shared__ double bsh[kMaxG];
   __shared__ int64_t total;
   const int k = blockIdx.x;
   const int t = threadIdx.x;
-  for (int idx = t; idx < g * g; idx += 256) {
+  const int gg = g * g;
+  // A: entry e = t % gg, slice t / gg
+  {
+    const int ns = 256 / gg;
+    const int e = t % gg, sl = t / gg;
     double acc = 0.0;
-    for (int i = 0; i < ng; ++i)
-      acc += (double)cnt[(int64_t)i * K + k] * Hb[(int64_t)i * g * g + idx];
-    A[idx] = acc;
-  }
-  if (t < g) {
-    double acc = 0.0;
-    for (int i = 0; i < ng; ++i) {
-      const double* h = Hb + (int64_t)i * g * g + t * g;
-      const double* sv = S + ((int64_t)i * K + k) * g;
-      double d = 0.0;
-      for (int v = 0; v < g; ++v) d += h[v] * sv[v];
-      acc += d;
+    if (sl < ns)
+      for (int i = sl; i < ng; i += ns)
+        acc += (double)cnt[(int64_t)i * K + k] * Hb[(int64_t)i * gg + e];
+    part[t] = acc;
+    __syncthreads();
+    if (t < gg) {
+      double sum = 0.0;
+      for (int q = 0; q < ns; ++q) sum += part[q * gg + t];
+      A[t] = sum;
     }
-    bsh[t] = acc;
+    __syncthreads();
   }
-  if (t == 0) {
-    int64_t c = 0;
-    for (int i = 0; i < ng; ++i) c += cnt[(int64_t)i * K + k];
-    total = c;
+  // b: entry u = t % g, slice t / g
+  {
+    const int ns = 256 / g;
+    const int u = t % g, sl = t / g;
+    double acc = 0.0;
+    if (sl < ns)
+      for (int i = sl; i < ng; i += ns) {
+        const double* hr = Hb + (int64_t)i * gg + u * g;
+        const double* sv = S + ((int64_t)i * K + k) * g;
+        double d = 0.0;
+        for (int v = 0; v < g; ++v) d += hr[v] * sv[v];
+        acc += d;
+      }
+    part[t] = acc;
+    if (t == 0) {
+      int64_t c = 0;
+      for (int i = 0; i < ng; ++i) c += cnt[(int64_t)i * K + k];
+      total = c;
+    }
+    __syncthreads();
+    if (t < g) {
+      double sum = 0.0;
+      for (int q = 0; q < ns; ++q) sum += part[q * g + t];
+      bsh[t] = sum;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (t != 0 || total == 0) return;
   // Cholesky A = L L^T in place (lower), then forward / back substitution
   for (int j = 0; j < g; ++j) {
@@ -252,22 +333,32 @@ __global__ __launch_bounds__(256) void oaem_apply(double* __restrict__ R, int n,
 
 // Per-workgroup sums of e^T H_i e over 256 groups (index r ng + i), fixed
 // tree; the last launch of a stage sums the partials in order.
+template <int GS>
 __global__ __launch_bounds__(256) void oaem_objective(const double* __restrict__ R, int m,
-                                                      int n, int g,
+                                                      int n, int g_rt,
                                                       const double* __restrict__ Hb,
                                                       double* __restrict__ part) {
+  constexpr int GM = GS > 0 ? GS : kMaxG;
+  const int g = GS > 0 ? GS : g_rt;
   __shared__ double red[256];
   const int ng = n / g;
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   double val = 0.0;
   if (q < (int64_t)m * ng) {
     const int r = (int)(q / ng), i = (int)(q % ng);
-    double e[kMaxG];
-    for (int u = 0; u < g; ++u) e[u] = R[(int64_t)r * n + i * g + u];
+    double e[GM];
+#pragma unroll
+    for (int u = 0; u < GM; ++u) {
+      const double x = R[(int64_t)r * n + i * g + (u < g ? u : 0)];
+      e[u] = u < g ? x : 0.0;
+    }
     const double* h = Hb + (int64_t)i * g * g;
-    for (int u = 0; u < g; ++u) {
+#pragma unroll
+    for (int u = 0; u < GM; ++u) {
       double s = 0.0;
-      for (int v = 0; v < g; ++v) s += h[u * g + v] * e[v];
+#pragma unroll
+      for (int v = 0; v < GM; ++v)
+        if (u < g && v < g) s += h[u * g + v] * e[v];
       val += e[u] * s;
     }
   }
@@ -319,10 +410,17 @@ hipError_t launch_oaem(const void* W, int32_t wdtype, int64_t m64, int64_t n64, 
     oaem_seed<<<kb, 256, 0, st>>>(w.R, m, n, g, seeds + (int64_t)t * K, K, C, res);
     for (int it = 0; it <= iters; ++it) {
       oaem_qtable<<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.Hb, C, K, g, w.Q);
-      oaem_estep<<<dim3((unsigned)ng, (unsigned)((m + 255) / 256)), 256, lds, st>>>(
-          w.R, m, n, g, w.Hb, C, w.Q, K, a);
+      if (g == 8)
+        oaem_estep<8, 2><<<dim3((unsigned)ng, (unsigned)((m + 511) / 512)), 256, lds, st>>>(
+            w.R, m, n, g, w.Hb, C, w.Q, K, a);
+      else
+        oaem_estep<0, 1><<<dim3((unsigned)ng, (unsigned)((m + 255) / 256)), 256, lds, st>>>(
+            w.R, m, n, g, w.Hb, C, w.Q, K, a);
       if (it < iters) {
-        oaem_msums<<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
+        if (g == 8)
+          oaem_msums<8><<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
+        else
+          oaem_msums<0><<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
         oaem_msolve<<<(unsigned)K, 256, 0, st>>>(w.Hb, ng, g, w.S, w.cnt, K, C);
       }
       e = hipGetLastError();
@@ -330,7 +428,10 @@ hipError_t launch_oaem(const void* W, int32_t wdtype, int64_t m64, int64_t n64, 
     }
     oaem_apply<<<dim3((unsigned)((n + 255) / 256), (unsigned)m), 256, 0, st>>>(w.R, n, g, a, C);
     if (obj) {
-      oaem_objective<<<(unsigned)nparts, 256, 0, st>>>(w.R, m, n, g, w.Hb, w.part);
+      if (g == 8)
+        oaem_objective<8><<<(unsigned)nparts, 256, 0, st>>>(w.R, m, n, g, w.Hb, w.part);
+      else
+        oaem_objective<0><<<(unsigned)nparts, 256, 0, st>>>(w.R, m, n, g, w.Hb, w.part);
       oaem_objective_sum<<<1, 256, 0, st>>>(w.part, (int)nparts, obj + t);
     }
     e = hipGetLastError();
