@@ -16,7 +16,7 @@
 //
 // Kernels, per stage and round:
 //   oaem_qtable  Q[i][k] = c_k^T H_i c_k                     (ng x K)
-//   oaem_estep   one thread per row (two for groups of 8) of a group
+//   oaem_estep   one thread per row (four for groups of 8) of a group
 //                column: h = H_i w, then argmin_k Q[i][k] - 2 h . c_k with
 //                the codebook in LDS (the same argmin as the distance,
 //                which differs from it by w^T H_i w)
@@ -411,7 +411,7 @@ hipError_t launch_oaem(const void* W, int32_t wdtype, int64_t m64, int64_t n64, 
     for (int it = 0; it <= iters; ++it) {
       oaem_qtable<<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.Hb, C, K, g, w.Q);
       if (g == 8)
-        oaem_estep<8, 2><<<dim3((unsigned)ng, (unsigned)((m + 511) / 512)), 256, lds, st>>>(
+        oaem_estep<8, 4><<<dim3((unsigned)ng, (unsigned)((m + 1023) / 1024)), 256, lds, st>>>(
             w.R, m, n, g, w.Hb, C, w.Q, K, a);
       else
         oaem_estep<0, 1><<<dim3((unsigned)ng, (unsigned)((m + 255) / 256)), 256, lds, st>>>(

@@ -166,6 +166,25 @@ def test_oaem_edges():
     np.testing.assert_allclose(to_np(books), b_o, rtol=1e-10)
 
 
+def test_oaem_largest_codebook():
+    """K (g + 1) at the boundary's limit of 8192 doubles of LDS (groups of 8,
+    K = 910): the E-step launches and matches the oracle's distances."""
+    cfg, W, H, Hd, W64 = _setup(2, 200, 64, 600, "f32")
+    g, K = 8, 910
+    ng = 64 // g
+    rng = np.random.default_rng(11)
+    seeds_np = rng.choice(200 * ng, K, replace=False)[None]
+    books, codes, obj, res = P.oaem_init(W, H, torch.from_numpy(seeds_np).cuda(), g=g, iters=1,
+                                         damp=cfg.damp)
+    torch.cuda.synchronize()
+    assert P.read_result(res)["info"] == 0
+    Hb = O.oaem_blocks(Hd, g)
+    check_estep(W64, Hb, to_np(books)[0], to_np(codes)[0].astype(np.int64))
+    with pytest.raises(RuntimeError):
+        P.oaem_init(W, H, torch.zeros((1, 911), dtype=torch.int64, device="cuda"), g=g,
+                    iters=1, damp=cfg.damp)
+
+
 def test_oaem_full_size_qproj():
     """q_proj (4096 x 4096, groups of 8, K = 256, two stages, 3 rounds):
     sampled rows' assignments against the oracle's distances, the M-step
