@@ -241,7 +241,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n,
  * is smallest (ties: lower column index; NaN counts as smallest) and puts
  * it at position k, so position 0 is processed LAST by the back-to-front
  * sweep.  Computed in float64.
- *   H      : n x n float32 device, lower triangle read.
+ *   H      : n x n float32 device, lower triangle read; 1 <= n <= 65536.
  *   perm   : n int32 device out: perm[k] = column of position k.
  *   pivots : optional n float64 device out: D_kk (NULL to skip).
  *   result : device; info = 0, or k + 1 when pivot k is not positive (then
@@ -273,7 +273,8 @@ pwq_status pwq_min_pivot_order(const float* H, int64_t n, double damp,
  *   centroid with no group keeps its value), then a final E-step gives the
  *   stage's codes and the residual loses the chosen centroids.  float64.
  *   W          : m x n float32 or bfloat16 (row stride ldw >= n), device.
- *   H          : n x n float32 device, lower triangle read (undamped).
+ *   H          : n x n float32 device, lower triangle read (undamped);
+ *                1 <= n <= 65536, m (n / g) < 2^31.
  *   g, K       : 1 <= g <= 16 dividing n; K >= 1 with K (g + 1) <= 8192.
  *   seeds      : M x K int64 device; an index outside [0, m n / g) sets
  *                result->info = -1 (group 0 is used).

@@ -454,7 +454,7 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
 }
 
 size_t pwq_min_pivot_workspace_size(int64_t n) {
-  if (n <= 0) return 0;
+  if (n <= 0 || n > 65536) return 0;
   Carver c(nullptr);
   c.take(sizeof(DevFlags));
   c.take(sizeof(double));
@@ -466,7 +466,7 @@ size_t pwq_min_pivot_workspace_size(int64_t n) {
 pwq_status pwq_min_pivot_order(const float* H, int64_t n, double damp, int32_t* perm,
                                double* pivots, pwq_result* result, void* ws, size_t ws_bytes,
                                void* stream) {
-  if (n <= 0 || n > INT32_MAX) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 2^31)");
+  if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
   if (!H || !perm || !result)
     return fail(PWQ_ERR_INVALID_ARG, "H, perm and result must be non-NULL");
   if (!(damp >= 0.0) || !(damp < 1e30)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
@@ -496,7 +496,7 @@ static void carve_oaem(Carver& c, int64_t m, int64_t n, int32_t g, int32_t K, Oa
 }
 
 static bool oaem_shape_ok(int64_t m, int64_t n, int32_t g, int32_t K) {
-  return m >= 1 && n >= 1 && m <= INT32_MAX && n <= INT32_MAX && g >= 1 && g <= kOaemMaxG &&
+  return m >= 1 && n >= 1 && m <= INT32_MAX && n <= 65536 && g >= 1 && g <= kOaemMaxG &&
          n % g == 0 && K >= 1 && (int64_t)K * (g + 1) <= kOaemMaxLds &&
          m * (n / g) <= INT32_MAX;
 }
@@ -522,7 +522,8 @@ pwq_status pwq_oaem_init(const void* W, int32_t wdtype, int64_t m, int64_t n, in
     return fail(PWQ_ERR_INVALID_ARG, "W dtype must be PWQ_F32 or PWQ_BF16");
   if (!oaem_shape_ok(m, n, g, K))
     return fail(PWQ_ERR_INVALID_ARG,
-                "need m, n >= 1, 1 <= g <= %d dividing n, K >= 1 with K (g + 1) <= %d "
+                "need m >= 1, 1 <= n <= 65536, 1 <= g <= %d dividing n, K >= 1 with "
+                "K (g + 1) <= %d "
                 "(got m %lld n %lld g %d K %d)", kOaemMaxG, kOaemMaxLds, (long long)m,
                 (long long)n, g, K);
   if (ldw < n) return fail(PWQ_ERR_INVALID_ARG, "ldw < n");

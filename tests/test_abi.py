@@ -155,6 +155,9 @@ def test_min_pivot_validation():
     assert L.pwq_min_pivot_order(FAKE, 300, 0.01, FAKE, None, FAKE, FAKE, need - 256,
                                  None) == WS
     assert L.pwq_min_pivot_workspace_size(0) == 0
+    assert L.pwq_min_pivot_workspace_size(65537) == 0    # n x n fp64 beyond the layer's n
+    assert L.pwq_min_pivot_order(FAKE, 1 << 31, 0.01, FAKE, None, FAKE, FAKE, 4096,
+                                 None) == INVALID
     # the layer's workspace grows by the fp64 matrix for this order only
     a = L.pwq_quant_layer_workspace_size(64, 300, 0, 0, 3, 32, 0)
     b = L.pwq_quant_layer_workspace_size(64, 300, 0, 0, 4, 32, 0)
@@ -182,6 +185,8 @@ def test_oaem_validation():
     assert need >= 16 * 64 * 8
     assert call(wsb=need - 256) == WS
     assert L.pwq_oaem_workspace_size(16, 64, 7, 16) == 0
+    assert L.pwq_oaem_workspace_size(16, 65536 + 8, 8, 16) == 0
+    assert call(n=65536 + 8, ldw=65536 + 8) == INVALID
 
 
 def test_kernel_timer_validation():
