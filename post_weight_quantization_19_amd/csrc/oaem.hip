@@ -21,7 +21,8 @@
 //                the codebook in LDS (the same argmin as the distance,
 //                which differs from it by w^T H_i w)
 //   oaem_msums   per (group column, centroid): the sum of the assigned
-//                residual groups and their count, rows in increasing order
+//                residual groups and their count, four quarter sums (rows
+//                in increasing order within each) added in a fixed order
 //                (chunks of assignments and rows staged in LDS)
 //   oaem_msolve  one workgroup per centroid: A = sum_i cnt_ik H_i,
 //                b = sum_i H_i S_ik over fixed slices of i added in order,
@@ -178,37 +179,48 @@ __global__ __launch_bounds__(256) void oaem_estep(const double* __restrict__ R, 
   }
 }
 
-// grid (ng, ceil(K / 256)): thread k sums the groups of column i assigned
-// to centroid k, rows in increasing order.  GS as for the E-step (the loops
-// over the group are unrolled to a compile-time bound so that the sums stay
-// in registers).
+// grid (ng, ceil(K / 256)), 1024 threads: the groups of column i assigned
+// to centroid k are summed by four threads, quarter q of every chunk of
+// 1024 rows each (rows in increasing order within a quarter), and the four
+// partial sums are added in quarter order.  GS as for the E-step (loops
+// over the group unrolled to a compile-time bound so that the sums stay in
+// registers).
 template <int GS>
-__global__ __launch_bounds__(256) void oaem_msums(const double* __restrict__ R, int m, int n,
-                                                  int g_rt, const int32_t* __restrict__ a,
-                                                  int K, double* __restrict__ S,
-                                                  int32_t* __restrict__ cnt) {
+__global__ __launch_bounds__(1024) void oaem_msums(const double* __restrict__ R, int m, int n,
+                                                   int g_rt, const int32_t* __restrict__ a,
+                                                   int K, double* __restrict__ S,
+                                                   int32_t* __restrict__ cnt) {
   constexpr int GM = GS > 0 ? GS : kMaxG;
+  constexpr int CH = 1024;
   const int g = GS > 0 ? GS : g_rt;
-  __shared__ int32_t ac[256];
-  __shared__ double rc[256 * GM];
-  const int i = blockIdx.x, ng = n / g;
-  const int k = blockIdx.y * 256 + threadIdx.x;
+  __shared__ int32_t ac[CH];
+  __shared__ double rc[CH * GM];          // row groups; afterwards the quarter partials
+  __shared__ int32_t pc[CH];
+  const int ng = n / g;
+  // workgroup b runs on XCD b % 8: give each XCD a contiguous range of
+  // columns, so the lines of assignments (32 columns each) and of R (two
+  // columns of 8) are shared in that XCD's L2
+  const int per = (ng + 7) / 8;
+  const int i = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (i >= ng) return;
+  const int lane_k = threadIdx.x & 255, qtr = threadIdx.x >> 8;
+  const int k = blockIdx.y * 256 + lane_k;
   double s[GM];
 #pragma unroll
   for (int e = 0; e < GM; ++e) s[e] = 0.0;
   int c = 0;
-  for (int r0 = 0; r0 < m; r0 += 256) {
+  for (int r0 = 0; r0 < m; r0 += CH) {
     const int rr = r0 + threadIdx.x;
     ac[threadIdx.x] = rr < m ? a[(int64_t)rr * ng + i] : -1;
 #pragma unroll
     for (int e = 0; e < GM; ++e) {
-      // row rr's group, stored at rc[threadIdx.x GM + e]
       const double x = rr < m && e < g ? R[(int64_t)rr * n + i * g + e] : 0.0;
       rc[threadIdx.x * GM + e] = x;
     }
     __syncthreads();
     // rows past m hold -1 and never match; eight assignments per pass
-    for (int t0 = 0; t0 < 256; t0 += 8) {
+    const int t_lo = qtr * 256;
+    for (int t0 = t_lo; t0 < t_lo + 256; t0 += 8) {
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = ac[t0 + u];
@@ -223,20 +235,35 @@ __global__ __launch_bounds__(256) void oaem_msums(const double* __restrict__ R, 
     }
     __syncthreads();
   }
-  if (k < K) {
+  // quarter partials through LDS, added in quarter order
+#pragma unroll
+  for (int e = 0; e < GM; ++e) rc[(qtr * 256 + lane_k) * GM + e] = s[e];
+  pc[qtr * 256 + lane_k] = c;
+  __syncthreads();
+  if (qtr == 0 && k < K) {
+    double tot[GM];
+    int ct = 0;
+#pragma unroll
+    for (int e = 0; e < GM; ++e) tot[e] = 0.0;
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < GM; ++e) tot[e] += rc[(q * 256 + lane_k) * GM + e];
+      ct += pc[q * 256 + lane_k];
+    }
     const int64_t o = (int64_t)i * K + k;
-    cnt[o] = c;
+    cnt[o] = ct;
 #pragma unroll
     for (int e = 0; e < GM; ++e)
-      if (e < g) S[o * g + e] = s[e];
+      if (e < g) S[o * g + e] = tot[e];
   }
 }
 
 // grid K: centroid k <- solve (sum_i cnt_ik H_i) c = sum_i H_i S_ik, or
 // unchanged when no group is assigned to it.  The sums over the group
 // columns i are split into fixed slices (i = s, s + nslices, ...) over all
-// 256 threads and the slices are added in order, so the result does not
-// depend on timing.
+// 256 threads, each slice with four interleaved accumulators, and
+// everything is combined in a fixed order, so the result does not depend
+// on timing.
 __global__ __launch_bounds__(256) void oaem_msolve(const double* __restrict__ Hb, int ng, int g,
                                                    const double* __restrict__ S,
                                                    const int32_t* __restrict__ cnt, int K,
@@ -252,11 +279,21 @@ __global__ __launch_bounds__(256) void oaem_msolve(const double* __restrict__ Hb
   {
     const int ns = 256 / gg;
     const int e = t % gg, sl = t / gg;
-    double acc = 0.0;
-    if (sl < ns)
-      for (int i = sl; i < ng; i += ns)
-        acc += (double)cnt[(int64_t)i * K + k] * Hb[(int64_t)i * gg + e];
-    part[t] = acc;
+    // four interleaved accumulators (i, i + ns, i + 2 ns, i + 3 ns) keep four
+    // iterations' loads in flight; they are combined in a fixed order
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (sl < ns) {
+      int i = sl;
+      for (; i + 3 * ns < ng; i += 4 * ns) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ii = i + q * ns;
+          acc[q] += (double)cnt[(int64_t)ii * K + k] * Hb[(int64_t)ii * gg + e];
+        }
+      }
+      for (; i < ng; i += ns) acc[0] += (double)cnt[(int64_t)i * K + k] * Hb[(int64_t)i * gg + e];
+    }
+    part[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
     if (t < gg) {
       double sum = 0.0;
@@ -269,16 +306,29 @@ __global__ __launch_bounds__(256) void oaem_msolve(const double* __restrict__ Hb
   {
     const int ns = 256 / g;
     const int u = t % g, sl = t / g;
-    double acc = 0.0;
-    if (sl < ns)
-      for (int i = sl; i < ng; i += ns) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (sl < ns) {
+      int i = sl;
+      for (; i + 3 * ns < ng; i += 4 * ns) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ii = i + q * ns;
+          const double* hr = Hb + (int64_t)ii * gg + u * g;
+          const double* sv = S + ((int64_t)ii * K + k) * g;
+          double d = 0.0;
+          for (int v = 0; v < g; ++v) d += hr[v] * sv[v];
+          acc[q] += d;
+        }
+      }
+      for (; i < ng; i += ns) {
         const double* hr = Hb + (int64_t)i * gg + u * g;
         const double* sv = S + ((int64_t)i * K + k) * g;
         double d = 0.0;
         for (int v = 0; v < g; ++v) d += hr[v] * sv[v];
-        acc += d;
+        acc[0] += d;
       }
-    part[t] = acc;
+    }
+    part[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     if (t == 0) {
       int64_t c = 0;
       for (int i = 0; i < ng; ++i) c += cnt[(int64_t)i * K + k];
@@ -417,10 +467,11 @@ hipError_t launch_oaem(const void* W, int32_t wdtype, int64_t m64, int64_t n64, 
         oaem_estep<0, 1><<<dim3((unsigned)ng, (unsigned)((m + 255) / 256)), 256, lds, st>>>(
             w.R, m, n, g, w.Hb, C, w.Q, K, a);
       if (it < iters) {
+        const unsigned gx = (unsigned)(8 * ((ng + 7) / 8));   // whole XCD ranges
         if (g == 8)
-          oaem_msums<8><<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
+          oaem_msums<8><<<dim3(gx, kb), 1024, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
         else
-          oaem_msums<0><<<dim3((unsigned)ng, kb), 256, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
+          oaem_msums<0><<<dim3(gx, kb), 1024, 0, st>>>(w.R, m, n, g, a, K, w.S, w.cnt);
         oaem_msolve<<<(unsigned)K, 256, 0, st>>>(w.Hb, ng, g, w.S, w.cnt, K, C);
       }
       e = hipGetLastError();
