@@ -353,6 +353,19 @@ def test_min_pivot_on_a_diagonal_matrix_sorts_ascending():
     np.testing.assert_array_equal(O.order_permutation("min_pivot", 5, H), pi)
 
 
+def test_min_pivot_handworked_3x3():
+    """tests/golden/handworked_min_pivot_3x3.txt: the order, the pivots and
+    the lower trace than the natural order, worked on paper."""
+    g = load("handworked_min_pivot_3x3.txt")
+    pi, piv, info = O.min_pivot_order(g["H"])
+    assert info == 0
+    np.testing.assert_array_equal(pi, g["order"].astype(np.int64))
+    np.testing.assert_allclose(piv, g["pivots"], rtol=1e-15)
+    L = O.cholesky_lower(g["H"])[0]
+    np.testing.assert_allclose(np.diag(L) ** 2, g["natural_pivots"], rtol=1e-15)
+    assert piv.sum() < g["natural_pivots"].sum()
+
+
 def test_min_pivot_matches_greedy_determinant_ratios():
     """Brute force: the Schur-complement diagonal of candidate i after the
     chosen set S is det H[S+i] / det H[S] (a ratio of principal minors), so
@@ -633,6 +646,17 @@ def _kmeans(X, C0, iters):
     km = KMeans(n_clusters=len(C0), init=C0, n_init=1, max_iter=iters, algorithm="lloyd",
                 tol=0.0).fit(X)
     return km.cluster_centers_, km.labels_
+
+
+def test_oaem_handworked_scalar_round():
+    """tests/golden/handworked_oaem_scalar.txt: one E/M round and the final
+    E-step with scalar groups, worked on paper."""
+    gd = load("handworked_oaem_scalar.txt")
+    books, codes, objs, R = O.oaem_init(gd["W"], gd["H"], 1,
+                                        gd["seeds"].astype(np.int64)[None], iters=1)
+    np.testing.assert_allclose(books[0][:, 0], gd["codebook"], rtol=1e-15)
+    np.testing.assert_array_equal(codes[0], gd["codes"].astype(np.int64))
+    assert objs[0] == pytest.approx(gd["objective"], rel=1e-15)
 
 
 def test_oaem_identity_metric_is_lloyd_kmeans():
