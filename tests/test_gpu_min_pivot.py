@@ -145,6 +145,35 @@ def test_min_pivot_layer(cfg_id, m, n, ntok):
     assert ref["D"].sum() <= nat["D"].sum()
 
 
+def test_min_pivot_spectral_layer_f64():
+    """The spectral layer (H given, damp 0, column spacing c / l_kk, fp64
+    factor and sweep) in min-pivot order: the spacings follow the permuted
+    factor, so this checks the order end to end in the other precision."""
+    cfg = synth.config(5).resized(m=48, n=512)
+    lay = synth.make_layer(cfg)
+    W, _, H = upload(lay)
+    c = 0.001
+    g = P.Grid("colspacing", 0, 0, c)
+    out = P.quant_layer(W, H=H, grid=g, order="min_pivot", damp=cfg.damp, block=cfg.block,
+                        prec="f64")
+    torch.cuda.synchronize()
+    r = P.read_result(out["result"])
+    assert r["info"] == 0
+    perm, _, _ = P.min_pivot_order(H, damp=cfg.damp)
+    torch.cuda.synchronize()
+    pg = to_np(perm).astype(np.int64)
+    Hg = to_np(H).astype(np.float64)
+    Hd, _, _, _ = O.fix_dead_and_damp(Hg, np.zeros((1, cfg.n)), cfg.damp)
+    _check_valid(Hd, pg)
+    ref = O.quant_layer(lay.W64(), H=Hg, grid_kind="colspacing", c=c, damp=cfg.damp,
+                        order="perm", perm=pg)
+    np.testing.assert_allclose(to_np(out["scales"]).astype(np.float64), ref["scales"],
+                               rtol=1e-6)
+    check_codes(to_np(out["codes"]), ref, None, label="min_pivot f64")
+    check_loss(r["loss"], ref["loss"], "min_pivot f64")
+    print(f"[min-pivot] spectral f64: trace D {ref['D'].sum():.6g}", flush=True)
+
+
 def test_min_pivot_failures():
     n = 64
     # all ones: the first pivot (column 0) leaves a zero Schur complement

@@ -147,6 +147,12 @@ def test_oaem_edges():
     C0 = W64[0, 5 * g:6 * g][None]                 # group 5 of row 0 (8 groups a row)
     ref = O.oaem_mstep(W64, Hb, np.zeros((20, 8), dtype=np.int64), C0)
     np.testing.assert_allclose(to_np(books)[0], ref, rtol=1e-10)
+    # W as a view with a row stride above n: the same result bitwise
+    wide = torch.zeros((20, 32 + 24), dtype=W.dtype, device="cuda")
+    wide[:, :32] = W
+    b2, c2, _, _ = P.oaem_init(wide[:, :32], H, seeds, g=g, iters=1, damp=cfg.damp)
+    torch.cuda.synchronize()
+    assert torch.equal(b2, books) and torch.equal(c2, codes)
     # a seed outside the groups is reported
     bad = torch.tensor([[0, 20 * 8]], dtype=torch.int64, device="cuda")
     _, _, _, res = P.oaem_init(W, H, bad, g=g, iters=1, damp=cfg.damp)
