@@ -78,6 +78,28 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_tiles256_qproj_4096x4096_tra
 KERNEL_SOURCE = os.path.join(ROOT, "post_weight_quantization_19_amd", "csrc", "hessian.hip")
 
 
+def input_hashes(lay):
+    """sha256 of the generated inputs as stored on the host (bf16 bits of W
+    and X, or the float32 H), so that runs can be checked to use the same
+    data."""
+    import hashlib
+
+    def h(a):
+        return hashlib.sha256(a.tobytes()).hexdigest()
+    out = {}
+    if lay.W_bits is not None:
+        out["W_bf16"] = h(lay.W_bits)
+    elif lay.W is not None:
+        out["W_f32"] = h(lay.W)
+    if lay.X_bits is not None:
+        out["X_bf16"] = h(lay.X_bits)
+    elif lay.X is not None:
+        out["X_f32"] = h(lay.X)
+    if lay.H is not None:
+        out["H_f32"] = h(lay.H)
+    return out
+
+
 def measured_traffic(x_layout):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, or None if the kernel source has changed since
@@ -213,6 +235,7 @@ def ssqr_bench(args):
     print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
           flush=True)
     lay = synth.make_layer(cfg, keep_x_f32=False)
+    hashes = input_hashes(lay)
     dev = torch.device("cuda:0")
     W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -251,7 +274,7 @@ def ssqr_bench(args):
         "data": "synthetic (seeded)",
         "config": {"workload": f"{cfg.name} (SSQR, outlier density {args.ssqr}, "
                                f"{args.ssqr_iters} halvings of log2 kappa in [-8, 0])",
-                   "m": m, "n": n, "ntok": N, "x_layout": xl},
+                   "m": m, "n": n, "ntok": N, "x_layout": xl, "input_sha256": hashes},
         "ssqr": {"kappa": out["kappa"], "n_outliers": out["n_outliers"],
                  "density": out["n_outliers"] / (m * n),
                  "quantizations_per_call": f"{nq} or {nq + 1}",
@@ -285,6 +308,7 @@ def oaem_bench(args):
     print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
           flush=True)
     lay = synth.make_layer(cfg, keep_x_f32=False)
+    hashes = input_hashes(lay)
     dev = torch.device("cuda:0")
     W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -330,7 +354,7 @@ def oaem_bench(args):
         "data": "synthetic (seeded)",
         "config": {"workload": f"{cfg.name} (OA-EM: groups of {g}, K {K}, M {M} codebooks, "
                                f"{T} EM rounds each, seeded initial groups)",
-                   "m": m, "n": n, "ntok": N, "x_layout": xl},
+                   "m": m, "n": n, "ntok": N, "x_layout": xl, "input_sha256": hashes},
         "oaem": {"objective_per_stage": o, "info": P.read_result(res)["info"]},
         "roofline": {"bound": "alu (fp64 vector FMA)",
                      "kernel": "oaem_estep (+ its damping, load and norm table, timed as one "
@@ -371,6 +395,7 @@ def main():
     print(f"[bench] generating workload {cfg.name} m={m} n={n} ntok={N}", file=sys.stderr,
           flush=True)
     lay = synth.make_layer(cfg, keep_x_f32=False)
+    hashes = input_hashes(lay)
     dev = torch.device("cuda:0")
     W = torch.from_numpy(lay.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     has_x = lay.X_bits is not None
@@ -522,7 +547,7 @@ def main():
                                f"block {cfg.block}, damp {cfg.damp}"
                                + ("" if order == "back_to_front" else f", order {order}"),
                    "m": m, "n": n, "ntok": N, "x_layout": xl if has_x else None,
-                   "layer_quantize_time_s": dt},
+                   "layer_quantize_time_s": dt, "input_sha256": hashes},
         "roofline": roofline,
         "stages_ms": {"hessian_accum": t_hess, "damp_cholesky": t_chol,
                       "sweep_and_update": t_sweep, "lazy_updates_in_step": upd_ms,
