@@ -1,14 +1,16 @@
-"""Benchmark: quantize one q_proj-shaped layer end to end on one MI355X.
+"""Benchmark: quantize one down_proj-shaped layer end to end on one MI355X.
 
 A step is one whole quant_layer call on device-resident inputs: H = 2 X X^T
 (bf16 MFMA SYRK), dead features + damping, blocked Cholesky, grid steps,
 the back-to-front nearest-plane sweep with lazy MFMA block updates, and the
-loss/bound reduction.  Default workload (--config 2): W 4096 x 4096 bf16,
-X 4096 x 131072 bf16 (Student-t, 8 outlier channels x20) stored token-major
-(131072 rows of 4096 channels; --x-layout channels stores it 4096 x 131072),
-asymmetric 4-bit, group 128, block 128, damp 0.01 -- synthetic, seeded.  --config 3 / 4 time
-the up_proj / down_proj layers, --config 5 the spectral layer (H given, fp64
-factor and sweep, no SYRK: `roofline` is null there).
+loss/bound reduction.  Default workload (--config 4), the largest layer with
+every stage: W 4096 x 14336 bf16 N(0, 0.01^2), X 14336 x 262144 bf16
+(Laplace(0, 1) times LogNormal(0, 1) channel scales) stored token-major
+(262144 rows of 14336 channels; --x-layout channels stores it
+14336 x 262144), symmetric 2-bit, group 64, block 128, damp 0.01 --
+synthetic, seeded.  --config 2 / 3 time the q_proj / up_proj layers,
+--config 5 the spectral layer (H given, fp64 factor and sweep, no SYRK:
+`roofline` is null there).
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the Hessian
 SYRK tiles): algorithmic flops n(n+1)N per launch over its average duration,
@@ -46,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload table entry")
+    ap.add_argument("--config", type=int, default=4, help="workload table entry")
     ap.add_argument("--x-layout", choices=["channels", "tokens"], default="tokens",
                     help="storage of the activations: token-major [ntok, n] (one row per "
                          "token, as a layer's inputs are captured; the default) or [n, ntok]")
@@ -66,16 +68,22 @@ def parse():
     ap.add_argument("--oaem-rounds", type=int, default=10)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the achievable-peak probe (MFMA and copy microbenchmarks)")
-    ap.add_argument("--cpu-token-fraction", type=int, default=8,
-                    help="oracle Hessian is timed on 1/k of the tokens, scaled by k")
+    ap.add_argument("--cpu-token-fraction", type=int, default=0,
+                    help="oracle Hessian is timed on 1/k of the tokens, scaled by k "
+                         "(0: the smallest k that keeps the sample near 2e12 flop)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference kernel "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_tiles256_qproj_4096x4096_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "post_weight_quantization_19_amd", "csrc", "hessian.hip")
+
+
+def traffic_file(cfg):
+    """Committed rocprofv3 counter summary of the SYRK tiles for a layer."""
+    tag = cfg.name.replace("_", "")
+    return os.path.join(ROOT, "profiles", f"syrk_tiles256_{tag}_{cfg.m}x{cfg.n}_traffic.json")
 
 
 def input_hashes(lay):
@@ -100,13 +108,13 @@ def input_hashes(lay):
     return out
 
 
-def measured_traffic(x_layout):
+def measured_traffic(cfg, x_layout):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, or None if the kernel source has changed since
     the counters were taken or they were taken for the other X layout."""
     import hashlib
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(cfg)) as f:
             t = json.load(f)
         with open(KERNEL_SOURCE, "rb") as f:
             h = hashlib.sha256(f.read()).hexdigest()
@@ -125,16 +133,34 @@ def spacing_constant(cfg):
         return float(json.load(f)["c"])
 
 
+def blas_threads():
+    """(vendor string, threads) of the BLAS numpy calls, from threadpoolctl."""
+    try:
+        from threadpoolctl import threadpool_info
+        b = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+    except Exception:       # threadpoolctl missing or failing: unknown
+        return "unknown", None
+    if not b:
+        return "unknown", None
+    return (", ".join(f"{d.get('internal_api')} {d.get('version')}" for d in b),
+            max(int(d.get("num_threads") or 0) for d in b))
+
+
 def cpu_baseline(lay, cfg, frac):
     """Time the fp64 oracle on a bounded sample and project the whole layer:
     the Hessian over 1/frac of the tokens (x frac), the full Cholesky, and
     the blocked sweep over all rows, or over a row sample (x m / rows) when
     the sweep would take more than about 10 s."""
+    import math
+
     import numpy as np
 
     import oracle as O
     import synth
-    cores = len(os.sched_getaffinity(0))
+    affinity = len(os.sched_getaffinity(0))
+    vendor, nthreads = blas_threads()
+    if frac <= 0 and lay.X_bits is not None:
+        frac = max(1, math.ceil(2.0 * cfg.n * cfg.n * cfg.ntok / 2e12))
     t_h = 0.0
     if lay.X_bits is not None:
         ntok_s = cfg.ntok // frac
@@ -163,9 +189,12 @@ def cpu_baseline(lay, cfg, frac):
     t_s = (time.perf_counter() - t0) * cfg.m / rows
     total = t_h + t_c + t_s
     return {
-        "value": cfg.m * cfg.n / total, "unit": "weights/s", "cores": cores,
-        "kind": "oracle",
-        "sample": (f"fp64 numpy/OpenBLAS oracle: {h_txt}full Cholesky; blocked sweep of "
+        "value": cfg.m * cfg.n / total, "unit": "weights/s",
+        "cores": nthreads if nthreads else affinity, "kind": "oracle",
+        "blas": vendor, "blas_threads": nthreads, "cpus_in_affinity": affinity,
+        "os_cpu_count": os.cpu_count(),
+        "sample": (f"fp64 numpy oracle ({vendor}, {nthreads} BLAS threads, {affinity} CPUs in "
+                   f"the affinity mask): {h_txt}full Cholesky; blocked sweep of "
                    f"{rows} of {cfg.m} rows (x{cfg.m / rows:.3g}); projected whole-layer "
                    f"time {total:.2f} s (H {t_h:.2f} s, chol {t_c:.2f} s, sweep {t_s:.2f} s)"),
     }
@@ -448,7 +477,7 @@ def main():
                     "kernel": "syrk_tiles256 (bf16 SYRK tiles of H = 2 X X^T)",
                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / PEAK_BF16_TFLOPS,
-                    "traffic": measured_traffic(xl) if args.config == 2 else None,
+                    "traffic": measured_traffic(cfg, xl),
                     "avg_launch_ms": t_tiles * 1e3, "launches_timed": len(tiles_ms),
                     "flops_per_launch": flops_h}
 

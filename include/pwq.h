@@ -76,18 +76,21 @@ enum { PWQ_X_TOKEN_MAJOR = 0x100 };
  *   COLSPACING : one spacing per column, alpha_k = c / l_kk of the Cholesky
  *                factor [WSIC 2]; stored code = lattice integer.
  * Steps are taken from W (after dead-feature erasure) before the sweep; a
- * zero step becomes 1.  bits in [2, 16] for SYM/ASYM; c > 0 for COLSPACING. */
+ * zero step becomes 1.  bits in [2, 16] for SYM/ASYM; c > 0 for COLSPACING.
+ * Each field belongs to one family of kinds; the other family's field must
+ * be 0 (a call that sets it is rejected with PWQ_ERR_INVALID_ARG). */
 typedef enum { PWQ_GRID_SYM = 0, PWQ_GRID_ASYM = 1, PWQ_GRID_COLSPACING = 2 } pwq_grid_kind;
 typedef struct {
-  int32_t kind;        /* pwq_grid_kind                                  */
-  int32_t bits;
-  int32_t group_size;  /* 0 = one step per row; must divide n otherwise  */
-  int32_t reserved;
-  double c;            /* COLSPACING: alpha_k = c / l_kk.  SYM / ASYM:   */
-                       /* a multiplier kappa on every step, applied after */
-                       /* the step rule (the asymmetric zero point uses   */
-                       /* the scaled step); 0 means none.  [GEOM 3: SSQR  */
-                       /* adjusts the scale]                              */
+  int32_t kind;        /* pwq_grid_kind                                   */
+  int32_t bits;        /* SYM / ASYM                                      */
+  int32_t group_size;  /* SYM / ASYM: 0 = one step per row; else divides n */
+  int32_t reserved;    /* must be 0                                       */
+  double c;            /* COLSPACING only: alpha_k = c / l_kk, finite > 0 */
+  double kappa;        /* SYM / ASYM only: a multiplier on every step,    */
+                       /* applied in float32 after the step rule (the     */
+                       /* asymmetric zero point uses the scaled step);    */
+                       /* 0 means none, else finite > 0.  [GEOM 3: SSQR   */
+                       /* adjusts the scale to a target outlier density]  */
 } pwq_grid;
 
 /* Processing order.  Position k of the permuted problem holds original
@@ -342,7 +345,8 @@ pwq_status pwq_column_entropy(const int32_t* codes, int64_t m, int64_t n, int64_
  * pwq_ssqr_quant_layer: the whole layer with the scale search.  H (from X,
  * or given), the damping and the factor are computed once; the layer is
  * then quantized as by pwq_quant_layer (back-to-front) at step multiplier
- * kappa (pwq_grid.c: steps, then the sweep), and log2 kappa is bisected in
+ * kappa (the grid's step multiplier: steps, then the sweep; the caller's
+ * grid->kappa is ignored), and log2 kappa is bisected in
  * [log2_lo, 0]: kappa = 1 is tried first (if its outlier count already
  * exceeds floor(density m n) it is kept), then 2^log2_lo (kept if it meets
  * the target), then `iters` halvings of the bracket; the result is the

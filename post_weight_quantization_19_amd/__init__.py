@@ -28,10 +28,11 @@ class Grid:
     kind: str = "sym"       # "sym" | "asym" | "colspacing"
     bits: int = 4
     group: int = 0          # 0 = one step per row
-    c: float = 0.0          # colspacing constant (alpha_k = c / l_kk)
+    c: float = 0.0          # colspacing constant (alpha_k = c / l_kk); colspacing only
+    kappa: float = 0.0      # step multiplier (0 = none); sym / asym only
 
     def c_struct(self):
-        return make_grid(self.kind, self.bits, self.group, self.c)
+        return make_grid(self.kind, self.bits, self.group, self.c, self.kappa)
 
 
 def _stream():
@@ -70,6 +71,31 @@ def _row_major(t: torch.Tensor) -> int:
     return t.stride(0)
 
 
+def _check(t: Optional[torch.Tensor], name: str, shape, dtypes):
+    """A tensor handed to the library as a raw pointer must have exactly the
+    shape, element type and (contiguous, row-major) layout the C ABI reads."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def _check_result(res: Optional[torch.Tensor]):
+    if res is None:
+        return
+    if res.dtype != torch.uint8 or res.numel() < _lib.RESULT_BYTES or not res.is_contiguous():
+        raise ValueError(f"result must be a contiguous uint8 tensor of >= {_lib.RESULT_BYTES} "
+                         "bytes (see new_result)")
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -102,6 +128,7 @@ def hessian_accum(X: torch.Tensor, H: Optional[torch.Tensor] = None,
     (``x_layout="channels"``) or [ntok, n] (``x_layout="tokens"``)."""
     _require_cuda(X, H)
     n, ntok, ldx, xdt = _x_args(X, x_layout)
+    _check(H, "H", (n, n), _F32)
     if H is None:
         H = torch.empty((n, n), dtype=torch.float32, device=X.device)
     L = lib()
@@ -116,6 +143,7 @@ def damp_cholesky(H: torch.Tensor, damp: float = 0.01, prec: str = "f32"):
     """(L, dead, result) for H_d = H' + lambda I (lower factor)."""
     _require_cuda(H)
     n = H.shape[0]
+    _check(H, "H", (n, n), _F32)
     L_ = lib()
     Lt = torch.empty((n, n), dtype=_tdt(prec), device=H.device)
     dead = torch.empty(n, dtype=torch.int32, device=H.device)
@@ -178,6 +206,9 @@ def grid_steps(W: torch.Tensor, grid: Grid, dead: Optional[torch.Tensor] = None)
     """(scales [m, n/G], zeros [m, n/G] or None) for SYM / ASYM grids."""
     _require_cuda(W, dead)
     m, n = W.shape
+    _check(dead, "dead", (n,), _I32)
+    if grid.group and n % grid.group:
+        raise ValueError(f"group {grid.group} does not divide n = {n}")
     G = grid.group or n
     scales = torch.empty((m, n // G), dtype=torch.float32, device=W.device)
     zeros = (torch.empty((m, n // G), dtype=torch.int32, device=W.device)
@@ -192,13 +223,22 @@ def babai_sweep(W: torch.Tensor, L: torch.Tensor, grid: Grid, scales=None, zeros
                 dead=None, block: int = 128, result: Optional[torch.Tensor] = None):
     """Nearest-plane sweep given a factor L (natural order).  Returns
     (codes, scales, result)."""
-    _require_cuda(W, L)
+    _require_cuda(W, L, scales, zeros, dead)
     m, n = W.shape
+    _check(L, "L", (n, n), (torch.float32, torch.float64))
     prec = "f64" if L.dtype == torch.float64 else "f32"
+    _check(dead, "dead", (n,), _I32)
+    _check_result(result)
     if grid.kind == "colspacing":
         scales = torch.empty(n, dtype=torch.float32, device=W.device)
     elif scales is None:
         raise ValueError("SYM/ASYM sweeps need scales (see grid_steps)")
+    else:
+        if grid.group and n % grid.group:
+            raise ValueError(f"group {grid.group} does not divide n = {n}")
+        ng = n // (grid.group or n)
+        _check(scales, "scales", (m, ng), _F32)
+        _check(zeros, "zeros", (m, ng), _I32)
     codes = torch.empty((m, n), dtype=torch.int32, device=W.device)
     res = new_result(W.device) if result is None else result
     L_ = lib()
@@ -227,7 +267,7 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
     """quant_layer(W, X or H, grid, order, damp) -> dict(codes, scales, zeros,
     result[, H, L]).  ``out`` may pass preallocated outputs (same keys);
     ``x_layout`` as for hessian_accum."""
-    _require_cuda(W, X, H, perm)
+    _require_cuda(W, X, H, perm, workspace)
     m, n = W.shape
     dev = W.device
     ntok, ldx, xdt = 0, 0, 0
@@ -235,7 +275,23 @@ def quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
         nx, ntok, ldx, xdt = _x_args(X, x_layout)
         if nx != n:
             raise ValueError(f"X has {nx} channels, W has {n} columns")
+    _check(H, "H", (n, n), _F32)
+    _check(perm, "perm", (n,), _I32)
+    if grid.kind != "colspacing" and grid.group and n % grid.group:
+        raise ValueError(f"group {grid.group} does not divide n = {n}")
     G = n if grid.kind == "colspacing" else (grid.group or n)
+    for k, t in (out or {}).items():
+        _require_cuda(t)
+    if out:
+        ng = n // G
+        _check(out.get("codes"), "out['codes']", (m, n), _I32)
+        _check(out.get("scales"), "out['scales']",
+               (n,) if grid.kind == "colspacing" else (m, ng), _F32)
+        if grid.kind == "asym":
+            _check(out.get("zeros"), "out['zeros']", (m, ng), _I32)
+        _check_result(out.get("result"))
+        _check(out.get("H"), "out['H']", (n, n), _F32)
+        _check(out.get("L"), "out['L']", (n, n), (_tdt(prec),))
     o = dict(out or {})
     if "codes" not in o:
         o["codes"] = torch.empty((m, n), dtype=torch.int32, device=dev)
@@ -333,7 +389,14 @@ def overflow_entries(codes: torch.Tensor, scales: torch.Tensor, grid: Grid,
     (rows, cols, vals, count) -- the first min(count, max_out) entries of the
     (row, column)-sorted list, and the device int64 count."""
     _require_cuda(codes, scales, zeros)
+    if codes.dtype != torch.int32:
+        raise TypeError("codes must be int32")
     m, n = codes.shape
+    if grid.group and n % grid.group:
+        raise ValueError(f"group {grid.group} does not divide n = {n}")
+    ng = n // (grid.group or n)
+    _check(scales, "scales", (m, ng), _F32)
+    _check(zeros, "zeros", (m, ng), _I32)
     ldc = _row_major(codes) if m > 0 else n
     cap = m * n if max_out is None else int(max_out)
     dev = codes.device
@@ -369,6 +432,9 @@ def ssqr_quant_layer(W: torch.Tensor, X: Optional[torch.Tensor] = None,
         nx, ntok, ldx, xdt = _x_args(X, x_layout)
         if nx != n:
             raise ValueError(f"X has {nx} channels, W has {n} columns")
+    _check(H, "H", (n, n), _F32)
+    if grid.group and n % grid.group:
+        raise ValueError(f"group {grid.group} does not divide n = {n}")
     G = grid.group or n
     cap = m * n if max_outliers is None else int(max_outliers)
     o = {"codes": torch.empty((m, n), dtype=torch.int32, device=dev),

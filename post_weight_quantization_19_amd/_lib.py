@@ -40,7 +40,7 @@ TIMED_KERNELS = {"hessian_tiles": PWQ_TIMER_HESSIAN_TILES, "lazy_update": PWQ_TI
 class PwqGrid(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("c", ctypes.c_double)]
+                ("c", ctypes.c_double), ("kappa", ctypes.c_double)]
 
 
 RESULT_BYTES = 64          # sizeof(pwq_result) = 56, padded
@@ -117,8 +117,8 @@ def check(status):
         raise PwqError(L.pwq_status_string(status).decode(), L.pwq_last_error().decode())
 
 
-def make_grid(kind="sym", bits=4, group=0, c=0.0):
-    return PwqGrid(GRID_KINDS[kind], int(bits), int(group), 0, float(c))
+def make_grid(kind="sym", bits=4, group=0, c=0.0, kappa=0.0):
+    return PwqGrid(GRID_KINDS[kind], int(bits), int(group), 0, float(c), float(kappa))
 
 
 def parse_result(raw: bytes):

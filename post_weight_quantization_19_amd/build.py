@@ -20,17 +20,34 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpwq.so; returns the library path."""
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-result", "-o", LIB + ".tmp"]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
+OBJDIR = os.path.join(HERE, "_build")
+
+
+def _run(cmd, what):
     r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in (r.stderr or "").splitlines()
-                    if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
+        raise RuntimeError(f"hipcc failed ({what}):\n" + err)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (one object each, in parallel) and link
+    libpwq.so; returns the library path."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+
+    def compile_one(i):
+        return _run([hipcc(), *FLAGS, "-c", "-o", objs[i], os.path.join(CSRC, SOURCES[i])],
+                    SOURCES[i])
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        errs = list(ex.map(compile_one, range(len(SOURCES))))
+    errs.append(_run([hipcc(), *FLAGS, "-shared", "-o", LIB + ".tmp", *objs], "link"))
+    err = "\n".join(e for e in errs if e.strip())
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(LIB + ".tmp", LIB)

@@ -59,6 +59,11 @@ __global__ __launch_bounds__(256) void act_order_perm(const float* __restrict__ 
   if (i < n) perm[n - 1 - rank] = i;
 }
 
+__global__ __launch_bounds__(256) void iota_perm(int32_t* __restrict__ perm, int n) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k < n) perm[k] = k;
+}
+
 __global__ __launch_bounds__(256) void clear_i32(int32_t* __restrict__ p, int n) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k < n) p[k] = 0;
@@ -91,6 +96,11 @@ __global__ __launch_bounds__(256) void check_seen(const int32_t* __restrict__ se
 
 hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, hipStream_t st) {
   init_flags<<<1, 64, 0, st>>>(flags, res, reset_info);
+  return hipGetLastError();
+}
+
+hipError_t launch_identity_perm(int32_t* perm, int64_t n, hipStream_t st) {
+  iota_perm<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, (int)n);
   return hipGetLastError();
 }
 

@@ -73,6 +73,7 @@ pwq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 pwq_status check_grid(const pwq_grid* g, int64_t n, bool allow_colspacing) {
   if (!g) return fail(PWQ_ERR_INVALID_ARG, "grid is NULL");
+  if (g->reserved != 0) return fail(PWQ_ERR_INVALID_ARG, "grid.reserved must be 0");
   if (g->kind == PWQ_GRID_SYM || g->kind == PWQ_GRID_ASYM) {
     if (g->bits < 2 || g->bits > 16)
       return fail(PWQ_ERR_INVALID_ARG, "bits must be in [2, 16] (got %d)", g->bits);
@@ -80,14 +81,18 @@ pwq_status check_grid(const pwq_grid* g, int64_t n, bool allow_colspacing) {
     if (g->group_size > 0 && n % g->group_size)
       return fail(PWQ_ERR_INVALID_ARG, "group_size %d does not divide n = %lld", g->group_size,
                   (long long)n);
-    if (!(g->c >= 0.0) || !(g->c < 1e30))
-      return fail(PWQ_ERR_INVALID_ARG, "the step multiplier c must be 0 (none) or finite > 0");
+    if (g->c != 0.0)
+      return fail(PWQ_ERR_INVALID_ARG, "grid.c is the COLSPACING constant: 0 for SYM / ASYM");
+    if (!(g->kappa >= 0.0) || !(g->kappa < 1e30))
+      return fail(PWQ_ERR_INVALID_ARG, "the step multiplier kappa must be 0 (none) or finite > 0");
     return PWQ_OK;
   }
   if (g->kind == PWQ_GRID_COLSPACING) {
     if (!allow_colspacing) return fail(PWQ_ERR_INVALID_ARG, "COLSPACING steps need the factor");
     if (!(g->c > 0.0) || !(g->c < 1e300))
       return fail(PWQ_ERR_INVALID_ARG, "COLSPACING needs a finite c > 0");
+    if (g->kappa != 0.0)
+      return fail(PWQ_ERR_INVALID_ARG, "grid.kappa is for SYM / ASYM: 0 for COLSPACING");
     return PWQ_OK;
   }
   return fail(PWQ_ERR_INVALID_ARG, "unknown grid kind %d", g->kind);
@@ -95,8 +100,8 @@ pwq_status check_grid(const pwq_grid* g, int64_t n, bool allow_colspacing) {
 
 int group_of(const pwq_grid* g, int64_t n) { return g->group_size > 0 ? g->group_size : (int)n; }
 
-// SYM / ASYM: c is a multiplier on every step (0 means none).
-float step_multiplier(const pwq_grid* g) { return g->c > 0.0 ? (float)g->c : 1.0f; }
+// SYM / ASYM: kappa is a multiplier on every step (0 means none).
+float step_multiplier(const pwq_grid* g) { return g->kappa > 0.0 ? (float)g->kappa : 1.0f; }
 
 // ---- workspace layouts (shared by sizing and carving)
 
@@ -422,6 +427,9 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   if (e == hipSuccess && mp) {
     // the order is taken on the damped matrix: lambda first
     e = launch_damp_lambda(Hm, n, damp, w.dead, result, w.flags, w.lam, st);
+    // a failing pivot leaves the positions after it unwritten: start from
+    // the identity so the map never holds workspace garbage
+    if (e == hipSuccess) e = launch_identity_perm(w.perm, n, st);
     if (e == hipSuccess)
       e = launch_min_pivot(Hm, n, w.lam, w.mp, w.perm, nullptr, w.flags, result, st);
     colmap = w.perm;
@@ -709,7 +717,7 @@ pwq_status pwq_ssqr_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_
   double last = -1.0;
   auto evaluate = [&](double k, int64_t* cnt) -> pwq_status {
     pwq_grid g = *grid;
-    g.c = k;
+    g.kappa = k;
     pwq_status q = pwq_grid_steps(W, wdtype, m, n, ldw, dead, &g, scales, zeros, stream);
     if (q != PWQ_OK) return q;
     q = pwq_babai_sweep(W, wdtype, m, n, ldw, L, prec, dead, &g, scales, zeros, block, codes,

@@ -104,6 +104,8 @@ hipError_t launch_sweep(const SweepLaunch& sl, hipStream_t st);
 hipError_t launch_order(int32_t order_kind, const float* H, int64_t n, const int32_t* perm_in,
                         int32_t* perm_out, int32_t* seen, pwq_result* res, DevFlags* flags,
                         hipStream_t st);
+// perm[k] = k (a valid map for every later kernel whatever happens after).
+hipError_t launch_identity_perm(int32_t* perm, int64_t n, hipStream_t st);
 hipError_t launch_init_flags(DevFlags* flags, pwq_result* res, int reset_info, hipStream_t st);
 
 // Min-pivot order (pivoted LDL^T in fp64).  Workspace: A n x n doubles,

@@ -193,6 +193,11 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int l
   typedef typename Vec16<T>::type V;
   __shared__ __attribute__((aligned(16))) T Lt[B * LP];
   __shared__ double red[4][4];
+  // After a failed factorization or an invalid permutation (info != 0) the
+  // column map may hold anything: no index is formed from it.  The flag is
+  // the same for the whole launch, so every workgroup leaves before its
+  // first barrier.
+  if (a.flags->info != 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane & 15;

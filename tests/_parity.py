@@ -35,18 +35,19 @@ def lattice_ints(codes, zeros, n):
     return Z
 
 
-def check_codes(codes_gpu, ref, zeros_gpu=None, rows=None, label=""):
+def check_codes(codes_gpu, ref, zeros_gpu=None, label=""):
     """Compare GPU codes with an oracle result dict ``ref`` (from
-    oracle.quant_layer).  ``rows`` restricts to a row sample.  Returns a dict
-    of statistics; raises AssertionError on failure."""
+    oracle.quant_layer, or the same keys for a row sample: codes, pi, Sp, W0
+    and L).  Returns a dict of statistics; raises AssertionError on
+    failure."""
     codes_gpu = np.asarray(codes_gpu, np.int64)
-    ref_codes = ref["codes"] if rows is None else ref["codes"]
+    ref_codes = ref["codes"]
     same = float(np.mean(codes_gpu == ref_codes))
     n = codes_gpu.shape[1]
     Zg = lattice_ints(codes_gpu, zeros_gpu, n)
     pi = ref["pi"]
     Sp = ref["Sp"]
-    W0 = ref["W0"] if rows is None else ref["W0"]
+    W0 = ref["W0"]
     S = np.empty_like(Sp)
     S[:, pi] = Sp
     Dp = (W0 - S * Zg)[:, pi]

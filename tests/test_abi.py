@@ -69,8 +69,8 @@ def test_cholesky_validation():
     assert L.pwq_damp_cholesky(FAKE, 8, 0.01, 0, FAKE, None, FAKE, None, 0, None) == WS
 
 
-def _grid(kind=0, bits=4, group=0, c=0.0):
-    return B.PwqGrid(kind, bits, group, 0, c)
+def _grid(kind=0, bits=4, group=0, c=0.0, kappa=0.0):
+    return B.PwqGrid(kind, bits, group, 0, c, kappa)
 
 
 def test_steps_and_sweep_validation():
@@ -252,8 +252,23 @@ def test_ssqr_validation():
         L.pwq_ssqr_workspace_size(64, 128, 0, 0, 32, 0)
 
 
-def test_grid_step_multiplier_validation():
+def test_grid_fields_validation():
+    """kappa (the SYM / ASYM step multiplier) and c (the COLSPACING
+    constant) are separate fields; each kind rejects the other's field."""
     L = B.lib()
+    assert ctypes.sizeof(B.PwqGrid) == 32
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert L.pwq_grid_steps(FAKE, 1, 4, 8, 8, None, _grid(0, 4, 0, kappa=bad), FAKE, None,
+                                None) == INVALID
+    # c belongs to COLSPACING: rejected for SYM / ASYM
+    assert L.pwq_grid_steps(FAKE, 1, 4, 8, 8, None, _grid(0, 4, 0, c=0.5), FAKE, None,
+                            None) == INVALID
+    assert L.pwq_grid_steps(FAKE, 1, 4, 8, 8, None, _grid(1, 4, 0, c=0.5), FAKE, FAKE,
+                            None) == INVALID
     g = _grid(0, 4, 0)
-    g.c = -1.0
+    g.reserved = 1
     assert L.pwq_grid_steps(FAKE, 1, 4, 8, 8, None, g, FAKE, None, None) == INVALID
+    # kappa belongs to SYM / ASYM: rejected for COLSPACING
+    args = (FAKE, 0, 4, 128, 128, FAKE, 0, None)
+    assert L.pwq_babai_sweep(*args, _grid(2, 0, 0, c=1.0, kappa=0.5), FAKE, None, 128, FAKE,
+                             FAKE, FAKE, 1 << 30, None) == INVALID

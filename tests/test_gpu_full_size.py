@@ -1,17 +1,20 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (the layer's own grid, block, damping and precision), on
-outputs the fp64 oracle can compute one by one:
+benchmark times (the layer's own grid, block, damping and precision, X
+stored token-major), on outputs the fp64 oracle can compute:
 
-  H      sampled entries 2 sum_t x_it x_jt (all from the same bf16 bits),
-         stratified into diagonal and off-diagonal samples; the stratified
-         estimate of the relative Frobenius error must be <= 1e-4
+  H      bitwise equal to the Hessian of the same X stored channel-major
+         (the two layouts feed the same operands to the same MFMAs in the
+         same order); sampled entries 2 sum_t x_it x_jt (all from the same
+         bf16 bits), stratified into diagonal and off-diagonal samples; the
+         stratified estimate of the relative Frobenius error must be <= 1e-4
   L      the oracle's fp64 Cholesky of the GPU's own H (stage-fed), whole
          matrix, relative Frobenius <= 1e-4; lambda to 1e-12
   steps  whole matrix from the oracle's float32 step rule, <= 1e-6, zero
          points exact
-  codes  a seeded sample of rows swept by the oracle (blocked form, fp64)
-         with its own factor and steps: >= 99.9% identical and every GPU
-         code a nearest rounding (|G| <= 1/2 + 1e-5)
+  codes  every row (q_proj, up_proj) or a seeded sample of 1024 rows
+         (down_proj, the spectral layer) swept by the oracle (blocked form,
+         fp64) with its own factor and steps: >= 99.9% identical and every
+         GPU code a nearest rounding (|G| <= 1/2 + 1e-5)
   losses tr(D H D^T) of the GPU's own codes for every row, against the
          GPU's reported loss (1e-3); bound (1/4) sum s^2 l_kk^2 (1e-3)
   rate   (spectral layer) mean per-column code entropy of all GPU codes at
@@ -36,7 +39,8 @@ from _parity import TOL_H, TOL_L, TOL_LOSS, TOL_STEP, check_codes, check_loss, r
 pytestmark = pytest.mark.gpu
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SAMPLE_ROWS = 64
+SAMPLE_ROWS = 1024        # rows swept by the oracle where not every row is
+ALL_ROWS = (2, 3)         # layers whose every row is compared
 SAMPLE_H = 512
 
 
@@ -99,13 +103,18 @@ def _run_x_layer(key):
     log(f"{cfg.name}: generated W {cfg.m}x{cfg.n}, X {cfg.n}x{cfg.ntok}", t0)
     W, X, _ = upload(lay)
     t0 = time.time()
-    out = P.quant_layer(W, X=X, grid=_grid(cfg), damp=cfg.damp, block=cfg.block, prec="f32",
-                        want_H=True, want_L=True)
+    Hc = P.hessian_accum(X)                 # channel-major reference H
+    Xt = X.t().contiguous()                 # the benchmark's token-major storage
+    del X
+    out = P.quant_layer(W, X=Xt, grid=_grid(cfg), damp=cfg.damp, block=cfg.block, prec="f32",
+                        want_H=True, want_L=True, x_layout="tokens")
     torch.cuda.synchronize()
     res = P.read_result(out["result"])
-    log(f"{cfg.name}: GPU quant_layer done, info {res['info']}", t0)
-    del X
+    log(f"{cfg.name}: GPU quant_layer done (X token-major), info {res['info']}", t0)
+    del Xt
     assert res["info"] == 0 and res["ndead"] == 0
+    assert torch.equal(out["H"], Hc), "token-major H differs from channel-major H"
+    del Hc
     Hg = to_np(out["H"])
     t0 = time.time()
     relH = _check_h_sampled(lay, Hg, seed=key)
@@ -135,9 +144,11 @@ def _run_x_layer(key):
         assert np.array_equal(zg, z_grp.astype(np.int64))
     S = O.expand_group_steps(s_grp, cfg.n)
 
-    # codes of a row sample, swept by the oracle with its own factor
+    # codes of every row or of a row sample, swept by the oracle with its
+    # own factor
     t0 = time.time()
-    rows = np.sort(np.random.default_rng(100 + key).choice(cfg.m, SAMPLE_ROWS, replace=False))
+    rows = (np.arange(cfg.m) if key in ALL_ROWS else
+            np.sort(np.random.default_rng(100 + key).choice(cfg.m, SAMPLE_ROWS, replace=False)))
     codes = to_np(out["codes"]).astype(np.int64)
     Zr, rho = O.nearest_plane_sweep_blocked(W0[rows], L, S[rows], cfg.block)
     ref = {"codes": Zr.astype(np.int64), "pi": np.arange(cfg.n), "Sp": S[rows],
@@ -203,7 +214,7 @@ def test_full_size_spectral_layer():
 
     t0 = time.time()
     W0 = lay.W64()
-    rows = np.sort(np.random.default_rng(105).choice(cfg.m, SAMPLE_ROWS // 2, replace=False))
+    rows = np.sort(np.random.default_rng(105).choice(cfg.m, SAMPLE_ROWS, replace=False))
     codes = to_np(out["codes"]).astype(np.int64)
     Sr = np.broadcast_to(alpha[None, :], (len(rows), cfg.n))
     Zr, _ = O.nearest_plane_sweep_blocked(W0[rows], L, Sr, cfg.block)

@@ -29,7 +29,7 @@ def test_step_multiplier(kind, bits, group):
     lay = synth.make_layer(cfg)
     W, _, _ = upload(lay)
     for kappa in (0.375, 0.0625, 1.0):
-        s, z = P.grid_steps(W, P.Grid(kind, bits, group, kappa))
+        s, z = P.grid_steps(W, P.Grid(kind, bits, group, kappa=kappa))
         torch.cuda.synchronize()
         s_o, z_o = O.grid_steps(lay.W64(), kind, bits, group, step_scale=kappa)
         assert np.array_equal(to_np(s).astype(np.float64), s_o)
