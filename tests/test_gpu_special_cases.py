@@ -114,8 +114,8 @@ def _dyadic_layer(rng, m, n, G, kind, step_log2=-6):
 
 
 @pytest.mark.parametrize("kind,G,wdt,src", [("sym", 64, "f32", "H"), ("sym", 64, "bf16", "X"),
-                                            ("asym", 128, "f32", "X"),
-                                            ("asym", 64, "bf16", "H")])
+                                            ("asym", 64, "f32", "X"),
+                                            ("asym", 32, "bf16", "H")])
 def test_lattice_points_are_fixed_points(kind, G, wdt, src):
     rng = np.random.default_rng(31)
     m, n, ntok = 96, 320, 2048
