@@ -66,9 +66,11 @@ def _require_cuda(*ts):
 
 
 def _row_major(t: torch.Tensor) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    """Row stride (elements) of a 2-D row-major tensor.  A single row may
+    carry any stride in torch; its row stride is then its length."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
         raise ValueError("expected a 2-D tensor with unit column stride")
-    return t.stride(0)
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 def _check(t: Optional[torch.Tensor], name: str, shape, dtypes):
