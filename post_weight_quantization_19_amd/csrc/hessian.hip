@@ -9,18 +9,23 @@
 // of Y = W X, whose Hessian for X = channels x tokens is 2 X X^T.
 //
 // Design (gfx950): the product is a symmetric rank-N update, so only the
-// lower-triangular 128x128 output tiles are computed.  Both operands are
-// rows of X with the token axis contiguous, which is exactly the K-major
-// operand layout of the MFMA units, so X is streamed from HBM with 16-byte
-// coalesced loads into double-buffered LDS tiles and fed to
-// v_mfma_f32_32x32x16_bf16 (bf16 inputs; the products are exact in fp32) or
-// v_mfma_f32_32x32x2f32 (fp32 inputs).  Long token axes are split (split-K)
-// to fill the 256 CUs; partial tiles are summed in a fixed order by a second
-// kernel (no float atomics, so results are bitwise reproducible), which also
-// applies the factor 2, the optional accumulation into the previous H and
-// the mirror into the upper triangle.
+// lower-triangular output tiles are computed.  bf16 X on layers of >= 1024
+// channels (16-byte aligned rows) takes syrk_tiles256: 256x256 tiles, X
+// streamed HBM -> LDS by asynchronous copies through a ten-slot ring, MFMA
+// operands read from LDS one stage ahead of the v_mfma_f32_32x32x16_bf16
+// that use them (bf16 products are exact in fp32).  Each XCD owns a
+// contiguous range of tiles; it computes whole rounds of them in one pass
+// over the token axis and splits the remainder over the token axis so its
+// 32 CUs finish together.  fp32 X, small or unaligned layers take
+// syrk_tiles: 128x128 tiles with register-staged double buffering and
+// v_mfma_f32_32x32x16_bf16 or v_mfma_f32_32x32x2f32.  Split tiles are summed
+// in a fixed order by a reduction kernel (no float atomics, so results are
+// bitwise reproducible), which also applies the factor 2, the optional
+// accumulation into the previous H and the mirror into the upper triangle.
 #include "pwq_device.h"
 #include "pwq_internal.h"
+
+#include <algorithm>
 
 namespace pwq {
 
@@ -256,305 +261,348 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
       }
 }
 
-// Large-tile variant for bf16 X: 256x256 output tiles computed by 8 waves,
-// each 64x128 (2x4 v_mfma_f32_32x32x16_bf16 accumulators), two waves per
-// SIMD so one wave's LDS waits hide behind the other's MFMAs; 32 tokens per
-// stage.  Twice the arithmetic per byte moved from L2 of a 128x128 tile.
-// X streams HBM -> LDS with global_load_lds_dwordx4 (no register staging)
-// through a ring of 5 stages (the whole 160 KB LDS), issued 4 stages ahead,
-// so about 2 us of load latency is covered.  LDS rows are 64 B (four 16-byte
-// chunks) with the chunk index XOR-swizzled by bits 2..3 of the row: 16
-// consecutive rows read at one logical chunk hit 16 distinct bank groups.
-constexpr int BL = 256;        // large tile edge
-constexpr int BKL = 32;        // tokens per stage
-constexpr int NSLOT = 5;       // LDS ring slots
-constexpr int AHEAD = 4;       // stages in flight ahead of the one computed
-// 8 waves of 64x128 (two per SIMD) measured faster than 4 waves of 128x128:
-// the second wave per SIMD hides LDS latency better than the halved LDS
-// traffic of the larger wave tile saves.
+// Large-tile kernel for bf16 X: 256x256 output tiles, 8 waves of 64x128
+// (2x4 v_mfma_f32_32x32x16_bf16 accumulators), two waves per SIMD.
+//
+// Stages of 16 tokens (one MFMA K step) stream HBM -> LDS through a ring of
+// NSLOT slots of 16 KB (the A and B panels, 8 KB each; 160 KB in all) with
+// AHEAD stages in flight.  The copies are global_load_lds_dwordx4 issued
+// from inline asm: the compiler then does not see an asynchronous LDS
+// writer, so it neither drains the copy queue before LDS reads nor reorders
+// them, and each wave waits for exactly its own copies (vmcnt) before the
+// stage barrier.  The operands of stage s + 1 are read right after that
+// barrier and before the MFMAs of stage s, so the LDS reads of one stage run
+// under the MFMAs of the previous one (two operand register sets in turn).
+// The ring is safe because the slot refilled after barrier s + 1 held stage
+// s - 2, which every wave finished reading before it arrived there.
+//
+// Token-major X (TM): a panel stage is 16 token rows of 512 B (256
+// channels); the MFMA operand (8 consecutive tokens of one channel per
+// lane) comes from two ds_read_b64_tr_b16 (within each 16-lane group, lane i
+// receives element i % 4 of the 8 bytes addressed by lane 4 j + i / 4 as
+// its element j, so source lane 4 j + a addressing token row t0 + j,
+// channels f0 + 4 a .. f0 + 4 a + 3 gives lane i tokens t0 .. t0 + 3 of
+// channel f0 + i).  The 16-byte chunks of a token row are XOR-swizzled by
+// 4 (row % 4) so the four rows a group reads fall in distinct banks.
+// Channel-major X: a panel stage is 256 channel rows of 32 B (16 tokens);
+// the operand is one ds_read_b128 of 8 tokens; the two chunks of a row are
+// swapped on rows with bit 3 set, so 16 consecutive rows at one logical
+// chunk cover all banks.  Both layouts feed the same values to the same
+// MFMAs in the same order: H is bitwise the same.
+constexpr int BL = 256;        // tile edge
+constexpr int BKS = 16;        // tokens per stage
+constexpr int PANEL = BL * BKS * 2;   // bytes of one panel stage
+constexpr int NSLOT = 10;      // LDS ring slots of two panels
+constexpr int AHEAD = 8;       // stages in flight (<= NSLOT - 2)
 constexpr int NWL = 8;         // waves per workgroup
 constexpr int NTL = 64 * NWL;  // threads
-
-__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
-
-// Token-major X: an LDS panel stage is 32 token rows of 512 B (256 channels,
-// 32 chunks of 16 B); logical chunk c of token row r is stored at chunk
-// c ^ tm_swz(r).  The MFMA operands (8 consecutive tokens of one channel per
-// lane) come from pairs of ds_read_b64_tr_b16: within each 16-lane group,
-// lane i receives element i % 4 of the 8 bytes addressed by lane
-// 4 j + i / 4 as its element j.  When source lane 4 j + a addresses token
-// row t0 + j, channels f0 + 4a .. f0 + 4a + 3, lane i therefore receives
-// tokens t0 .. t0 + 3 of channel f0 + i.  A group reads 4 consecutive token
-// rows at the same channels; the swizzle moves those rows' 32-byte pieces
-// to distinct banks.
-#ifndef PWQ_TM_SWZ
-#define PWQ_TM_SWZ 4
-#endif
-__device__ __forceinline__ int tm_swz(int r) { return PWQ_TM_SWZ * (r & 3); }
+static_assert(NSLOT * 2 * PANEL <= 160 * 1024, "ring fits the LDS");
+static_assert(AHEAD <= NSLOT - 2, "refilled slot is two stages old");
+static_assert(PANEL == NWL * 1024, "one 1 KB copy per wave and panel");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// The twelve MFMA operands of one stage (two token steps of 16; each
-// operand is 8 consecutive tokens t0 .. t0 + 7 of channel f0 + lane % 16)
-// from the LDS addresses p[0..5] of the first step: two transposed reads 4
-// token rows (2048 B) apart per operand, the second step 16 rows (8192 B)
-// further.  All 24 reads are issued together and waited for (lgkmcnt(0))
-// inside the same asm block, so every output is complete when the block
-// ends.  (Written as asm because the compiler, not seeing which LDS bytes
-// the builtin reads, would otherwise wait for every LDS copy still in
-// flight before the first read.)
-__device__ __forceinline__ void tr_operands12(const uint32_t (&p)[6], bf16x8_t (&out)[12]) {
-  v4i16 lo[12], hi[12];
+__device__ __forceinline__ int tm_swz(int r) { return 4 * (r & 3); }
+
+// Copy 16 bytes per lane from global memory into LDS at lds + 16 lane
+// (lds wave-uniform).  M0 holds the LDS base for the copy and is restored.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t keep;
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %24\n\t"
-      "ds_read_b64_tr_b16 %1, %24 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %2, %25\n\t"
-      "ds_read_b64_tr_b16 %3, %25 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %4, %26\n\t"
-      "ds_read_b64_tr_b16 %5, %26 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %6, %27\n\t"
-      "ds_read_b64_tr_b16 %7, %27 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %8, %28\n\t"
-      "ds_read_b64_tr_b16 %9, %28 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %10, %29\n\t"
-      "ds_read_b64_tr_b16 %11, %29 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %12, %24 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %13, %24 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %14, %25 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %15, %25 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %16, %26 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %17, %26 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %18, %27 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %19, %27 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %20, %28 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %21, %28 offset:10240\n\t"
-      "ds_read_b64_tr_b16 %22, %29 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %23, %29 offset:10240\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
-        "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
-        "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7]), "=&v"(lo[8]), "=&v"(hi[8]),
-        "=&v"(lo[9]), "=&v"(hi[9]), "=&v"(lo[10]), "=&v"(hi[10]), "=&v"(lo[11]), "=&v"(hi[11])
-      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5])
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(src), "s"(lds)
       : "memory");
-#pragma unroll
-  for (int t = 0; t < 12; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[t][e] = lo[t][e];
-      out[t][4 + e] = hi[t][e];
-    }
 }
 
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= v and lgkmcnt = 0.
-constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
+// Wait until at most `later` stages of this wave's copies (P instructions
+// each) are still in flight, then meet the other waves.
+template <int P>
+__device__ __forceinline__ void stage_barrier(int later) {
+  switch (later) {
+#define PWQ_SB(L) \
+    case L: asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(P * L) : "memory"); break;
+    PWQ_SB(1) PWQ_SB(2) PWQ_SB(3) PWQ_SB(4) PWQ_SB(5) PWQ_SB(6) PWQ_SB(7)
+#undef PWQ_SB
+    default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
+static_assert(AHEAD - 1 <= 7 && 2 * 7 <= 63, "stage_barrier covers every count");
 
+__device__ __forceinline__ bf16x8_t tr_operand(uint32_t a) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)a);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(a + 4 * 512));
+  bf16x8_t r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = lo[e];
+    r[4 + e] = hi[e];
+  }
+  return r;
+}
+
+// 256 tiles: the XCD x owns tiles [tb, tb + cnt) of the super-block order;
+// the first `d` of them are computed whole, the other `rem` are split.
+__host__ __device__ __forceinline__ void xcd_tiles(int64_t T, int x, int mode, int& tb, int& d,
+                                                   int& rem) {
+  tb = (int)(T * x / 8);
+  const int cnt = (int)(T * (x + 1) / 8) - tb;
+  d = mode == 2 ? cnt : (mode == 1 ? 32 * (cnt / 32) : 0);
+  rem = cnt - d;
+}
+
+template <bool TM, bool DIAG>
+__device__ __forceinline__ void syrk256_tile(const uint16_t* __restrict__ X, int n, int64_t ldx,
+                                             int r0, int c0, int64_t kbeg, int64_t kend,
+                                             lds_char* Ls, f32x16_t (&acc)[2][4]) {
+  constexpr int P = DIAG ? 1 : 2;           // copies per wave and stage
+  constexpr uint32_t BOFF = DIAG ? 0 : PANEL;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;   // rows 64 wm, columns 128 wn of the tile
+  // waves entirely above the diagonal of a diagonal tile only copy
+  const bool skip = DIAG && (64 * wm + 63 < 128 * wn);
+  const int nfull = (int)((kend - kbeg) / BKS);
+  const int nstage = (int)((kend - kbeg + BKS - 1) / BKS);
+  const uint32_t lbase = (uint32_t)(uintptr_t)Ls;
+
+  // copy sources: lane l of wave w fills LDS unit u = 64 w + l of a panel
+  const int u = 64 * wave + lane;
+  const uint16_t* ga;
+  const uint16_t* gb;
+  int64_t kstep;
+  if constexpr (TM) {
+    // token row u / 32, physical chunk u % 32 holding logical chunk
+    // c = (u % 32) ^ tm_swz(row) of 8 channels; channels past n read
+    // channels n - 8 .. n - 1 (only outputs past n, never stored, use them)
+    const int t = u >> 5, c = (u & 31) ^ tm_swz(u >> 5);
+    ga = X + (kbeg + t) * ldx + min(r0 + 8 * c, n - 8);
+    gb = X + (kbeg + t) * ldx + min(c0 + 8 * c, n - 8);
+    kstep = (int64_t)BKS * ldx;
+  } else {
+    // channel row u / 2, physical chunk u % 2 holding logical chunk
+    // (u % 2) ^ bit 3 of the row (8 tokens); rows past n read row n - 1
+    const int r = u >> 1, c = (u & 1) ^ ((r >> 3) & 1);
+    ga = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
+    gb = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
+    kstep = BKS;
+  }
+  auto issue = [&](int stage) {
+    const uint32_t dst = lbase + (uint32_t)(stage % NSLOT) * (2 * PANEL) + 1024u * wave;
+    dma16(ga + stage * kstep, dst);
+    if constexpr (!DIAG) dma16(gb + stage * kstep, dst + PANEL);
+  };
+  // operand addresses within a slot: A fragments t < 2 (rows 64 wm + 32 t),
+  // B fragments t >= 2 (columns 128 wn + 32 (t - 2))
+  uint32_t off[6];
+#pragma unroll
+  for (int t = 0; t < 6; ++t) {
+    const int f0 = t < 2 ? wm * 64 + 32 * t : wn * 128 + 32 * (t - 2);
+    const uint32_t pb = t < 2 ? 0u : BOFF;
+    if constexpr (TM) {
+      const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+      const int f = f0 + 16 * (g & 1) + 4 * a;
+      off[t] = pb + (uint32_t)((8 * (g >> 1) + j) * 512 + (((f >> 3) ^ tm_swz(j)) << 4) +
+                               2 * (f & 7));
+    } else {
+      const int row = f0 + (lane & 31), c = (lane >> 5) ^ ((row >> 3) & 1);
+      off[t] = pb + (uint32_t)(row * 32 + 16 * c);
+    }
+  }
+  auto read = [&](int slot, bf16x8_t (&o)[6]) {
+    const uint32_t sb = lbase + (uint32_t)slot * (2 * PANEL);
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+      if constexpr (TM)
+        o[t] = tr_operand(sb + off[t]);
+      else
+        o[t] = *(const bf16x8_t*)(Ls + (sb - lbase) + off[t]);
+    }
+  };
+  auto mfma = [&](const bf16x8_t (&o)[6]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[i], o[2 + j], acc[i][j], 0, 0, 0);
+  };
+  // Interleave of one stage's work: MFMA, two LDS reads, MFMA, two reads,
+  // ... (6 x), then the last two MFMAs.  Measured against "all reads, then
+  // all MFMAs": the LDS reads and the matrix pipe then run side by side
+  // (about 520 instead of 700 cycles per stage with both waves of a SIMD).
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+    }
+  };
+  // one stage in the steady state, its ring slot K = s % NSLOT known at
+  // compile time (the LDS offsets fold into the instructions): wait for
+  // stage s + 1 and meet, refill the slot of stage s - 2 with stage
+  // s + AHEAD from the running copy sources, read stage s + 1, multiply
+  // stage s
+  const uint16_t* pa = ga + AHEAD * kstep;
+  const uint16_t* pb = gb + AHEAD * kstep;
+  auto step = [&](auto KK, bf16x8_t (&cur)[6], bf16x8_t (&nxt)[6]) {
+    constexpr int K = decltype(KK)::value;
+    stage_barrier<P>(AHEAD - 2);
+    const uint32_t dst = lbase + (uint32_t)((K + AHEAD) % NSLOT) * (2 * PANEL) + 1024u * wave;
+    dma16(pa, dst);
+    if constexpr (!DIAG) dma16(pb, dst + PANEL);
+    pa += kstep;
+    pb += kstep;
+    if (!skip) {
+      read((K + 1) % NSLOT, nxt);
+      mfma(cur);
+      interleave();
+    }
+  };
+  // the same near the end of the range, where fewer copies are in flight
+  auto step_tail = [&](int s, bf16x8_t (&cur)[6], bf16x8_t (&nxt)[6]) {
+    if (s + 1 < nfull) {
+      stage_barrier<P>(min(nfull, s + AHEAD) - (s + 2));
+      if (s + AHEAD < nfull) issue(s + AHEAD);
+      if (!skip) read((s + 1) % NSLOT, nxt);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!skip) mfma(cur);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  bf16x8_t oa[6], ob[6];
+  if (nfull > 0) {
+    const int first = min(nfull, AHEAD);
+    for (int s = 0; s < first; ++s) issue(s);
+    stage_barrier<P>(first - 1);
+    if (!skip) read(0, oa);
+  }
+  int s = 0;
+  // steady state: NSLOT stages per trip, every one issuing its copy
+  static_assert(NSLOT % 2 == 0, "operand sets alternate within a trip");
+  for (; s + NSLOT + AHEAD <= nfull; s += NSLOT) {
+    static_for_up<NSLOT>([&](auto KK) {
+      constexpr int K = decltype(KK)::value;
+      if constexpr (K % 2 == 0)
+        step(KK, oa, ob);
+      else
+        step(KK, ob, oa);
+    });
+  }
+  for (; s < nfull; s += 2) {
+    step_tail(s, oa, ob);
+    if (s + 1 < nfull) step_tail(s + 1, ob, oa);
+  }
+  if (nstage > nfull) {
+    // ragged token tail: one masked stage through registers into the slot
+    // after the last full stage (every copy has landed: the last waits
+    // above left none in flight)
+    __syncthreads();
+    const uint32_t sl = (uint32_t)(nfull % NSLOT) * (2 * PANEL);
+    const int64_t k0 = kbeg + (int64_t)nfull * BKS;
+#pragma unroll
+    for (int pnl = 0; pnl < (DIAG ? 1 : 2); ++pnl) {
+      const int base = pnl ? c0 : r0;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if constexpr (TM) {
+        const int t = u >> 5, c = (u & 31) ^ tm_swz(u >> 5);
+        if (k0 + t < kend) v = *(const uint4*)(X + (k0 + t) * ldx + min(base + 8 * c, n - 8));
+      } else {
+        const int r = u >> 1, c = (u & 1) ^ ((r >> 3) & 1);
+        const uint16_t* src = X + (int64_t)min(base + r, n - 1) * ldx + k0 + 8 * c;
+        uint16_t tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = (k0 + 8 * c + e < kend) ? src[e] : (uint16_t)0;
+        __builtin_memcpy(&v, tmp, sizeof(v));
+      }
+      *(uint4*)(Ls + sl + pnl * PANEL + 16 * u) = v;
+    }
+    __syncthreads();
+    if (!skip) {
+      read(nfull % NSLOT, oa);
+      mfma(oa);
+    }
+  }
+}
+
+// Work item of workgroup blockIdx: XCD x = blockIdx % 8 (round-robin
+// dispatch) takes its items in order: its whole tiles, then its split tiles
+// split by split.  Whole tiles write H (x2, optional accumulation, lower
+// triangle and its mirror); split tiles write their partial sum.
 template <bool TM>
 __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
     const uint16_t* __restrict__ X, int n, int64_t ntok, int64_t ldx, int64_t kps,
-    int aligned, float* __restrict__ partial, float* __restrict__ H, int direct,
-    int accumulate, int ntiles, int nsplit, int per_xcd) {
-  constexpr int WR = 512 / NWL;        // rows per wave (the wave grid is (NWL/2) x 2)
-  constexpr int TI = WR / 32;          // 32-row accumulator blocks per wave
-  constexpr int CPW = 16 / NWL;        // 1 KB DMA chunks per wave per panel and stage
-  __shared__ __attribute__((aligned(16))) uint4 Ls[NSLOT][2][BL * 4];
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (item >= ntiles * nsplit) return;
-  const int split = item / ntiles, tile = item % ntiles;
+    float* __restrict__ partial, float* __restrict__ H, int accumulate, int64_t T, int nsplit,
+    int mode, int nrem) {
+  __shared__ __attribute__((aligned(16))) char Lsm[NSLOT * 2 * PANEL];
+  lds_char* Ls = (lds_char*)Lsm;
+  const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
+  int tb, d, rem;
+  xcd_tiles(T, x, mode, tb, d, rem);
+  int tile, pslot = -1;
+  int64_t kbeg = 0, kend = ntok;
+  if (l < d) {
+    tile = tb + l;
+  } else {
+    const int j = l - d;
+    if (j >= rem * nsplit) return;
+    const int split = j / rem, r = j % rem;
+    tile = tb + d + r;
+    kbeg = (int64_t)split * kps;
+    kend = min(ntok, kbeg + kps);
+    int pre = 0;
+    for (int y = 0; y < x; ++y) {
+      int a, b, c;
+      xcd_tiles(T, y, mode, a, b, c);
+      pre += c;
+    }
+    pslot = split * nrem + pre + r;
+  }
   const int nt = (n + BL - 1) / BL;
   int ti, tj;
   tile_coords(tile, nt, ti, tj);
-  const bool diag = ti == tj;
   const int r0 = ti * BL, c0 = tj * BL;
-  const int64_t kbeg = (int64_t)split * kps;
-  const int64_t kend = min(ntok, kbeg + kps);
-  const int nstage = (int)((kend - kbeg + BKL - 1) / BKL);
-  const int nfull = (int)((kend - kbeg) / BKL);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;      // rows WR wm, cols 128 wn
-  // waves entirely above the diagonal of a diagonal tile have nothing to do
-  const bool skip = diag && (WR * wm + WR - 1 < 128 * wn);
-
-  f32x16_t acc[TI][4];
+  f32x16_t acc[2][4];
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (ti == tj)
+    syrk256_tile<TM, true>(X, n, ldx, r0, c0, kbeg, kend, Ls, acc);
+  else
+    syrk256_tile<TM, false>(X, n, ldx, r0, c0, kbeg, kend, Ls, acc);
 
-  // DMA: each stage and panel is 16 wave-chunks of 1 KB (64 lanes x 16 B);
-  // wave w fills chunks CPW w .. CPW w + CPW-1, and lane l of chunk q fills
-  // LDS unit u = 64 q + l.
-  // Channel-major: unit u = channel row u/4, physical chunk u%4, i.e.
-  // logical chunk (u%4) ^ ((row>>2)&3) of 8 tokens.  Rows past n read row
-  // n-1 (those products only reach outputs >= n, which are never stored).
-  // Token-major: unit u = token row u/32, physical chunk u%32, logical chunk
-  // (u%32) ^ tm_swz(row) of 8 channels; channels past n read channels n-8 ..
-  // n-1 (n is a multiple of 8 on this path), again only reaching outputs
-  // that are never stored.
-  const uint16_t* ga[CPW];
-  const uint16_t* gb[CPW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
+  if (pslot >= 0) {
+    float* Pt = partial + (int64_t)pslot * (BL * BL);
 #pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int u = (CPW * wave + q) * 64 + lane;
-    if constexpr (TM) {
-      const int t = u >> 5, c = (u & 31) ^ tm_swz(u >> 5);
-      ga[q] = X + (kbeg + t) * ldx + min(r0 + 8 * c, n - 8);
-      gb[q] = X + (kbeg + t) * ldx + min(c0 + 8 * c, n - 8);
-    } else {
-      const int r = u >> 2, c = (u & 3) ^ ((r >> 2) & 3);
-      ga[q] = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
-      gb[q] = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
-    }
-  }
-  const int64_t kstep = TM ? (int64_t)BKL * ldx : (int64_t)BKL;   // elements per stage
-  // token-major operand reads: lane-constant byte offsets of the A (t < TI)
-  // and B (t >= TI) fragments within a slot, for tokens 8 (lane/32) .. + 3
-  // of the stage's first 16 (the other reads add constant row offsets)
-  int toff[TM ? TI + 4 : 1];
-  if constexpr (TM) {
-    const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
-#pragma unroll
-    for (int t = 0; t < TI + 4; ++t) {
-      const int f = (t < TI ? wm * WR + 32 * t : wn * 128 + 32 * (t - TI)) + 16 * (g & 1) + 4 * a;
-      toff[t] = (t < TI ? 0 : BL * 64) + (8 * (g >> 1) + j) * 512 +
-                (((f >> 3) ^ tm_swz(j)) << 4) + 2 * (f & 7);
-    }
-  }
-  auto issue = [&](int stage) {
-    const int slot = stage % NSLOT;
-    const int64_t ko = (int64_t)stage * kstep;
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(ga[q] + ko),
-          (__attribute__((address_space(3))) void*)&Ls[slot][0][(CPW * wave + q) * 64], 16, 0,
-          0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(gb[q] + ko),
-          (__attribute__((address_space(3))) void*)&Ls[slot][1][(CPW * wave + q) * 64], 16, 0,
-          0);
-    }
-  };
-  auto compute = [&](int slot) {
-    if (skip) return;
-    const uint4* A = Ls[slot][0];
-    const uint4* B = Ls[slot][1];
-    if constexpr (TM) {
-      // both token steps' operands in one block of transposed reads
-      static_assert(TI + 4 == 6, "six operands per token step");
-      const uint32_t sb = (uint32_t)(uintptr_t)(const lds_char*)&Ls[slot][0][0];
-      uint32_t p[6];
-      bf16x8_t o[12];
-#pragma unroll
-      for (int t = 0; t < 6; ++t) p[t] = sb + toff[t];
-      tr_operands12(p, o);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[6 * ks + i], o[6 * ks + TI + j],
-                                                                acc[i][j], 0, 0, 0);
-      return;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = 2 * ks + (lane >> 5);
-      bf16x8_t a[TI], b[4];
-#pragma unroll
-      for (int t = 0; t < TI; ++t)
-        a[t] = __builtin_bit_cast(bf16x8_t, A[swz(wm * WR + 32 * t + (lane & 31), c)]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        b[t] = __builtin_bit_cast(bf16x8_t, B[swz(wn * 128 + 32 * t + (lane & 31), c)]);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-  // Wait until this wave's DMA for the stage about to be computed has landed
-  // (`later` stages, 2 CPW instructions each, may stay in flight) and its own
-  // LDS reads are done, then meet the other waves.
-  auto sync_stage = [&](int later) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    switch (later) {
-      case 0: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0)); break;
-      case 1: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * CPW)); break;
-      case 2: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * CPW)); break;
-      default: __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(6 * CPW)); break;
-    }
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
-
-  for (int s = 0; s < AHEAD && s < nfull; ++s) issue(s);
-  int s = 0;
-  // steady state: stages s+1..s+3 in flight while stage s is waited for;
-  // stage s+4 goes into the slot computed in the previous iteration, which
-  // every wave has finished reading (barrier above)
-  for (; s + AHEAD < nfull; ++s) {
-    sync_stage(AHEAD - 1);
-    issue(s + AHEAD);
-    compute(s % NSLOT);
-  }
-  for (; s < nfull; ++s) {
-    sync_stage(nfull - 1 - s);
-    compute(s % NSLOT);
-  }
-  if (nstage > nfull) {
-    // ragged token tail: one masked stage through registers
-    sync_stage(0);
-    const int slot = nfull % NSLOT;
-    const int64_t k0 = kbeg + (int64_t)nfull * BKL;
-#pragma unroll
-    for (int i = 0; i < 1024 / NTL; ++i) {
-      if constexpr (TM) {
-        const int u = tid + NTL * i, t = u >> 5, c = (u & 31) ^ tm_swz(t);
-        uint4 va = make_uint4(0, 0, 0, 0), vb = va;
-        if (k0 + t < kend) {
-          va = *(const uint4*)(X + (k0 + t) * ldx + min(r0 + 8 * c, n - 8));
-          vb = *(const uint4*)(X + (k0 + t) * ldx + min(c0 + 8 * c, n - 8));
-        }
-        Ls[slot][0][u] = va;
-        Ls[slot][1][u] = vb;
-      } else {
-        const int row = (tid >> 2) + (NTL / 4) * i;
-        const int64_t kk = k0 + (tid & 3) * 8;
-        Ls[slot][0][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, r0 + row, n, kk, kend, aligned);
-        Ls[slot][1][swz(row, tid & 3)] = load_vec<uint16_t>(X, ldx, c0 + row, n, kk, kend, aligned);
-      }
-    }
-    __syncthreads();
-    compute(slot);
-  }
-
-  if (!direct) {
-    float* P = partial + ((int64_t)split * ntiles + tile) * (BL * BL);
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * WR + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int col = wn * 128 + j * 32 + (lane & 31);
-          P[row * BL + col] = acc[i][j][r];
+          Pt[row * BL + col] = acc[i][j][r];
         }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int gr = r0 + wm * WR + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int gc = c0 + wn * 128 + j * 32 + (lane & 31);
         if (gr < n && gc <= gr) {
           float v = 2.0f * acc[i][j][r];
@@ -563,6 +611,68 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
           if (gc != gr) H[(int64_t)gc * n + gr] = v;
         }
       }
+}
+
+// Sum the split partials of the split tiles in split order, x2, (+H), write
+// the lower triangle and its mirror.  One workgroup per 64x64 sub-block of
+// a split tile (split tile R of the list ordered by XCD, then position).
+__global__ __launch_bounds__(256) void syrk_reduce_split(const float* __restrict__ partial,
+                                                         int64_t T, int mode, int nsplit,
+                                                         int nrem, int n, float* __restrict__ H,
+                                                         int accumulate) {
+  __shared__ float Tt[64][65];
+  const int R = blockIdx.x / 16, q = blockIdx.x % 16;
+  int tile = 0, pre = 0;
+  for (int y = 0; y < 8; ++y) {
+    int tb, d, rem;
+    xcd_tiles(T, y, mode, tb, d, rem);
+    if (R < pre + rem) {
+      tile = tb + d + (R - pre);
+      break;
+    }
+    pre += rem;
+  }
+  int ti, tj;
+  tile_coords(tile, (n + BL - 1) / BL, ti, tj);
+  const int qr = (q / 4) * 64, qc = (q % 4) * 64;
+  const int r0 = ti * BL + qr, c0 = tj * BL + qc;
+  if (ti == tj && qr < qc) return;  // strictly-upper sub-block of a diagonal tile
+  const int tid = threadIdx.x;
+  const int64_t split_stride = (int64_t)nrem * (BL * BL) / 4;   // float4 units
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int e4 = tid + 256 * v;
+    const int lr = e4 >> 4, lc = (e4 & 15) * 4;
+    const float4* src = (const float4*)(partial + (int64_t)R * (BL * BL) +
+                                        (int64_t)(qr + lr) * BL + qc + lc);
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float4 p = src[sp * split_stride];
+      s.x += p.x;
+      s.y += p.y;
+      s.z += p.z;
+      s.w += p.w;
+    }
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gr = r0 + lr, gc = c0 + lc + u;
+      float val = 2.0f * sv[u];
+      if (gr < n && gc < n && gc <= gr) {
+        if (accumulate) val += H[(int64_t)gr * n + gc];
+        H[(int64_t)gr * n + gc] = val;
+      }
+      Tt[lr][lc + u] = val;
+    }
+  }
+  __syncthreads();
+  // mirrored writes, coalesced along the destination row
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int lr = e >> 6, lc = e & 63;   // destination row c0+lr, col r0+lc
+    const int gr = r0 + lc, gc = c0 + lr; // source lower element (gr, gc)
+    if (gr < n && gc < n && gc < gr) H[(int64_t)gc * n + gr] = Tt[lc][lr];
+  }
 }
 
 // Sum split partials in split order, x2, (+H), write lower and mirror.
@@ -630,33 +740,76 @@ bool syrk_aligned(const void* X, int64_t n, int64_t ldx, int32_t xdtype) {
 }
 
 void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* p) {
-  // bf16 inputs on layers of >= 1024 channels (16-byte aligned rows) use the
-  // 256x256 tile
   xdtype &= kXTypeMask;
   const bool big = xdtype == 1 && n >= 1024 && aligned;
-  const int te = big ? BL : BM;
-  const int bk = big ? BKL : (xdtype == 1 ? SyrkCfg<uint16_t>::BK : SyrkCfg<float>::BK);
+  p->mode = -1;
+  p->nrem = 0;
+  if (big) {
+    // 256 tiles (bf16, >= 1024 channels, 16-byte rows): per-XCD tile ranges
+    const int64_t nt = (n + BL - 1) / BL;
+    const int64_t T = nt * (nt + 1) / 2;
+    const int64_t stages = (ntok + BKS - 1) / BKS;
+    p->tile = BL;
+    p->ntiles = T;
+    // time of one whole tile on one CU, and of writing and reading back one
+    // partial tile, as estimates for choosing the decomposition
+    const double t_tile = 2.0 * BL * BL * (double)ntok / 6.0e12;
+    const double t_part = 2.0 * BL * BL * 4.0 / 4.0e12;
+    double best = -1.0;
+    int bmode = 2;
+    int64_t bs = 1;
+    for (int mode = 0; mode <= 2; ++mode) {
+      const int64_t smax = mode == 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(64, stages / 16));
+      for (int64_t S = (mode == 2 ? 1 : 2); S <= smax; ++S) {
+        double worst = 0.0;
+        int64_t nrem = 0;
+        for (int x = 0; x < 8; ++x) {
+          int tb, d, rem;
+          xcd_tiles(T, x, mode, tb, d, rem);
+          const double rounds = (double)((d + 31) / 32) +
+                                (rem ? (double)((rem * S + 31) / 32) / (double)S : 0.0);
+          worst = std::max(worst, rounds);
+          nrem += rem;
+        }
+        const double cost = worst * t_tile + (S > 1 ? (double)(S * nrem) * t_part : 0.0);
+        if (best < 0.0 || cost < best * (1.0 - 1e-9)) {
+          best = cost;
+          bmode = mode;
+          bs = S;
+        }
+      }
+    }
+    int64_t kps = ((stages + bs - 1) / bs) * BKS;
+    if (kps < BKS) kps = BKS;
+    int64_t S = std::max<int64_t>(1, (ntok + kps - 1) / kps);
+    if (S == 1) bmode = 2;
+    p->mode = bmode;
+    p->nsplit = bmode == 2 ? 1 : S;
+    p->kps = bmode == 2 ? std::max<int64_t>(ntok, 1) : kps;
+    int64_t nrem = 0, items = 0;
+    for (int x = 0; x < 8; ++x) {
+      int tb, d, rem;
+      xcd_tiles(T, x, bmode, tb, d, rem);
+      nrem += rem;
+      items = std::max<int64_t>(items, d + rem * p->nsplit);
+    }
+    p->nrem = nrem;
+    p->grid = 8 * std::max<int64_t>(items, 1);
+    p->partial_bytes = nrem > 0 ? (size_t)p->nsplit * nrem * BL * BL * sizeof(float) : 0;
+    return;
+  }
+  const int te = BM;
+  const int bk = xdtype == 1 ? SyrkCfg<uint16_t>::BK : SyrkCfg<float>::BK;
   const int64_t nt = (n + te - 1) / te;
   p->tile = te;
   p->ntiles = nt * (nt + 1) / 2;
   const int64_t stages = (ntok + bk - 1) / bk;
-  // Enough work items for a few rounds of workgroups; below that, a multiple
-  // of 8 splits so that each XCD streams its own token range.
-  const int64_t slots = big ? 256 : 512;      // resident workgroups
-  const int64_t maxs = stages / 8 > 0 ? stages / 8 : 1;  // >= 8 stages per split
+  // enough work items for a few rounds of workgroups: a multiple of 8
+  // splits, so that each XCD streams its own token range
+  const int64_t slots = 512;                                // resident workgroups
+  const int64_t maxs = stages / 8 > 0 ? stages / 8 : 1;     // >= 8 stages per split
   int64_t ns = 1;
-  if (p->ntiles < 3 * slots && big) {
-    // 8..16 splits: the count whose last round of workgroups is fullest,
-    // i.e. the least rounds x stages-per-split (ties: fewer partials)
-    int64_t best = -1;
-    for (int64_t c = 8; c <= 16; ++c) {
-      const int64_t cost = ((p->ntiles * c + slots - 1) / slots) * ((stages + c - 1) / c);
-      if (best < 0 || cost < best) {
-        best = cost;
-        ns = c;
-      }
-    }
-  } else if (p->ntiles < 3 * slots) {
+  if (p->ntiles < 3 * slots) {
     const int64_t want = (4 * slots + p->ntiles - 1) / p->ntiles;
     ns = (want + 7) / 8 * 8;
   }
@@ -670,6 +823,7 @@ void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* 
   p->nsplit = ns;
   p->kps = kps;
   p->partial_bytes = ns > 1 ? (size_t)ns * p->ntiles * te * te * sizeof(float) : 0;
+  p->grid = 8 * ((p->ntiles * ns + 7) / 8);
 }
 
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
@@ -678,10 +832,6 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
   const bool aligned = syrk_aligned(X, n, ldx, xdtype);
   const bool tm = (xdtype & kXTokenMajor) != 0;
   xdtype &= kXTypeMask;
-  const int direct = p.nsplit == 1;
-  const int64_t items = p.ntiles * p.nsplit;
-  const int per_xcd = (int)((items + 7) / 8);
-  const unsigned grid = (unsigned)(8 * per_xcd);
   if (p.tile == BL && !aligned) return hipErrorInvalidValue;  // checked by the caller
   KernelTimer& timer = g_timers[PWQ_TIMER_HESSIAN_TILES];
   hipError_t te = hipSuccess;
@@ -690,14 +840,25 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
   const float* Xf = (const float*)X;
   const uint16_t* Xh = (const uint16_t*)X;
   float* P = (float*)partial;
+  const unsigned grid = (unsigned)p.grid;
+  if (p.tile == BL) {
+    if (tm)
+      syrk_tiles256<true><<<grid, NTL, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, P, H, accumulate,
+                                                p.ntiles, (int)p.nsplit, p.mode, (int)p.nrem);
+    else
+      syrk_tiles256<false><<<grid, NTL, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, P, H, accumulate,
+                                                 p.ntiles, (int)p.nsplit, p.mode, (int)p.nrem);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = timer.end(ti, st);
+    if (e != hipSuccess || p.nrem == 0) return e;
+    syrk_reduce_split<<<(unsigned)(p.nrem * 16), 256, 0, st>>>(
+        P, p.ntiles, p.mode, (int)p.nsplit, (int)p.nrem, (int)n, H, accumulate);
+    return hipGetLastError();
+  }
+  const int direct = p.nsplit == 1;
+  const int per_xcd = (int)(p.grid / 8);
   const int nti = (int)p.ntiles, nsp = (int)p.nsplit;
-  if (p.tile == BL && tm)
-    syrk_tiles256<true><<<grid, NTL, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P, H,
-                                              direct, accumulate, nti, nsp, per_xcd);
-  else if (p.tile == BL)
-    syrk_tiles256<false><<<grid, NTL, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P, H,
-                                               direct, accumulate, nti, nsp, per_xcd);
-  else if (xdtype == 1 && tm)
+  if (xdtype == 1 && tm)
     syrk_tiles<uint16_t, true><<<grid, NT, 0, st>>>(Xh, (int)n, ntok, ldx, p.kps, aligned, P,
                                                     H, direct, accumulate, nti, nsp, per_xcd);
   else if (xdtype == 1)
@@ -712,12 +873,8 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int32_t xdtype,
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = timer.end(ti, st);
   if (e != hipSuccess || direct) return e;
-  if (p.tile == BL)
-    syrk_reduce<BL><<<(unsigned)(p.ntiles * 16), 256, 0, st>>>(
-        (const float*)partial, (int)p.ntiles, (int)p.nsplit, (int)n, H, accumulate);
-  else
-    syrk_reduce<BM><<<(unsigned)(p.ntiles * 4), 256, 0, st>>>(
-        (const float*)partial, (int)p.ntiles, (int)p.nsplit, (int)n, H, accumulate);
+  syrk_reduce<BM><<<(unsigned)(p.ntiles * 4), 256, 0, st>>>(
+      (const float*)partial, (int)p.ntiles, (int)p.nsplit, (int)n, H, accumulate);
   return hipGetLastError();
 }
 

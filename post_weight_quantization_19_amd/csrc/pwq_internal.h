@@ -13,9 +13,17 @@ namespace pwq {
 struct SyrkPlan {
   int tile;              // output tile edge (128 or 256)
   int64_t ntiles;
-  int64_t nsplit;
+  int64_t nsplit;        // splits of the token axis (of every split tile)
   int64_t kps;           // tokens per split (multiple of the LDS stage)
-  size_t partial_bytes;  // 0 when a single split writes H directly
+  size_t partial_bytes;  // 0 when every tile writes H directly
+  // 256 tiles: each XCD owns a contiguous range of tiles; `mode` says which
+  // of them are computed whole (written straight into H) and which are
+  // split over the token axis (partials, summed by the reduction).
+  //   0: every tile split; 1: whole rounds of 32 tiles direct, the rest
+  //   split; 2: every tile direct.
+  int mode;
+  int64_t nrem;          // split tiles over all XCDs
+  int64_t grid;          // workgroups launched
 };
 
 // Overflow entries (SSQR): per-row counts, offsets and total; the sorted
