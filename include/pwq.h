@@ -167,6 +167,19 @@ pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t pre
                              void* L, int32_t* dead, pwq_result* result,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* pwq_damp_cholesky without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments and results as for pwq_damp_cholesky;
+ * it calls no allocating routine.  Its scratch (status flags, lambda and the
+ * side buffer of diagonal blocks: 68 KB at most, whatever n) is a static
+ * device array of the library; each GPU the library runs on holds one copy
+ * until the process ends.  Every call on a GPU uses that GPU's copy, so calls
+ * that overlap on one GPU (on different streams, or from different threads)
+ * race: serialise them.  A size that would need more scratch than the array
+ * holds is rejected with PWQ_ERR_WORKSPACE before anything is enqueued. */
+pwq_status pwq_damp_cholesky_static(const float* H, int64_t n, double damp, int32_t prec,
+                                    void* L, int32_t* dead, pwq_result* result, void* stream);
+
 /* ---------------------------------------------------------------------- *
  * Steps for SYM / ASYM grids from W [GEOM 2.1: fixed basis X diag(s)].
  *   scales : m x (n / G) float32 (G = group_size, or n when 0)

@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import PwqError, check, lib, make_grid, parse_result
 
-__all__ = ["Grid", "hessian_accum", "damp_cholesky", "grid_steps", "babai_sweep",
+__all__ = ["Grid", "hessian_accum", "damp_cholesky", "damp_cholesky_static", "grid_steps", "babai_sweep",
            "quant_layer", "column_entropy", "read_result", "PwqError", "KernelTimer",
            "HessianTileTimer", "overflow_entries", "ssqr_quant_layer"]
 
@@ -154,6 +154,29 @@ def damp_cholesky(H: torch.Tensor, damp: float = 0.01, prec: str = "f32"):
     check(L_.pwq_damp_cholesky(H.data_ptr(), n, float(damp), _prec(prec), Lt.data_ptr(),
                                dead.data_ptr(), res.data_ptr(), ws.data_ptr(), ws.numel(),
                                _stream()))
+    return Lt, dead, res
+
+
+def damp_cholesky_static(H: torch.Tensor, damp: float = 0.01, prec: str = "f32",
+                         out: Optional[tuple] = None):
+    """damp_cholesky through pwq_damp_cholesky_static: no workspace (the
+    library's static device scratch; calls overlapping on one GPU race).
+    ``out`` may pass preallocated (L, dead, result) so that the call itself
+    allocates nothing."""
+    _require_cuda(H)
+    n = H.shape[0]
+    _check(H, "H", (n, n), _F32)
+    if out is None:
+        out = (torch.empty((n, n), dtype=_tdt(prec), device=H.device),
+               torch.empty(n, dtype=torch.int32, device=H.device), new_result(H.device))
+    Lt, dead, res = out
+    _require_cuda(Lt, dead, res)
+    _check(Lt, "L", (n, n), (_tdt(prec),))
+    _check(dead, "dead", (n,), _I32)
+    _check_result(res)
+    check(lib().pwq_damp_cholesky_static(H.data_ptr(), n, float(damp), _prec(prec),
+                                         Lt.data_ptr(), dead.data_ptr(), res.data_ptr(),
+                                         _stream()))
     return Lt, dead, res
 
 

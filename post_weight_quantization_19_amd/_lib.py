@@ -21,7 +21,7 @@ ORDERS = {"back_to_front": 0, "front_to_back": 1, "perm": 2, "act_order": 3, "mi
 EXPORTS = [
     "pwq_status_string", "pwq_last_error",
     "pwq_hessian_workspace_size", "pwq_hessian_accum",
-    "pwq_cholesky_workspace_size", "pwq_damp_cholesky",
+    "pwq_cholesky_workspace_size", "pwq_damp_cholesky", "pwq_damp_cholesky_static",
     "pwq_grid_steps",
     "pwq_sweep_workspace_size", "pwq_babai_sweep",
     "pwq_quant_layer_workspace_size", "pwq_quant_layer",
@@ -64,6 +64,7 @@ _SIGS = {
     "pwq_hessian_accum": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _i32, _vp, _sz, _vp]),
     "pwq_cholesky_workspace_size": (_sz, [_i64, _i32]),
     "pwq_damp_cholesky": (_i32, [_vp, _i64, _f64, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pwq_damp_cholesky_static": (_i32, [_vp, _i64, _f64, _i32, _vp, _vp, _vp, _vp]),
     "pwq_grid_steps": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, ctypes.POINTER(PwqGrid),
                               _vp, _vp, _vp]),
     "pwq_sweep_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),

@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 using namespace pwq;
 
@@ -58,6 +59,42 @@ struct Carver {
 };
 
 size_t elem(int32_t prec) { return prec == PWQ_F64 ? 8 : 4; }
+
+// Scratch of pwq_damp_cholesky_static: the status flags, lambda and the
+// side buffer of diagonal blocks that pwq_damp_cholesky otherwise carves from
+// the caller's workspace.  One copy per GPU, held until the process ends;
+// host code uses only the device address looked up below, never the name.
+constexpr size_t kStaticScratchBytes = 68 * 1024;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch copy on the GPU that runs `st` (the current
+// GPU for the null stream), looked up once per GPU with that GPU current.
+hipError_t static_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128 || b == 256; }
 
@@ -244,15 +281,22 @@ size_t pwq_cholesky_workspace_size(int64_t n, int32_t prec) {
   return c.size();
 }
 
-pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec, void* L,
-                             int32_t* dead, pwq_result* result, void* ws, size_t ws_bytes,
-                             void* stream) {
+static pwq_status check_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
+                                      const void* L, const pwq_result* result) {
   if (!H || !L || !result) return fail(PWQ_ERR_INVALID_ARG, "H, L and result must be non-NULL");
   if (n <= 0 || n > 65536) return fail(PWQ_ERR_INVALID_ARG, "n must be in [1, 65536]");
   if (prec != PWQ_F32 && prec != PWQ_F64)
     return fail(PWQ_ERR_INVALID_ARG, "prec must be PWQ_F32 or PWQ_F64");
   if (!(damp >= 0.0) || !(damp < 1e30)) return fail(PWQ_ERR_INVALID_ARG, "damp must be >= 0");
-  pwq_status s = check_ws(ws, ws_bytes, pwq_cholesky_workspace_size(n, prec));
+  return PWQ_OK;
+}
+
+pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec, void* L,
+                             int32_t* dead, pwq_result* result, void* ws, size_t ws_bytes,
+                             void* stream) {
+  pwq_status s = check_damp_cholesky(H, n, damp, prec, L, result);
+  if (s != PWQ_OK) return s;
+  s = check_ws(ws, ws_bytes, pwq_cholesky_workspace_size(n, prec));
   if (s != PWQ_OK) return s;
   Carver c(ws);
   DevFlags* flags = (DevFlags*)c.take(sizeof(DevFlags));
@@ -265,6 +309,20 @@ pwq_status pwq_damp_cholesky(const float* H, int64_t n, double damp, int32_t pre
                              st);
   if (e != hipSuccess) return hip_fail(e, "damp_cholesky launch");
   return ok();
+}
+
+pwq_status pwq_damp_cholesky_static(const float* H, int64_t n, double damp, int32_t prec,
+                                    void* L, int32_t* dead, pwq_result* result, void* stream) {
+  pwq_status s = check_damp_cholesky(H, n, damp, prec, L, result);
+  if (s != PWQ_OK) return s;
+  const size_t need = pwq_cholesky_workspace_size(n, prec);
+  if (need > kStaticScratchBytes)
+    return fail(PWQ_ERR_WORKSPACE, "needs %zu bytes of scratch; the static scratch holds %zu",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = static_scratch((hipStream_t)stream, &ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
+  return pwq_damp_cholesky(H, n, damp, prec, L, dead, result, ws, kStaticScratchBytes, stream);
 }
 
 // -------------------------------------------------------------------- steps

@@ -25,7 +25,7 @@ def header_functions():
 def test_exports_match_header():
     L = B.lib()
     names = header_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     assert sorted(B.EXPORTS) == names
     for nm in names:
         assert getattr(L, nm) is not None
@@ -67,6 +67,13 @@ def test_cholesky_validation():
     assert L.pwq_damp_cholesky(FAKE, 8, -1.0, 0, FAKE, None, FAKE, FAKE, 4096, None) == INVALID
     assert L.pwq_damp_cholesky(FAKE, 8, 0.01, 5, FAKE, None, FAKE, FAKE, 4096, None) == INVALID
     assert L.pwq_damp_cholesky(FAKE, 8, 0.01, 0, FAKE, None, FAKE, None, 0, None) == WS
+    # the variant with the library's static scratch validates the same way
+    # (before looking the scratch up, so no device is touched here)
+    assert L.pwq_damp_cholesky_static(None, 8, 0.01, 0, FAKE, None, FAKE, None) == INVALID
+    assert L.pwq_damp_cholesky_static(FAKE, 0, 0.01, 0, FAKE, None, FAKE, None) == INVALID
+    assert L.pwq_damp_cholesky_static(FAKE, 8, -1.0, 0, FAKE, None, FAKE, None) == INVALID
+    assert L.pwq_damp_cholesky_static(FAKE, 8, 0.01, 5, FAKE, None, FAKE, None) == INVALID
+    assert L.pwq_damp_cholesky_static(FAKE, 70000, 0.01, 0, FAKE, None, FAKE, None) == INVALID
 
 
 def _grid(kind=0, bits=4, group=0, c=0.0, kappa=0.0):
