@@ -32,10 +32,13 @@ namespace pwq {
 namespace {
 
 constexpr int NB = 64;   // panel width
-// Panels per trailing update: fp64 trailing tiles are bound by their
-// read-modify-write, so it pays to apply several panels at once; the fp32
-// tile is not, and the wider K only lengthens the launch.
-template <typename T> constexpr int lazy_panels() { return sizeof(T) == 8 ? 8 : 1; }
+// Panels per trailing update.  fp64 trailing tiles are bound by their
+// read-modify-write, so it pays to apply several panels at once.  fp32 tiles
+// are too once the trailing triangle is large (n = 14336: 20.8 ms with one
+// panel per pass, 17.2 with two, 16.3 with four, 16.8 with eight); on small
+// matrices the wider K only lengthens the panel role (n = 4096: 1.58 ms with
+// one or two, 1.78 with four).
+template <typename T> int lazy_panels(int n) { return sizeof(T) == 8 ? 8 : (n >= 8192 ? 4 : 1); }
 
 // lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;
 // fixed-order fp64 reduction.
@@ -733,8 +736,8 @@ hipError_t factor_impl(T* A, int n, T* dbuf, DevFlags* flags, pwq_result* res,
     const int np = (n - p1 + NB - 1) / NB;
     const int base2 = k0 + 2 * NB;
     const int nt = base2 < n ? (n - base2 + 127) / 128 : 0;
-    // the trailing triangle takes the pending panels lazy_panels<T>() at a time
-    const bool trail = nt > 0 && (k0 - kfrom) / NB + 1 >= lazy_panels<T>();
+    // the trailing triangle takes the pending panels lazy_panels<T>(n) at a time
+    const bool trail = nt > 0 && (k0 - kfrom) / NB + 1 >= lazy_panels<T>(n);
     const int ntrail = trail ? nt * (nt + 1) / 2 : 0;
     chol_step<T><<<np + ntrail + 1, 256, 0, st>>>(A, n, k0, kfrom, np, ntrail, dbuf, flags,
                                                   res);

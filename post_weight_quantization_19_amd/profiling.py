@@ -4,6 +4,9 @@
         per-kernel call count / average / total from DIR/*_kernel_stats.csv
     python -m post_weight_quantization_19_amd.profiling traffic --fetch DIR --write DIR \
             --kernel NAME --algorithmic-bytes B --source FILE --command CMD ... --out FILE.json
+    python -m post_weight_quantization_19_amd.profiling kernels --trace DIR --sq DIR \
+            --fetch DIR --write DIR --kernel NAME[=PEAK] ... --command CMD ... --out FILE.md
+        per-kernel MFMA rate, MFMA busy fraction, clock and HBM bytes
         HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE,
         WRITE_SIZE in KiB per dispatch), each scaled by what the same counter
         reads for the 1 GiB device copy in the same run.
@@ -145,6 +148,79 @@ def traffic(fetch_dir, write_dir, kernel, algorithmic_bytes, source, commands, t
     }
 
 
+def _dispatches(d, counters=None):
+    """{short kernel name: {dispatch id: {counter: value, "_ns": duration}}}
+    from one counter-collection run."""
+    out = {}
+    with open(_one(os.path.join(d, "*counter_collection.csv"))) as f:
+        for r in csv.DictReader(f):
+            if counters and r["Counter_Name"] not in counters:
+                continue
+            k = short_name(r["Kernel_Name"])
+            disp = out.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+            disp[r["Counter_Name"]] = disp.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            disp["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def kernels_markdown(trace, sq, fetch, write, kernels, commands, title, peaks):
+    """Per kernel: launch statistics from the kernel trace; MFMA work, MFMA
+    busy cycles and the shader clock from the SQ run; HBM bytes from the
+    FETCH_SIZE / WRITE_SIZE runs, each scaled by what the same counter reads
+    for the 1 GiB device copy of that run.  Rates are totals over every
+    dispatch of the kernel in the counter run divided by the summed dispatch
+    durations of that run."""
+    st = {r["name"]: r for r in kernel_stats(trace)}
+    sqd = _dispatches(sq)
+    fd = _dispatches(fetch, {"FETCH_SIZE"})
+    wd = _dispatches(write, {"WRITE_SIZE"})
+
+    def copy_factor(dd, counter):
+        for k, v in dd.items():
+            if COPY_KERNEL in k:
+                return COPY_KIB / max(x[counter] for x in v.values())
+        raise SystemExit(f"no {COPY_KERNEL} dispatch in the {counter} run")
+    ff, wf = copy_factor(fd, "FETCH_SIZE"), copy_factor(wd, "WRITE_SIZE")
+
+    def pick(dd, key):
+        for k, v in dd.items():
+            if k == key:
+                return list(v.values())
+        raise SystemExit(f"kernel {key} not in a counter run")
+    out = [f"# {title}", "", "Commands (from the repository root):", "", "```"] + commands + [
+        "```", "",
+        "Launch statistics come from the kernel trace; every other column is a total over all "
+        "dispatches of the kernel in the counter run (MOPS x 512 = flop) divided by their summed "
+        "durations in that run.  MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x the "
+        "summed duration x 2.4 GHz.  HBM "
+        f"bytes: FETCH_SIZE x {ff:.3f} and WRITE_SIZE x {wf:.3f} KiB (factors from the 1 GiB "
+        "device copy of each run).", "",
+        "| kernel | calls | avg (us) | total (ms) | MFMA TFLOP/s | % of peak | MFMA busy "
+        "| read GB/dispatch | write GB/dispatch | HBM GB/s |",
+        "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for k in kernels:
+        t = st.get(k)
+        sq_v = pick(sqd, k)
+        ns = sum(x["_ns"] for x in sq_v)
+        flop = 512.0 * sum(x.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) +
+                           x.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) +
+                           x.get("SQ_INSTS_VALU_MFMA_MOPS_F64", 0.0) for x in sq_v)
+        busy = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in sq_v) / (1024 * ns * 2.4)
+        peak = peaks.get(k)
+        tf = flop / ns / 1e3
+        fv, wv = pick(fd, k), pick(wd, k)
+        rd = sum(x["FETCH_SIZE"] for x in fv) * ff * 1024
+        wr = sum(x["WRITE_SIZE"] for x in wv) * wf * 1024
+        fns = sum(x["_ns"] for x in fv) + sum(x["_ns"] for x in wv)
+        out.append(
+            f"| {k} | {t['calls'] if t else '-'} | {t['avg_us'] if t else 0:.1f} | "
+            f"{t['total_ms'] if t else 0:.3f} | {tf:.1f} | "
+            f"{(100 * tf / peak) if peak else float('nan'):.1f} | {busy:.3f} | "
+            f"{rd / len(fv) / 1e9:.4f} | {wr / len(wv) / 1e9:.4f} | "
+            f"{(rd + wr) / (fns / 2) :.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -166,9 +242,27 @@ def main(argv=None):
     t.add_argument("--workload", default="")
     t.add_argument("--x-layout", default=None, help="X layout the counters were taken with")
     t.add_argument("--out", required=True)
+    kk = sub.add_parser("kernels")
+    kk.add_argument("--trace", required=True)
+    kk.add_argument("--sq", required=True)
+    kk.add_argument("--fetch", required=True)
+    kk.add_argument("--write", required=True)
+    kk.add_argument("--kernel", action="append", required=True,
+                    help="short kernel name, optionally NAME=PEAK_TFLOPS")
+    kk.add_argument("--command", action="append", required=True)
+    kk.add_argument("--title", default="rocprofv3 counters per kernel")
+    kk.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         txt = stats_markdown(a.dir, a.command, a.title, a.launches, a.bench_log)
+    elif a.cmd == "kernels":
+        names, peaks = [], {}
+        for spec in a.kernel:
+            nm, _, pk = spec.partition("=")
+            names.append(nm)
+            if pk:
+                peaks[nm] = float(pk)
+        txt = kernels_markdown(a.trace, a.sq, a.fetch, a.write, names, a.command, a.title, peaks)
     else:
         txt = json.dumps(traffic(a.fetch, a.write, a.kernel, a.algorithmic_bytes, a.source,
                                  a.command, a.title, a.workload, a.x_layout), indent=1) + "\n"

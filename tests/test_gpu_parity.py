@@ -118,6 +118,28 @@ def test_cholesky_stage(layers, prec, tol):
     assert rel_fro(Lg, Lo) <= tol
 
 
+@pytest.mark.parametrize("n", [8200, 8256])
+def test_cholesky_large_fp32(n):
+    """From n = 8192 the fp32 factor applies four pending panels per pass
+    over the trailing triangle; a ragged last panel (8200) and an aligned
+    size (8256), against the oracle's fp64 factor of the same float32 input."""
+    rng = np.random.default_rng(n)
+    A = rng.standard_normal((n, n + 512)).astype(np.float32)
+    H = A @ A.T
+    del A
+    print(f"[cholesky] fp32 n={n}", flush=True)
+    L, _, res = P.damp_cholesky(torch.from_numpy(H).cuda(), damp=0.01, prec="f32")
+    torch.cuda.synchronize()
+    r = P.read_result(res)
+    Hd, _, lam, _ = O.fix_dead_and_damp(H.astype(np.float64), np.zeros((1, n)), 0.01)
+    Lo, info = O.cholesky_lower(Hd)
+    assert info == 0 and r["info"] == 0
+    assert r["lambda"] == pytest.approx(lam, rel=1e-12)
+    Lg = to_np(L)
+    assert np.all(np.triu(Lg, 1) == 0)
+    assert rel_fro(Lg, Lo) <= TOL_L
+
+
 def test_cholesky_reports_failing_minor():
     n = 200
     d = np.ones(n, np.float32)
