@@ -543,18 +543,24 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
   const int r0 = base + ti * TB, c0 = base + tj * TB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, li = lane & 31;
-  // acc = A_ij - sum_k P_ik P_jk: the accumulators start from the tile
+  // acc = A_ij - sum_k P_ik P_jk: the accumulators start from the tile.
+  // The tile's addresses are formed from opaque copies of n, here and at the
+  // stores, so the compiler cannot keep 64 of them live through the K loop.
   f32x16_t acc[2][2];
+  {
+    int nl = n;
+    asm volatile("" : "+s"(nl));
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = min(r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3), n - 1);
-        const int gc = min(c0 + wn * 64 + j * 32 + li, n - 1);
-        acc[i][j][r] = A[(int64_t)gr * n + gc];
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int gr = min(r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3), nl - 1);
+          const int gc = min(c0 + wn * 64 + j * 32 + li, nl - 1);
+          acc[i][j][r] = A[(int64_t)gr * nl + gc];
+        }
+  }
   const float* pa[2];
   const float* pb[2];
 #pragma unroll
@@ -562,21 +568,20 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
     pa[i] = A + (int64_t)min(r0 + wm * 64 + i * 32 + li, n - 1) * n + 32 * g;
     pb[i] = A + (int64_t)min(c0 + wn * 64 + i * 32 + li, n - 1) * n + 32 * g;
   }
-  for (int pc = 0; pc < npan; ++pc) {
-    const int kc = kfrom + pc * NB;
-    float4 a[2][8], b[2][8];
+  // Half a panel's operands (K steps 16 h .. 16 h + 15 of each lane's
+  // 32): 16 16-byte loads per lane.
+  auto load = [&](float4 (&a)[2][4], float4 (&b)[2][4], int kc, int h) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        a[i][q] = *(const float4*)(pa[i] + kc + 4 * q);
-        b[i][q] = *(const float4*)(pb[i] + kc + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        a[i][q] = *(const float4*)(pa[i] + kc + 16 * h + 4 * q);
+        b[i][q] = *(const float4*)(pb[i] + kc + 16 * h + 4 * q);
       }
-    // all 32 loads in flight before the first MFMA (the scheduler would
-    // otherwise interleave them a few at a time, paying the latency 8 times)
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma = [&](const float4 (&a)[2][4], const float4 (&b)[2][4]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float av[2], bv[2];
@@ -591,7 +596,33 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
+  };
+  // Two half-panel operand sets in turn: the next half's loads are issued
+  // before the current half's 64 MFMAs (a scheduling barrier keeps them
+  // there; the scheduler would otherwise spread them among the MFMAs), so
+  // their latency runs under the MFMAs; the wait before the MFMAs leaves
+  // the newer loads in flight (vector memory counts complete in order).
+  // The MFMAs take K in the same order as a whole panel at a time.
+  // The last panel is peeled off, so that every wait inside the loop sees
+  // the same loads in flight.
+  float4 a0[2][4], b0[2][4], a1[2][4], b1[2][4];
+  load(a0, b0, kfrom, 0);
+  int kc = kfrom;
+  for (int pc = 0; pc + 1 < npan; ++pc, kc += NB) {
+    load(a1, b1, kc, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    load(a0, b0, kc + NB, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
   }
+  load(a1, b1, kc, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(a0, b0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(a1, b1);
+  int ns = n;
+  asm volatile("" : "+s"(ns));
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -600,7 +631,7 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
       for (int r = 0; r < 16; ++r) {
         const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
         const int gc = c0 + wn * 64 + j * 32 + li;
-        if (gr < n && gc <= gr) A[(int64_t)gr * n + gc] = acc[i][j][r];
+        if (gr < ns && gc <= gr) A[(int64_t)gr * ns + gc] = acc[i][j][r];
       }
 }
 
