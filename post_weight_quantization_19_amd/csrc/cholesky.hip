@@ -161,31 +161,50 @@ __device__ __forceinline__ void panel_factor_store(T* __restrict__ A, int n, int
   // smallest over the waves is the first bad one); kept in a register and
   // published once after the loop, off the column chain
   int my_fail = NB;
-  __syncthreads();
+  // the owner's chain of group g: its 4 columns in registers, published in
+  // the group buffer
+  auto chain = [&](auto G) {
+    constexpr int g = decltype(G)::value;
+    constexpr int j0 = 4 * g, jl0 = j0 % 16;
+    static_for_up<4>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      constexpr int j = j0 + u, jl = jl0 + u;
+      const T piv = readlane_t(d0[jl], j);
+      const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
+      if (bad && my_fail == NB) my_fail = j;
+      T d, inv;
+      pivot_ops(piv, d, inv);
+      d0[jl] = (lane == j) ? d : d0[jl] * inv;
+      d1[jl] = d1[jl] * inv;
+      static_for_up<3 - u>([&](auto V) {
+        constexpr int k = j + 1 + decltype(V)::value;
+        const T lkj = readlane_t(d0[jl], k);
+        d0[jl0 + (k - j0)] -= d0[jl] * lkj;
+        d1[jl0 + (k - j0)] -= d1[jl] * lkj;
+      });
+      gbuf[g & 1][0][u][lane] = d0[jl];
+      gbuf[g & 1][1][u][lane] = d1[jl];
+    });
+  };
+  // rank-4 update of local column c by group g (li: this lane's row values)
+  auto upd = [&](int gb, int c, int k, const T (&li0)[4], const T (&li1)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const T lkj = gbuf[gb][0][u][k];
+      d0[c] -= li0[u] * lkj;
+      d1[c] -= li1[u] * lkj;
+    }
+  };
+  if (wave == 0) chain(std::integral_constant<int, 0>());
+  // After group g is published: the owner of group g + 1 updates that
+  // group's 4 columns, runs its chain, and only then updates its other
+  // later columns, all in one block, so the scheduler can fill the chain's
+  // dependent latencies with those independent updates; every other wave
+  // at or after g's owner updates its later columns.
   static_for_up<NB / 4>([&](auto G) {
     constexpr int g = decltype(G)::value;
-    constexpr int j0 = 4 * g, wj = j0 / 16, jl0 = j0 % 16;
-    if (wave == wj) {
-      static_for_up<4>([&](auto U) {
-        constexpr int u = decltype(U)::value;
-        constexpr int j = j0 + u, jl = jl0 + u;
-        const T piv = readlane_t(d0[jl], j);
-        const bool bad = !(piv > (T)0) || !(piv < (T)INFINITY);
-        if (bad && my_fail == NB) my_fail = j;
-        T d, inv;
-        pivot_ops(piv, d, inv);
-        d0[jl] = (lane == j) ? d : d0[jl] * inv;
-        d1[jl] = d1[jl] * inv;
-        static_for_up<3 - u>([&](auto V) {
-          constexpr int k = j + 1 + decltype(V)::value;
-          const T lkj = readlane_t(d0[jl], k);
-          d0[jl0 + (k - j0)] -= d0[jl] * lkj;
-          d1[jl0 + (k - j0)] -= d1[jl] * lkj;
-        });
-        gbuf[g & 1][0][u][lane] = d0[jl];
-        gbuf[g & 1][1][u][lane] = d1[jl];
-      });
-    }
+    constexpr int j0 = 4 * g, wj = j0 / 16;
+    constexpr int gn = g + 1, jn0 = 4 * gn, wn = jn0 / 16, jln = jn0 % 16;
     __syncthreads();
     if (wave >= wj) {
       T li0[4], li1[4];
@@ -194,16 +213,17 @@ __device__ __forceinline__ void panel_factor_store(T* __restrict__ A, int n, int
         li0[u] = gbuf[g & 1][0][u][lane];
         li1[u] = gbuf[g & 1][1][u][lane];
       }
+      if (gn < NB / 4 && wave == wn) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const int k = 16 * wave + c;
-        if (k >= j0 + 4) {                      // uniform per wave
+        for (int c = jln; c < jln + 4; ++c) upd(g & 1, c, 16 * wn + c, li0, li1);
+        if constexpr (gn < NB / 4) chain(std::integral_constant<int, gn>());
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const T lkj = gbuf[g & 1][0][u][k];
-            d0[c] -= li0[u] * lkj;
-            d1[c] -= li1[u] * lkj;
-          }
+        for (int c = jln + 4; c < 16; ++c) upd(g & 1, c, 16 * wn + c, li0, li1);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const int k = 16 * wave + c;
+          if (k >= j0 + 4) upd(g & 1, c, k, li0, li1);   // uniform per wave
         }
       }
     }
