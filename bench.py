@@ -200,16 +200,29 @@ def cpu_baseline(lay, cfg, frac):
     }
 
 
-def sweep_launches(n, B):
+def update_group_cols(prec):
+    """Columns of a lazy-update group in the library's sweep (256 in fp32,
+    512 in fp64)."""
+    return 512 if prec == "f64" else 256
+
+
+def sweep_launches(n, B, prec):
     """(sweep-block launches, lazy updates, update flops / m) of one sweep, in
-    the order the library issues them (blocks from the back, sub-blocks of at
+    the order the library issues them: blocks from the back, sub-blocks of at
     most 128 columns, an in-block update after every sub-block but the
-    block's first column group, a block update for every block above 0)."""
+    block's first column group; blocks in groups of update_group_cols
+    columns, each block's errors applied at once to the open columns of its
+    group and each group's errors to every column before the group once its
+    last block is swept."""
     bi = min(B, 128)
+    grp = update_group_cols(prec) // B
+    nblk = (n + B - 1) // B
     nsweep = nupd = 0
     flops_per_row = 0.0
-    for jb0 in range(((n - 1) // B) * B, -1, -B):
+    for b in range(nblk - 1, -1, -1):
+        jb0 = b * B
         jb1 = min(n, jb0 + B)
+        cg0 = (b // grp) * grp * B
         nsub = (jb1 - jb0 + bi - 1) // bi
         for s in range(nsub - 1, -1, -1):
             js0 = jb0 + s * bi
@@ -217,9 +230,13 @@ def sweep_launches(n, B):
             if s > 0:
                 nupd += 1
                 flops_per_row += 2.0 * min(jb1 - js0, bi) * (js0 - jb0)
-        if jb0 > 0:
+        if jb0 > cg0:
             nupd += 1
-            flops_per_row += 2.0 * (jb1 - jb0) * jb0
+            flops_per_row += 2.0 * (jb1 - jb0) * (jb0 - cg0)
+        if jb0 == cg0 and cg0 > 0:
+            kg = min(n, cg0 + grp * B) - cg0
+            nupd += 1
+            flops_per_row += 2.0 * kg * cg0
     return nsweep, nupd, flops_per_row
 
 
@@ -486,14 +503,19 @@ def main():
     # the lazy updates and block sweeps are timed in a separate pass of as
     # many steps (their 2 x 63 event records per step would perturb the
     # headline timing above)
-    nsweep, nupd, upd_flops_row = sweep_launches(n, cfg.block)
-    t_upd = P.KernelTimer("lazy_update", args.steps * nupd)
-    t_swp = P.KernelTimer("sweep_block", args.steps * nsweep)
+    nsweep, nupd, upd_flops_row = sweep_launches(n, cfg.block, prec)
+    t_upd = P.KernelTimer("lazy_update", args.steps * nupd + 1)
+    t_swp = P.KernelTimer("sweep_block", args.steps * nsweep + 1)
     torch.cuda.synchronize()
     with t_upd, t_swp:
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
+    # one spare slot each: a launch schedule that differs from the model
+    # above shows up as a count mismatch instead of silently dropped events
+    if t_upd.count != args.steps * nupd or t_swp.count != args.steps * nsweep:
+        raise RuntimeError(f"timed launches {t_upd.count} updates / {t_swp.count} sweeps, "
+                           f"expected {args.steps * nupd} / {args.steps * nsweep}")
 
     # stage breakdown (same library calls, separately)
     def timed(fn, r=3):

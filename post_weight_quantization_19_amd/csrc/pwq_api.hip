@@ -153,7 +153,7 @@ void carve_sweep(Carver& c, int64_t m, int64_t n, int32_t block, int32_t prec, S
   w->dg = c.take((size_t)n * elem(prec));
   w->alpha = c.take((size_t)n * elem(prec));
   w->acc = c.take((size_t)m * n * elem(prec));
-  w->E = c.take((size_t)m * block * elem(prec));
+  w->E = c.take((size_t)m * update_group_cols(prec) * elem(prec));   // a group of errors per row
   w->partials = (double*)c.take(sweep_partials_bytes(m, n, block, prec));
 }
 

@@ -81,6 +81,13 @@ hipError_t launch_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n
                              int32_t* zeros, const DevFlags* flags, hipStream_t st,
                              float kappa = 1.0f);
 
+// Columns of a lazy-update group: the sweep applies a block's errors to the
+// rest of its group at once and a whole group's errors to the columns before
+// it in one pass; the sweep workspace holds one group of errors per row.
+// fp32: 256 (the register-resident E of the group kernel); fp64: 512 (the
+// generic kernel stages any K through LDS).  A multiple of every block size.
+inline int update_group_cols(int32_t prec) { return prec == PWQ_F64 ? 512 : 256; }
+
 struct SweepLaunch {
   const void* W;
   int32_t wdtype;

@@ -674,28 +674,278 @@ __global__ __launch_bounds__(UPD_NT, 1) void lazy_update_f32(
   }
 }
 
-// One lazy update launch (either form).
+// The update of a whole group of blocks (K up to 128 NCH), for fp32 with
+// 16-byte aligned rows: acc[:, c_lo:j0] += E L over the errors of every
+// block of the group at once, so acc is read and written once per group
+// instead of once per block.  Persistent, one 512-thread workgroup per CU
+// owning row strip w % nstrip (128 rows) and the column tiles w / nstrip,
+// w / nstrip + ngrp, ...  Wave v takes rows 16 v .. 16 v + 15 of the strip
+// and all 128 columns of a tile as eight v_mfma_f32_16x16x4f32
+// accumulators, so every row of E is held by one wave only and the whole
+// strip's E stays in registers for the launch: lane (r, q) = (l % 16,
+// l / 16) holds E[r][16 g + 4 q .. 16 g + 4 q + 3] for every 16-row group g
+// of K (one 16-byte load each).  MFMA step s of group g sums
+// k = 16 g + 4 q + s over the lane groups q; the B operand of lane (c, q)
+// is L[k_lo + 16 g + 4 q + s][c0 + 16 j + c], read from LDS.  K runs in
+// chunks of 128 rows of L (64 KB), double-buffered in LDS and copied with
+// global_load_lds_dwordx4 one chunk ahead; a tile's acc values are loaded
+// during its predecessor's last chunk and stored once after its own last
+// chunk.  The four rows one MFMA step reads are 512 B apart, so the 16-byte
+// column chunks of row k are stored XOR-swizzled by 4 ((k / 4) mod 4): the
+// lane groups then read distinct banks.
+// 16x16 result layout: lane l, register r -> row 4 (l / 16) + r, col l % 16.
+template <int NCH>
+__global__ __launch_bounds__(UPD_NT, 1) void lazy_update_f32_group(
+    const float* __restrict__ E, int ldE, int e_off, int kb, const float* __restrict__ L,
+    int n, int k_lo, int c_lo, int j0, int m, float* __restrict__ acc, int first, int nstrip,
+    int ngrp) {
+  constexpr int TM = 128, KC = 128;
+  __shared__ __attribute__((aligned(16))) float Ls[2][KC * TM];   // [k][col]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int ncol = (j0 - c_lo + TM - 1) / TM;
+  const int r0 = (blockIdx.x % nstrip) * TM;
+  const int tile0 = blockIdx.x / nstrip;
+  if (tile0 >= ncol) return;
+  const int nch = (kb + KC - 1) / KC;   // 1 .. NCH
+
+  // the strip's E: ea[8 ch + g] = E[row][e_off + 128 ch + 16 g + 4 lq + 0..3]
+  // (zero past kb)
+  f32x4_t ea[NCH * 8];
+  {
+    const int gr = r0 + 16 * wave + lr;
+    const float* er = E + (int64_t)(gr < m ? gr : 0) * ldE + e_off + 4 * lq;
+#pragma unroll
+    for (int i = 0; i < NCH * 8; ++i) {
+      f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int k = 16 * i + 4 * lq;
+      if (gr < m && k + 3 < kb) {
+        v = *(const f32x4_t*)(er + 16 * i);
+      } else if (gr < m && k < kb) {   // ragged end of K: element by element
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (k + t < kb) v[t] = er[16 * i + t];
+      }
+      ea[i] = v;
+    }
+  }
+  // chunk ch of the L panel (rows k_lo + 128 ch .., columns c0 .. c0 + 127)
+  // -> LDS buffer (physical 16-byte chunk q of row r holds logical chunk
+  // q ^ 4 ((r / 4) mod 4)).  Rows past kb repeat row k_lo (their E values are
+  // zero); column chunks past n read the last chunk of the row (those
+  // outputs are not stored).
+  auto fetch_l = [&](int c0, int ch, int buf) {
+#pragma unroll
+    for (int i = 0; i < KC * TM / 4 / UPD_NT; ++i) {
+      const int ci = tid + UPD_NT * i;         // 16-byte chunk of the [k][col] panel
+      const int r = ci / (TM / 4), k = KC * ch + r;
+      const int q = (ci % (TM / 4)) ^ (4 * ((r >> 2) & 3));
+      const int row = k_lo + (k < kb ? k : 0);
+      const int col = min(c0 + 4 * q, n - 4);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(L + (int64_t)row * n + col),
+          (__attribute__((address_space(3))) void*)&Ls[buf][(wave * 64 + UPD_NT * i) * 4], 16,
+          0, 0);
+    }
+  };
+  // acc through a buffer resource: an element outside the tile's valid range
+  // gets an out-of-range offset (its load returns 0, its store is dropped),
+  // so every lane issues the same 32 loads / 32 stores per tile (the
+  // in-order vmcnt waits below rely on that count)
+  const __amdgpu_buffer_rsrc_t racc =
+      __builtin_amdgcn_make_buffer_rsrc(acc, 0, m * n * 4, 0x00020000);
+  const int rbase = r0 + 16 * wave + 4 * lq;
+  auto c_off = [&](int c0, int j, int r) -> int {
+    const int gr = rbase + r, gc = c0 + 16 * j + lr;
+    return (gr < m && gc < j0) ? (gr * n + gc) * 4 : -1;
+  };
+  const int lmask = first ? -1 : 0;   // first update: acc is written, not read
+  auto fetch_c = [&](int c0, f32x4_t (&cn)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cn[j][r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(racc, c_off(c0, j, r) | lmask, 0, 0));
+  };
+
+  int t = tile0, buf = 0;
+  // One tile: every chunk of K into `cur` (its acc values already there),
+  // then one store.  The next chunk (or the next tile's first chunk and its
+  // acc values, into `nxt`) is copied while this chunk's MFMAs run.
+  auto tile = [&](f32x4_t (&cur)[8], f32x4_t (&nxt)[8]) -> bool {
+    const int c0 = c_lo + t * TM;
+    const int tn = t + ngrp;
+    static_for_up<NCH>([&](auto CH) {
+      constexpr int ch = decltype(CH)::value;
+      if (ch < nch) {
+        // This chunk's copy (and on the first chunk the tile's acc values)
+        // was issued before the previous tile's 32 stores; vector memory
+        // counts complete in order, so on the first chunk waiting until at
+        // most 32 remain leaves only those stores in flight.
+        if (ch == 0)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(32));
+        else
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_barrier();
+        if (ch + 1 < nch) {
+          fetch_l(c0, ch + 1, buf ^ 1);
+        } else if (tn < ncol) {
+          fetch_l(c_lo + tn * TM, 0, buf ^ 1);
+          // the LDS copies before the acc loads (as in lazy_update_f32)
+          __builtin_amdgcn_sched_barrier(0);
+          fetch_c(c_lo + tn * TM, nxt);
+        }
+        // step i = 4 g + sk reads row 16 g + 4 lq + sk, logical columns
+        // 16 j + lr (physical 16 (j ^ lq) + lr); the reads of step i + 1 are
+        // issued before the MFMAs of step i (two operand sets in turn)
+        const float* Lb = Ls[buf] + 4 * lq * TM + lr;
+        float bv[2][8];
+        auto rd = [&](int i, float (&v)[8]) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = Lb[(16 * (i >> 2) + (i & 3)) * TM + 16 * (j ^ lq)];
+        };
+        rd(0, bv[0]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i + 1 < 32) rd(i + 1, bv[(i + 1) & 1]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            cur[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[8 * ch + (i >> 2)][i & 3],
+                                                          bv[i & 1][j], cur[j], 0, 0, 0);
+          if (i + 1 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        buf ^= 1;
+      }
+    });
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur[j][r]), racc, c_off(c0, j, r),
+                                              0, 0);
+    t = tn;
+    return tn < ncol;
+  };
+
+  f32x4_t ca[8], cb[8];
+  fetch_l(c_lo + t * TM, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_c(c_lo + t * TM, ca);
+  __builtin_amdgcn_s_waitcnt(0);     // E, the first chunk and the acc values
+  while (tile(ca, cb) && tile(cb, ca)) {
+  }
+}
+
+// A lazy update over a narrow column range (K <= 128), for fp32 with
+// 16-byte aligned rows: a block's errors reaching the open columns of its
+// own group, which the persistent kernels would give to only a few
+// workgroups.  One 256-thread workgroup per 16 rows and 128 columns; wave w
+// takes columns 32 w .. 32 w + 31 as two v_mfma_f32_16x16x4f32
+// accumulators, with E and L loaded straight into registers (both are small
+// and shared through L2): lane (r, q) = (l % 16, l / 16) holds
+// E[r][16 g + 4 q .. 16 g + 4 q + 3] and L[k_lo + 16 g + 4 q + s][c + r]
+// for its columns c, so MFMA step s of group g sums k = 16 g + 4 q + s over
+// the lane groups q.
+// 16x16 result layout: lane l, register r -> row 4 (l / 16) + r, col l % 16.
+__global__ __launch_bounds__(256) void near_update_f32(
+    const float* __restrict__ E, int ldE, int e_off, int kb, const float* __restrict__ L,
+    int n, int k_lo, int c_lo, int j0, int m, float* __restrict__ acc, int first) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int r0 = blockIdx.x * 16;
+  const int c0 = c_lo + blockIdx.y * 128 + 32 * wave;
+  if (c0 >= j0) return;   // the wave's columns are all past the range
+  // E rows past m read row m - 1 and K past kb reads zeros (outputs of rows
+  // past m are not stored)
+  const float* er = E + (int64_t)min(r0 + lr, m - 1) * ldE + e_off + 4 * lq;
+  f32x4_t ea[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int k = 16 * g + 4 * lq;
+    f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (k + 3 < kb) {
+      v = *(const f32x4_t*)(er + 16 * g);
+    } else if (k < kb) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (k + t < kb) v[t] = er[16 * g + t];
+    }
+    ea[g] = v;
+  }
+  // L rows past kb repeat row k_lo (their E values are zero); columns past
+  // n - 1 read column n - 1 (those outputs are not stored)
+  float bv[8][4][2];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int sk = 0; sk < 4; ++sk) {
+      const int k = 16 * g + 4 * lq + sk;
+      const float* lrow = L + (int64_t)(k < kb ? k_lo + k : k_lo) * n;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) bv[g][sk][jj] = lrow[min(c0 + 16 * jj + lr, n - 1)];
+    }
+  f32x4_t c[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gr = r0 + 4 * lq + r, gc = c0 + 16 * jj + lr;
+      c[jj][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
+    }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (16 * g >= kb) break;   // uniform
+#pragma unroll
+    for (int sk = 0; sk < 4; ++sk)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        c[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[g][sk], bv[g][sk][jj], c[jj], 0, 0, 0);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gr = r0 + 4 * lq + r, gc = c0 + 16 * jj + lr;
+      if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = c[jj][r];
+    }
+}
+
+// One lazy update launch: acc[:, c_lo:j0] (+)= E[:, e_off:e_off+kb] L[k_lo:k_lo+kb, c_lo:j0]
+// (E with leading dimension ldE).
 template <typename T>
-void update_launch(const T* E, int B, int e_off, int kb, const T* L, int n, int k_lo, int c_lo,
+void update_launch(const T* E, int ldE, int e_off, int kb, const T* L, int n, int k_lo, int c_lo,
                    int j0, int m, T* acc, int first, const DevFlags* flags, hipStream_t st) {
   dim3 g((unsigned)((j0 - c_lo + 127) / 128), (unsigned)((m + 127) / 128));
   if constexpr (sizeof(T) == 4) {
-    if (n % 4 == 0 && ((uintptr_t)L % 16) == 0 && ((uintptr_t)E % 16) == 0 && B % 4 == 0 &&
+    if (n % 4 == 0 && ((uintptr_t)L % 16) == 0 && ((uintptr_t)E % 16) == 0 && ldE % 4 == 0 &&
         e_off % 4 == 0 && (int64_t)m * n * 4 < ((int64_t)1 << 31)) {
+      if (kb <= 128 && j0 - c_lo <= 256) {
+        // a narrow range: one workgroup per 16 rows and 128 columns
+        near_update_f32<<<dim3((unsigned)((m + 15) / 16), (unsigned)((j0 - c_lo + 127) / 128)),
+                          256, 0, st>>>(E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first);
+        return;
+      }
       // one workgroup per CU: every row strip, as many column groups as fit
       const int nstrip = (m + 127) / 128;
       const int ncol = (j0 - c_lo + 127) / 128;
       int ngrp = 256 / nstrip;
       if (ngrp < 1) ngrp = 1;
       if (ngrp > ncol) ngrp = ncol;
-      for (int kh = 0; kh < kb; kh += 128)   // K <= 128 per launch
+      if (kb <= 128)
         lazy_update_f32<<<(unsigned)(nstrip * ngrp), UPD_NT, 0, st>>>(
-            E, B, e_off + kh, min(128, kb - kh), L, n, k_lo + kh, c_lo, j0, m, acc,
-            first && kh == 0, nstrip, ngrp);
-      return;
+            E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first, nstrip, ngrp);
+      else if (kb <= 256)
+        lazy_update_f32_group<2><<<(unsigned)(nstrip * ngrp), UPD_NT, 0, st>>>(
+            E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first, nstrip, ngrp);
+      // (K = 512 would need 128 registers of E per lane: more than fit)
+      if (kb <= 256) return;
+      // wider K: the generic kernel below
     }
   }
-  lazy_update<T><<<g, 256, 0, st>>>(E, B, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first, flags);
+  lazy_update<T><<<g, 256, 0, st>>>(E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first,
+                                    flags);
 }
 
 // ---------------------------------------------------------------- finalize
@@ -766,11 +1016,28 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
   const int n = (int)sl.n, m = (int)sl.m, B = sl.block;
   const int nblk = (n + B - 1) / B;
   const unsigned nwg = (unsigned)((m + 15) / 16);
+  // Blocks go in groups of grp (update_group_cols columns).  A block's errors
+  // reach the open columns of its own group at once (K = the block); the
+  // columns before the group receive the errors of the whole group in one
+  // pass once its last block is swept (K = the group), so acc is read and
+  // written once per group rather than once per block.  E holds the group's
+  // errors (leading dimension ldE), block b at column (b - first block) B.
+  const int grp = update_group_cols(sl.prec) / B, ldE = grp * B;
+  const int top = (nblk - 1) / grp;
   int part = 0;
   KernelTimer& tsweep = g_timers[PWQ_TIMER_SWEEP_BLOCK];
   KernelTimer& tupd = g_timers[PWQ_TIMER_LAZY_UPDATE];
+  auto timed_update = [&](int e_off, int kb, int k_lo, int c_lo, int j0, int first) {
+    hipError_t te = hipSuccess;
+    const int64_t ti = tupd.begin(st, &te);
+    if (te != hipSuccess) return te;
+    update_launch<T>((const T*)sl.E, ldE, e_off, kb, (const T*)sl.L, n, k_lo, c_lo, j0, m,
+                     (T*)sl.acc, first, sl.flags, st);
+    return tupd.end(ti, st);
+  };
   for (int b = nblk - 1; b >= 0 && nwg > 0; --b) {
     const int jb0 = b * B, jb1 = (n < jb0 + B) ? n : jb0 + B;
+    const int gb0 = (b / grp) * grp, cg0 = gb0 * B, e_base = (b - gb0) * B;
     const int nsub = (jb1 - jb0 + Bi - 1) / Bi;
     for (int s = nsub - 1; s >= 0; --s) {
       const int js0 = jb0 + s * Bi;
@@ -778,27 +1045,24 @@ hipError_t run_sweep(const SweepLaunch& sl, hipStream_t st) {
       hipError_t te = hipSuccess;
       int64_t ti = tsweep.begin(st, &te);
       if (te != hipSuccess) return te;
-      sweep_block<T, Bi><<<nwg, 256, 0, st>>>(a, js0, B, js0 - jb0, first_sub, part++);
+      sweep_block<T, Bi><<<nwg, 256, 0, st>>>(a, js0, ldE, e_base + js0 - jb0, first_sub,
+                                               part++);
       te = tsweep.end(ti, st);
       if (te != hipSuccess) return te;
       if (s > 0) {
         // the sub-block's errors reach the open columns of its own block
         const int kb = (jb1 - js0 < Bi) ? jb1 - js0 : Bi;
-        ti = tupd.begin(st, &te);
-        if (te != hipSuccess) return te;
-        update_launch<T>((const T*)sl.E, B, js0 - jb0, kb, (const T*)sl.L, n, js0, jb0, js0, m,
-                         (T*)sl.acc, first_sub, sl.flags, st);
-        te = tupd.end(ti, st);
+        te = timed_update(e_base + js0 - jb0, kb, js0, jb0, js0, first_sub);
         if (te != hipSuccess) return te;
       }
     }
-    if (jb0 > 0) {   // the block's errors reach every earlier column
-      hipError_t te = hipSuccess;
-      const int64_t ti = tupd.begin(st, &te);
+    if (jb0 > cg0) {   // the block's errors reach the open columns of its group
+      const hipError_t te = timed_update(e_base, jb1 - jb0, jb0, cg0, jb0, b == nblk - 1);
       if (te != hipSuccess) return te;
-      update_launch<T>((const T*)sl.E, B, 0, jb1 - jb0, (const T*)sl.L, n, jb0, 0, jb0, m,
-                       (T*)sl.acc, b == nblk - 1, sl.flags, st);
-      te = tupd.end(ti, st);
+    }
+    if (b == gb0 && cg0 > 0) {   // the group's errors reach every earlier column
+      const int kg = ((n < cg0 + ldE) ? n : cg0 + ldE) - cg0;
+      const hipError_t te = timed_update(0, kg, cg0, 0, cg0, b / grp == top);
       if (te != hipSuccess) return te;
     }
     hipError_t e = hipGetLastError();
