@@ -50,3 +50,29 @@ def test_sweep_and_update_timers_count_launches():
     assert tu.count == 4
     assert all(d > 0 for d in ts.durations_ms() + tu.durations_ms())
     assert torch.equal(out["codes"], ref["codes"])
+
+
+def test_grouped_update_launches():
+    """fp32, block 128 on 640 columns: blocks go in groups of two (256
+    columns).  From the back: block 4 (a group of its own) sends its errors
+    to columns 0..511 (K = 128); block 3 to the open block of its group
+    (columns 256..383); block 2 closes its group and sends both blocks'
+    errors to columns 0..255 (K = 256); block 1 to block 0.  Five sweeps,
+    four updates, and the same codes as with block 64 (a different
+    grouping of the same sums)."""
+    g = torch.Generator().manual_seed(5)
+    m, n, ntok = 64, 640, 2048
+    W = (0.02 * torch.randn((m, n), generator=g)).to(torch.bfloat16).cuda()
+    X = torch.randn((n, ntok), generator=g).to(torch.bfloat16).cuda()
+    grid = P.Grid("sym", 4, 128)
+    ts = P.KernelTimer("sweep_block", 64)
+    tu = P.KernelTimer("lazy_update", 64)
+    with ts, tu:
+        out = P.quant_layer(W, X=X, grid=grid, block=128)
+    torch.cuda.synchronize()
+    assert ts.count == 5
+    assert tu.count == 4
+    ref = P.quant_layer(W, X=X, grid=grid, block=64)
+    torch.cuda.synchronize()
+    same = (out["codes"] == ref["codes"]).float().mean().item()
+    assert same >= 0.999
