@@ -321,13 +321,14 @@ pwq_status pwq_oaem_init(const void* W, int32_t wdtype, int64_t m, int64_t n,
  *           or pwq_babai_sweep; zero points make no difference).
  *   bits  : n doubles: bits[k] = -sum_v p_v log2 p_v over the distinct
  *           values v of column k, p_v = (count of v) / m; 0 when m = 0;
- *           NaN for a column whose codes span more than 32768 values.
+ *           NaN for a column whose codes span more than 32768 values when
+ *           m > 16384.
  *   mean  : optional double: the mean of bits over the n columns.
  *   huff  : optional n int64: total length in bits of column k's m codes
  *           under a Huffman code built for that column (codebook not
  *           counted; one distinct value costs 0); -1 where not computed (a
- *           span above 32768 values, or more than 16385 distinct values in
- *           a column spanning more than 512).
+ *           span above 32768 values with m > 16384, or more than 16385
+ *           distinct values in a column spanning 513 to 32768 values).
  *   ws    : pwq_rate_workspace_size(n) bytes.
  * Counts are exact (integer), and the sums run in a fixed order; the
  * Huffman totals are exact integers (every optimal prefix code of the same

@@ -13,7 +13,11 @@
 //     H = -sum_b p_b log2 p_b,  p_b = c_b / m,
 // summed in bin order per lane and reduced in a fixed order (deterministic).
 // Columns whose code range exceeds 512 values are done by colhist_wide, one
-// workgroup per column with a 32768-bin histogram; wider ranges give NaN.
+// workgroup per column with a 32768-bin histogram; columns wider still (with
+// m <= 16384) are sorted there instead, and the length of every run of equal
+// codes is put at the run's first position, which makes a histogram of
+// their distinct values (zeros elsewhere) for the same entropy and Huffman
+// steps.
 //
 // Huffman-coded length ("The Geometry of LLM Quantization ...", technical
 // summary 3, HPTQ: the unconstrained integer codes are Huffman coded): the
@@ -32,6 +36,7 @@ namespace {
 constexpr int RC = 64;          // columns per workgroup
 constexpr int NBIN = 512;       // bins per column in colhist
 constexpr int NBIN_WIDE = 32768;
+constexpr int NSORT = NBIN_WIDE / 2;   // rows a column may have for the sorted path
 
 __global__ __launch_bounds__(256) void colrange(const int32_t* __restrict__ codes, int m, int n,
                                                 int64_t ldc, int32_t* __restrict__ cmin,
@@ -167,35 +172,77 @@ __global__ __launch_bounds__(256) void colhist_wide(const int32_t* __restrict__ 
   const int col = blockIdx.x;
   const int64_t range = (int64_t)cmax[col] - cmin[col] + 1;
   if (range <= NBIN) return;            // done by colhist
-  if (range > NBIN_WIDE) {
+  const auto sync = [] { __syncthreads(); };
+  if (range <= NBIN_WIDE) {
+    for (int i = threadIdx.x; i < NBIN_WIDE; i += 256) hist[i] = 0;
+    __syncthreads();
+    const int32_t base = cmin[col];
+    for (int r = threadIdx.x; r < m; r += 256)
+      atomicAdd(&hist[codes[(int64_t)r * ldc + col] - base], 1);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const double h = entropy_from_hist(hist, (int)range, m);
+      if (threadIdx.x == 0) bits[col] = h;
+    }
+    if (!huff) return;
+    __syncthreads();
+    bitonic_sort(hist, NBIN_WIDE, threadIdx.x, 256, sync);
+    int nz = 0;
+    for (int b = threadIdx.x; b < NBIN_WIDE; b += 256) nz += hist[b] == 0;
+    for (int o = 32; o >= 1; o >>= 1) nz += __shfl_xor(nz, o, 64);
+    if ((threadIdx.x & 63) == 0) nzs[threadIdx.x >> 6] = nz;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int z = nzs[0] + nzs[1] + nzs[2] + nzs[3];
+      // the merged nodes go into the zero prefix; too many symbols: -1
+      huff[col] = (NBIN_WIDE - z <= z + 1) ? huffman_merge(hist, z, NBIN_WIDE, hist) : -1;
+    }
+    return;
+  }
+  // Wider: sort the column's codes (padded with INT32_MAX to a power of
+  // two), put each run's length at its first position, and take the entropy
+  // and the Huffman total over those counts.  sv: the sorted codes, later
+  // the Huffman node queue; cv: the counts.
+  if (m > NSORT) {
     if (threadIdx.x == 0) {
       bits[col] = __builtin_nan("");
       if (huff) huff[col] = -1;
     }
     return;
   }
-  for (int i = threadIdx.x; i < NBIN_WIDE; i += 256) hist[i] = 0;
+  int32_t* sv = hist;
+  int32_t* cv = hist + NSORT;
+  int len = 2;                          // m >= 2: the range spans two values
+  while (len < m) len <<= 1;
+  for (int i = threadIdx.x; i < len; i += 256)
+    sv[i] = i < m ? codes[(int64_t)i * ldc + col] : INT32_MAX;
   __syncthreads();
-  const int32_t base = cmin[col];
-  for (int r = threadIdx.x; r < m; r += 256)
-    atomicAdd(&hist[codes[(int64_t)r * ldc + col] - base], 1);
+  bitonic_sort(sv, len, threadIdx.x, 256, sync);
+  for (int i = threadIdx.x; i < len; i += 256) {
+    int cnt = 0;
+    if (i < m && (i == 0 || sv[i] != sv[i - 1])) {
+      int j = i + 1;
+      while (j < m && sv[j] == sv[i]) ++j;
+      cnt = j - i;
+    }
+    cv[i] = cnt;
+  }
   __syncthreads();
   if (threadIdx.x < 64) {
-    const double h = entropy_from_hist(hist, (int)range, m);
+    const double h = entropy_from_hist(cv, len, m);
     if (threadIdx.x == 0) bits[col] = h;
   }
   if (!huff) return;
   __syncthreads();
-  bitonic_sort(hist, NBIN_WIDE, threadIdx.x, 256, [] { __syncthreads(); });
+  bitonic_sort(cv, len, threadIdx.x, 256, sync);
   int nz = 0;
-  for (int b = threadIdx.x; b < NBIN_WIDE; b += 256) nz += hist[b] == 0;
+  for (int b = threadIdx.x; b < len; b += 256) nz += cv[b] == 0;
   for (int o = 32; o >= 1; o >>= 1) nz += __shfl_xor(nz, o, 64);
   if ((threadIdx.x & 63) == 0) nzs[threadIdx.x >> 6] = nz;
   __syncthreads();
   if (threadIdx.x == 0) {
     const int z = nzs[0] + nzs[1] + nzs[2] + nzs[3];
-    // the merged nodes go into the zero prefix; too many symbols: -1
-    huff[col] = (NBIN_WIDE - z <= z + 1) ? huffman_merge(hist, z, NBIN_WIDE, hist) : -1;
+    huff[col] = huffman_merge(cv, z, len, sv);   // at most len - 1 merged nodes
   }
 }
 

@@ -57,15 +57,41 @@ def test_entropy_narrow_wide_and_ragged():
     assert got[100] == 0.0
 
 
-def test_entropy_too_wide_is_nan_and_empty():
-    codes = np.zeros((64, 3), np.int32)
+def test_entropy_very_wide_columns():
+    """Columns spanning more than 32768 values are sorted instead of
+    histogrammed (run lengths as counts): many distinct values over a span
+    of 2e6, two far values among zeros, INT32 extremes, and m not a power of
+    two."""
+    rng = np.random.default_rng(13)
+    m, n = 1000, 70
+    codes = rng.integers(-3, 4, size=(m, n))
+    codes[:, 3] = rng.integers(-10**6, 10**6, size=m)           # ~1000 distinct values
+    codes[:, 4] = 0
+    codes[0, 4], codes[1, 4] = -20000, 20000                      # span 40001, 3 values
+    codes[:, 40] = rng.integers(-5, 5, size=m)
+    codes[::7, 40] = 2**31 - 1                                    # extremes, runs of equal codes
+    codes[::11, 40] = -2**31
+    codes[:, 69] = rng.integers(0, 40, size=m) * 1000             # span 39001, 40 values
+    _check(codes)
+
+
+def test_entropy_too_wide_for_sorting_is_nan_and_empty():
+    """A span above 32768 values with more than 16384 rows is not computed:
+    NaN bits and Huffman length -1; other columns are unaffected."""
+    m = 16385
+    codes = np.zeros((m, 3), np.int32)
     codes[0, 1] = -20000
     codes[1, 1] = 20000
+    codes[:, 2] = np.arange(m) % 5
     bits, _, huff = P.column_entropy(torch.from_numpy(codes).cuda(), huffman=True)
     torch.cuda.synchronize()
     b = to_np(bits)
-    assert np.isnan(b[1]) and b[0] == 0.0 and b[2] == 0.0
-    assert list(to_np(huff)) == [0, -1, 0]
+    assert np.isnan(b[1]) and b[0] == 0.0
+    want = O.column_entropy_bits(codes[:, [2]].astype(np.int64))
+    assert abs(b[2] - want[0]) <= TOL_BITS
+    h = to_np(huff)
+    assert h[0] == 0 and h[1] == -1
+    assert h[2] == O.column_huffman_bits(codes[:, [2]].astype(np.int64))[0]
     bits, mean = P.column_entropy(torch.zeros((0, 5), dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert np.all(to_np(bits) == 0) and float(mean.item()) == 0.0
