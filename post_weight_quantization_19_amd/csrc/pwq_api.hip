@@ -209,7 +209,13 @@ void carve_layer(Carver& c, int64_t m, int64_t n, int64_t ntok, bool has_x, bool
 extern "C" {
 
 const char* pwq_status_string(pwq_status s) {
-  switch (s) {
+  // A C caller may pass any integer; an enum object holding a value outside
+  // its enumerators' range may not be read as the enum in C++, so its bytes
+  // are read as an integer.
+  int32_t v;
+  static_assert(sizeof(s) == sizeof(v), "pwq_status is 32-bit");
+  __builtin_memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case PWQ_OK: return "PWQ_OK";
     case PWQ_ERR_INVALID_ARG: return "PWQ_ERR_INVALID_ARG";
     case PWQ_ERR_UNSUPPORTED: return "PWQ_ERR_UNSUPPORTED";
