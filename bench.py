@@ -423,7 +423,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the "
               "quantizer's rows are independent, and a multi-GPU run would shard them "
-              "with one all-reduce of H, which this build does not implement.",
+              "with one all-reduce of H, which this library does not implement.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   PWQ_OK = 0,
   PWQ_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum or combination      */
-  PWQ_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  PWQ_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement */
   PWQ_ERR_WORKSPACE = 3,     /* ws NULL, misaligned or smaller than needed  */
   PWQ_ERR_HIP = 4            /* a HIP runtime call failed                   */
 } pwq_status;
