@@ -541,14 +541,18 @@ __device__ __forceinline__ void trailing_tile(T* __restrict__ A, int n, int kfro
 }
 
 // fp32 trailing tile with 16-byte aligned rows (n % 4 == 0): the same update
-// as trailing_tile, with both operands loaded straight into registers.  Lane
-// l of a wave takes the 32 consecutive K values 32 (l/32) .. 32 (l/32) + 31
-// of its rows (eight 16-byte loads per row), so MFMA step s sums K = s and
-// K = 32 + s; the same order is used for both operands, so this is the
-// product over all 64 K, in a different rounding order.  No LDS and no
-// barriers: the 128 MFMAs of a wave run back to back.  Rows and columns past
-// n are clamped into the matrix (they only reach outputs that are not
+// as trailing_tile, with both operands loaded straight into registers as
+// v_mfma_f32_16x16x4f32 operands.  Wave (wm, wn) takes rows 64 wm ..,
+// columns 64 wn .. of the tile as 4 x 4 accumulators of 16 x 16; lane
+// (r, q) = (l % 16, l / 16) holds K values 16 g + 4 q .. 16 g + 4 q + 3 of
+// its row of each 16-row block (one 16-byte load each, so the 4 lanes of a
+// row read 64 contiguous bytes and a load touches 16 rows), and MFMA step
+// s of group g sums K = 16 g + 4 q + s over the lane groups q; both
+// operands use the same order, so this is the product over all 64 K in a
+// different rounding order.  No LDS and no barriers.  Rows and columns
+// past n are clamped into the matrix (they only reach outputs that are not
 // stored).
+// 16x16 result layout: lane l, register r -> row 4 (l / 16) + r, col l % 16.
 __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int n, int kfrom,
                                                       int npan, int base, int t) {
   constexpr int TB = 128;
@@ -562,70 +566,67 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
   }
   const int r0 = base + ti * TB, c0 = base + tj * TB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, li = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1, lq = lane >> 4, lr = lane & 15;
   // acc = A_ij - sum_k P_ik P_jk: the accumulators start from the tile.
   // The tile's addresses are formed from opaque copies of n, here and at the
   // stores, so the compiler cannot keep 64 of them live through the K loop.
-  f32x16_t acc[2][2];
+  f32x4_t acc[4][4];
   {
     int nl = n;
     asm volatile("" : "+s"(nl));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gr = min(r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3), nl - 1);
-          const int gc = min(c0 + wn * 64 + j * 32 + li, nl - 1);
+        for (int r = 0; r < 4; ++r) {
+          const int gr = min(r0 + wm * 64 + i * 16 + 4 * lq + r, nl - 1);
+          const int gc = min(c0 + wn * 64 + j * 16 + lr, nl - 1);
           acc[i][j][r] = A[(int64_t)gr * nl + gc];
         }
   }
-  const float* pa[2];
-  const float* pb[2];
+  // Half a panel's operands (K groups g = 2 h, 2 h + 1 of each lane's rows):
+  // 16 16-byte loads per lane, their row addresses formed here (eight row
+  // pointers kept live would not fit beside the accumulators and operands).
+  const int ra = r0 + wm * 64 + lr, rb = c0 + wn * 64 + lr;
+  auto load = [&](float4 (&a)[4][2], float4 (&b)[4][2], int kc, int h) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    pa[i] = A + (int64_t)min(r0 + wm * 64 + i * 32 + li, n - 1) * n + 32 * g;
-    pb[i] = A + (int64_t)min(c0 + wn * 64 + i * 32 + li, n - 1) * n + 32 * g;
-  }
-  // Half a panel's operands (K steps 16 h .. 16 h + 15 of each lane's
-  // 32): 16 16-byte loads per lane.
-  auto load = [&](float4 (&a)[2][4], float4 (&b)[2][4], int kc, int h) {
+    for (int i = 0; i < 4; ++i) {
+      const float* pa = A + (int64_t)min(ra + 16 * i, n - 1) * n + 4 * lq + kc + 32 * h;
+      const float* pb = A + (int64_t)min(rb + 16 * i, n - 1) * n + 4 * lq + kc + 32 * h;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[i][q] = *(const float4*)(pa[i] + kc + 16 * h + 4 * q);
-        b[i][q] = *(const float4*)(pb[i] + kc + 16 * h + 4 * q);
+      for (int gg = 0; gg < 2; ++gg) {
+        a[i][gg] = *(const float4*)(pa + 16 * gg);
+        b[i][gg] = *(const float4*)(pb + 16 * gg);
       }
+    }
   };
-  auto mma = [&](const float4 (&a)[2][4], const float4 (&b)[2][4]) {
+  auto mma = [&](const float4 (&a)[4][2], const float4 (&b)[4][2]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float av[2], bv[2];
+        float av[4], bv[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          av[i] = -(&a[i][q].x)[e];
-          bv[i] = (&b[i][q].x)[e];
+        for (int i = 0; i < 4; ++i) {
+          av[i] = -(&a[i][gg].x)[e];
+          bv[i] = (&b[i][gg].x)[e];
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
   };
   // Two half-panel operand sets in turn: the next half's loads are issued
-  // before the current half's 64 MFMAs (a scheduling barrier keeps them
+  // before the current half's 128 MFMAs (a scheduling barrier keeps them
   // there; the scheduler would otherwise spread them among the MFMAs), so
-  // their latency runs under the MFMAs; the wait before the MFMAs leaves
-  // the newer loads in flight (vector memory counts complete in order).
-  // The MFMAs take K in the same order as a whole panel at a time.
-  // The last panel is peeled off, so that every wait inside the loop sees
-  // the same loads in flight.
-  float4 a0[2][4], b0[2][4], a1[2][4], b1[2][4];
+  // their latency runs under the MFMAs; the wait before the MFMAs leaves the
+  // newer loads in flight (vector memory counts complete in order).  The
+  // last panel is peeled off, so that every wait inside the loop sees the
+  // same loads in flight.
+  float4 a0[4][2], b0[4][2], a1[4][2], b1[4][2];
   load(a0, b0, kfrom, 0);
   int kc = kfrom;
   for (int pc = 0; pc + 1 < npan; ++pc, kc += NB) {
@@ -644,13 +645,13 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
   int ns = n;
   asm volatile("" : "+s"(ns));
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int gc = c0 + wn * 64 + j * 32 + li;
+      for (int r = 0; r < 4; ++r) {
+        const int gr = r0 + wm * 64 + i * 16 + 4 * lq + r;
+        const int gc = c0 + wn * 64 + j * 16 + lr;
         if (gr < ns && gc <= gr) A[(int64_t)gr * ns + gc] = acc[i][j][r];
       }
 }
