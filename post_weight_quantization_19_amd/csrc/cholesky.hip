@@ -656,6 +656,109 @@ __device__ __forceinline__ void trailing_tile_f32_reg(float* __restrict__ A, int
       }
 }
 
+// fp64 trailing tile with 16-byte aligned rows (n even): the register form
+// of trailing_tile for doubles, as trailing_tile_f32_reg with
+// v_mfma_f64_16x16x4f64: lane (r, q) = (l % 16, l / 16) holds K values
+// 16 g + 4 q .. 16 g + 4 q + 3 of its row of each 16-row block (two 16-byte
+// loads), MFMA step s of group g sums K = 16 g + 4 q + s over the lane
+// groups q, and the operands of one K group (16 loads per lane) are
+// double-buffered.  The fp64 kernel runs one workgroup per CU, so a lane
+// has room for the accumulators (128 registers) and both operand sets.
+// 16x16 f64 result layout: lane l, register r -> row 4 r + l / 16, col l % 16.
+__device__ __forceinline__ void trailing_tile_f64_reg(double* __restrict__ A, int n, int kfrom,
+                                                      int npan, int base, int t) {
+  constexpr int TB = 128;
+  int ti, tj;
+  {
+    int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    while (r * (r + 1) / 2 > t) --r;
+    ti = r;
+    tj = t - r * (r + 1) / 2;
+  }
+  const int r0 = base + ti * TB, c0 = base + tj * TB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, lq = lane >> 4, lr = lane & 15;
+  f64x4_t acc[4][4];
+  {
+    int nl = n;
+    asm volatile("" : "+s"(nl));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gr = min(r0 + wm * 64 + i * 16 + 4 * r + lq, nl - 1);
+          const int gc = min(c0 + wn * 64 + j * 16 + lr, nl - 1);
+          acc[i][j][r] = A[(int64_t)gr * nl + gc];
+        }
+  }
+  const int ra = r0 + wm * 64 + lr, rb = c0 + wn * 64 + lr;
+  // one K group (16 K values; four doubles per lane and row block): step st
+  // is group st % 4 of panel st / 4
+  auto load = [&](double2 (&a)[4][2], double2 (&b)[4][2], int st) {
+    const int kc = kfrom + NB * (st >> 2) + 16 * (st & 3) + 4 * lq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double* pa = A + (int64_t)min(ra + 16 * i, n - 1) * n + kc;
+      const double* pb = A + (int64_t)min(rb + 16 * i, n - 1) * n + kc;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        a[i][v] = *(const double2*)(pa + 2 * v);
+        b[i][v] = *(const double2*)(pb + 2 * v);
+      }
+    }
+  };
+  auto mma = [&](const double2 (&a)[4][2], const double2 (&b)[4][2]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = -(e & 1 ? a[i][e >> 1].y : a[i][e >> 1].x);
+        bv[i] = (e & 1 ? b[i][e >> 1].y : b[i][e >> 1].x);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // two operand sets in turn, one K group ahead (4 npan steps, an even
+  // count; the last two are peeled so every wait in the loop sees the same
+  // loads in flight)
+  double2 a0[4][2], b0[4][2], a1[4][2], b1[4][2];
+  const int nst = 4 * npan;
+  load(a0, b0, 0);
+  for (int st = 0; st + 2 < nst; st += 2) {
+    load(a1, b1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    load(a0, b0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+  }
+  load(a1, b1, nst - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(a0, b0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(a1, b1);
+  int ns = n;
+  asm volatile("" : "+s"(ns));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gr = r0 + wm * 64 + i * 16 + 4 * r + lq;
+        const int gc = c0 + wn * 64 + j * 16 + lr;
+        if (gr < ns && gc <= gr) A[(int64_t)gr * ns + gc] = acc[i][j][r];
+      }
+}
+
 // 64 rows r0 .. r0+63, columns kc .. kc+63 of fp32 A into LDS (row pitch
 // NB + 1), for 16-byte aligned rows: four 16-byte loads per thread from rows
 // clamped into the matrix, rows past n stored as zeros.
@@ -718,6 +821,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void chol_step(T* __re
     if constexpr (sizeof(T) == 4) {
       if (n % 4 == 0 && ((uintptr_t)A & 15) == 0) {
         trailing_tile_f32_reg(A, n, kfrom, npan, k0 + 2 * NB, blockIdx.x - np);
+        return;
+      }
+    } else {
+      if (n % 2 == 0 && ((uintptr_t)A & 15) == 0) {
+        trailing_tile_f64_reg(A, n, kfrom, npan, k0 + 2 * NB, blockIdx.x - np);
         return;
       }
     }
