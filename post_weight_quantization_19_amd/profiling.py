@@ -192,12 +192,14 @@ def kernels_markdown(trace, sq, fetch, write, kernels, commands, title, peaks):
         "Launch statistics come from the kernel trace; every other column is a total over all "
         "dispatches of the kernel in the counter run (MOPS x 512 = flop) divided by their summed "
         "durations in that run.  MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x the "
-        "summed duration x 2.4 GHz.  HBM "
+        "summed duration x 2.4 GHz.  Clock: GRBM_GUI_ACTIVE / (8 XCDs x duration), "
+        "the shader clock the kernel ran at, shown for kernels of 1 ms or more (the counters "
+        "of shorter dispatches include cycles outside them).  HBM "
         f"bytes: FETCH_SIZE x {ff:.3f} and WRITE_SIZE x {wf:.3f} KiB (factors from the 1 GiB "
         "device copy of each run).", "",
         "| kernel | calls | avg (us) | total (ms) | MFMA TFLOP/s | % of peak | MFMA busy "
-        "| read GB/dispatch | write GB/dispatch | HBM GB/s |",
-        "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        "| clock (GHz) | read GB/dispatch | write GB/dispatch | HBM GB/s |",
+        "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for k in kernels:
         t = st.get(k)
         sq_v = pick(sqd, k)
@@ -206,6 +208,8 @@ def kernels_markdown(trace, sq, fetch, write, kernels, commands, title, peaks):
                            x.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) +
                            x.get("SQ_INSTS_VALU_MFMA_MOPS_F64", 0.0) for x in sq_v)
         busy = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in sq_v) / (1024 * ns * 2.4)
+        gui = sum(x.get("GRBM_GUI_ACTIVE", 0.0) for x in sq_v)
+        clk = f"{gui / (8 * ns):.2f}" if gui > 0 and ns / len(sq_v) >= 1e6 else "—"
         peak = peaks.get(k)
         tf = flop / ns / 1e3
         fv, wv = pick(fd, k), pick(wd, k)
@@ -215,7 +219,7 @@ def kernels_markdown(trace, sq, fetch, write, kernels, commands, title, peaks):
         out.append(
             f"| {k} | {t['calls'] if t else '-'} | {t['avg_us'] if t else 0:.1f} | "
             f"{t['total_ms'] if t else 0:.3f} | {tf:.1f} | "
-            f"{(100 * tf / peak) if peak else float('nan'):.1f} | {busy:.3f} | "
+            f"{(100 * tf / peak) if peak else float('nan'):.1f} | {busy:.3f} | {clk} | "
             f"{rd / len(fv) / 1e9:.4f} | {wr / len(wv) / 1e9:.4f} | "
             f"{(rd + wr) / (fns / 2) :.1f} |")
     return "\n".join(out) + "\n"
