@@ -414,6 +414,12 @@ def oaem_bench(args):
 
 def main():
     args = parse()
+    import synth
+    if synth.config(args.config).wdtype != "bf16":
+        print(f"bench.py: config {args.config} ({synth.config(args.config).name}, fp32 weights "
+              "and activations) is a parity-test size; the timed layers are configs 2-5 "
+              "(bf16 weights)", file=sys.stderr)
+        sys.exit(2)
     if args.ssqr is not None and args.gpus == 1:
         ssqr_bench(args)
         return
