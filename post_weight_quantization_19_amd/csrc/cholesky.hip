@@ -18,9 +18,12 @@
 //                  diagonal block and its own 64 panel rows (4 waves, lane =
 //                  row, rank-4 column groups through LDS), so L_kk and
 //                  L_ik = A_ik L_kk^-T come out of one pass
-//   trailing role  A_ij -= L_ik L_jk^T as 128x128 MFMA tiles
-//                  (v_mfma_f32_32x32x2f32 / v_mfma_f64_16x16x4f64); both
-//                  operands are panel rows, contiguous along K.
+//   trailing role  A_ij -= L_ik L_jk^T as 128x128 MFMA tiles, several
+//                  pending panels at once (lazy_panels); with 16-byte
+//                  aligned rows the operands go straight from memory into
+//                  registers (v_mfma_f32_16x16x4f32 / v_mfma_f64_16x16x4f64),
+//                  otherwise through LDS; both operands are panel rows,
+//                  contiguous along K.
 // A non-positive or non-finite pivot stops the factorization and records the
 // LAPACK-style order of the failing minor; every later kernel sees the flag
 // and returns at once.

@@ -24,9 +24,13 @@
 //    then folds e * l_kj into its own open columns.  Rows of L for the block
 //    are staged in LDS (the diagonal and the upper triangle stored as zero,
 //    so updates of already-decided columns add exactly 0).
-//  * after a block, its errors E [m x B] reach every earlier column in one
-//    MFMA GEMM, acc[:, :j0] += E L[blk, :j0] (v_mfma_f32_32x32x2f32 or
-//    v_mfma_f64_16x16x4f64), written (not read) on the first block.
+//  * the errors E reach the earlier columns through MFMA GEMMs,
+//    acc[:, cols] += E L[blk, cols], in groups of blocks (256 columns in
+//    fp32, 512 in fp64): after each block, its errors reach the open columns
+//    of its own group; after a group's last block, the whole group's errors
+//    reach every column before the group in one pass, so acc is read and
+//    written once per group.  acc is written (not read) where a column is
+//    first touched.
 //  * losses are accumulated per workgroup in fp64 and summed in a fixed
 //    order by a final one-workgroup kernel.
 #include "pwq_device.h"
