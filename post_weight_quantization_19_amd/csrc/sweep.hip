@@ -404,12 +404,15 @@ __global__ __launch_bounds__(256) void sweep_block(SweepArgs<T> a, int j0, int l
 // values (their loads are issued first, so their latency overlaps the
 // operand loads and the MFMAs), K runs in chunks of 32 staged through LDS
 // with the next chunk's global loads in flight while the current chunk's
-// MFMAs run, and the tile is stored once.
+// MFMAs run, and the tile is stored once.  fp32 rows that are not 16-byte
+// aligned (the aligned ones take the kernels below); fp64 has its own form,
+// lazy_update_f64.
 template <typename T>
-__global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void lazy_update(
+__global__ __launch_bounds__(256, 2) void lazy_update(
     const T* __restrict__ E, int B, int e_off, int kb, const T* __restrict__ L, int n,
     int k_lo, int c_lo, int j0, int m, T* __restrict__ acc, int first,
     const DevFlags* flags) {
+  static_assert(sizeof(T) == 4, "fp32 only");
   constexpr int TM = 128, KC = 32, LDA = KC + 1, LDB = TM + 1;
   constexpr int PE = TM * KC / 256;   // elements per thread per operand
   __shared__ T Es[TM * LDA];
@@ -440,94 +443,47 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void lazy_update(
     }
   };
 
-  if constexpr (sizeof(T) == 4) {
-    // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
-    f32x16_t cc[2][2];
+  // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
+  f32x16_t cc[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          cc[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
-        }
-    gload(0);
-    for (int kc = 0; kc < kb; kc += KC) {
-      __syncthreads();
-      lstore();
-      __syncthreads();
-      if (kc + KC < kb) gload(kc + KC);
-#pragma unroll
-      for (int k = 0; k < KC; k += 2) {
-        const int ko = k + (lane >> 5);
-        const float a0 = Es[(wm * 64 + (lane & 31)) * LDA + ko];
-        const float a1 = Es[(wm * 64 + 32 + (lane & 31)) * LDA + ko];
-        const float b0 = Lt[ko * LDB + wn * 64 + (lane & 31)];
-        const float b1 = Lt[ko * LDB + wn * 64 + 32 + (lane & 31)];
-        cc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, cc[0][0], 0, 0, 0);
-        cc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, cc[0][1], 0, 0, 0);
-        cc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, cc[1][0], 0, 0, 0);
-        cc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, cc[1][1], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+        cc[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0f;
       }
+  gload(0);
+  for (int kc = 0; kc < kb; kc += KC) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (kc + KC < kb) gload(kc + KC);
+#pragma unroll
+    for (int k = 0; k < KC; k += 2) {
+      const int ko = k + (lane >> 5);
+      const float a0 = Es[(wm * 64 + (lane & 31)) * LDA + ko];
+      const float a1 = Es[(wm * 64 + 32 + (lane & 31)) * LDA + ko];
+      const float b0 = Lt[ko * LDB + wn * 64 + (lane & 31)];
+      const float b1 = Lt[ko * LDB + wn * 64 + 32 + (lane & 31)];
+      cc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, cc[0][0], 0, 0, 0);
+      cc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, cc[0][1], 0, 0, 0);
+      cc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, cc[1][0], 0, 0, 0);
+      cc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, cc[1][1], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
-          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[i][j][r];
-        }
-  } else {
-    // 16x16 f64 result layout: lane l, register r -> row 4r + l/16, col l%16
-    f64x4_t cc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
-          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          cc[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0;
-        }
-    gload(0);
-    for (int kc = 0; kc < kb; kc += KC) {
-      __syncthreads();
-      lstore();
-      __syncthreads();
-      if (kc + KC < kb) gload(kc + KC);
-#pragma unroll 2
-      for (int k = 0; k < KC; k += 4) {
-        const int ko = k + (lane >> 4);
-        double av[4], bv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          av[i] = Es[(wm * 64 + i * 16 + (lane & 15)) * LDA + ko];
-          bv[i] = Lt[ko * LDB + wn * 64 + i * 16 + (lane & 15)];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            cc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], cc[i][j], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gr = r0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
-          const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
-          if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[i][j][r];
-        }
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int gc = c0 + wn * 64 + j * 32 + (lane & 31);
+        if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[i][j][r];
+      }
 }
 
 // fp32 form of the same update for 16-byte aligned rows of L (n % 4 == 0),
@@ -916,6 +872,94 @@ __global__ __launch_bounds__(256) void near_update_f32(
     }
 }
 
+// fp64 form of the generic update: the same tiles and K order (chunks of
+// 32 through LDS, v_mfma_f64_16x16x4f64), with eight waves of 32 x 64 per
+// 128 x 128 tile, so that each SIMD has two waves to cover the other's LDS
+// and barrier waits, and a double-buffered LDS stage: the next chunk's
+// global loads are in flight under the current chunk's MFMAs and are
+// written to the other buffer afterwards, one barrier per chunk.
+constexpr int F64U_NT = 512;
+__global__ __launch_bounds__(F64U_NT, 1) void lazy_update_f64(
+    const double* __restrict__ E, int B, int e_off, int kb, const double* __restrict__ L, int n,
+    int k_lo, int c_lo, int j0, int m, double* __restrict__ acc, int first) {
+  constexpr int TM = 128, KC = 32, LDA = KC + 1, LDB = TM + 1;
+  constexpr int PE = TM * KC / F64U_NT;   // elements per thread per operand
+  __shared__ double Es[2][TM * LDA];
+  __shared__ double Lt[2][KC * LDB];
+  E += e_off;
+  const int c0 = c_lo + blockIdx.x * TM, r0 = blockIdx.y * TM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;   // rows 32 wm, columns 64 wn of the tile
+  double re[PE], rl[PE];
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int e = tid + F64U_NT * i;
+      const int r = e / KC, k = e % KC;          // E tile [TM][KC]
+      re[i] = (r0 + r < m && kc + k < kb) ? E[(int64_t)(r0 + r) * B + kc + k] : 0.0;
+      const int kr = e / TM, cc = e % TM;        // L tile [KC][TM]
+      rl[i] = (kc + kr < kb && c0 + cc < j0) ? L[(int64_t)(k_lo + kc + kr) * n + c0 + cc] : 0.0;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const int e = tid + F64U_NT * i;
+      Es[buf][(e / KC) * LDA + e % KC] = re[i];
+      Lt[buf][(e / TM) * LDB + e % TM] = rl[i];
+    }
+  };
+  // 16x16 f64 result layout: lane l, register r -> row 4r + l/16, col l%16
+  f64x4_t cc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gr = r0 + wm * 32 + i * 16 + 4 * r + (lane >> 4);
+        const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+        cc[i][j][r] = (!first && gr < m && gc < j0) ? acc[(int64_t)gr * n + gc] : 0.0;
+      }
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int nch = (kb + KC - 1) / KC;
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) gload((c + 1) * KC);
+    const double* Eb = Es[buf];
+    const double* Lb = Lt[buf];
+#pragma unroll 2
+    for (int k = 0; k < KC; k += 4) {
+      const int ko = k + (lane >> 4);
+      double av[2], bv[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) av[i] = Eb[(wm * 32 + i * 16 + (lane & 15)) * LDA + ko];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Lb[ko * LDB + wn * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          cc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], cc[i][j], 0, 0, 0);
+    }
+    // the other buffer's readers (chunk c - 1) passed the previous barrier
+    if (c + 1 < nch) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gr = r0 + wm * 32 + i * 16 + 4 * r + (lane >> 4);
+        const int gc = c0 + wn * 64 + j * 16 + (lane & 15);
+        if (gr < m && gc < j0) acc[(int64_t)gr * n + gc] = cc[i][j][r];
+      }
+}
+
 // One lazy update launch: acc[:, c_lo:j0] (+)= E[:, e_off:e_off+kb] L[k_lo:k_lo+kb, c_lo:j0]
 // (E with leading dimension ldE).
 template <typename T>
@@ -948,8 +992,12 @@ void update_launch(const T* E, int ldE, int e_off, int kb, const T* L, int n, in
       // wider K: the generic kernel below
     }
   }
-  lazy_update<T><<<g, 256, 0, st>>>(E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first,
-                                    flags);
+  if constexpr (sizeof(T) == 8)
+    lazy_update_f64<<<g, F64U_NT, 0, st>>>(E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc,
+                                           first);
+  else
+    lazy_update<T><<<g, 256, 0, st>>>(E, ldE, e_off, kb, L, n, k_lo, c_lo, j0, m, acc, first,
+                                      flags);
 }
 
 // ---------------------------------------------------------------- finalize

@@ -24,6 +24,9 @@ CASES = {
     "upproj_small_ragged": (synth.config(3).resized(m=100, n=256, ntok=3000), "f32", None),
     "downproj_small_ragged": (synth.config(4).resized(m=64, n=576, ntok=2048), "f32", None),
     "zsic_small": (synth.config(5).resized(m=48, n=512), "f64", 0.001),
+    # fp64 with three row tiles of the update (the last ragged) and a ragged
+    # last group of blocks
+    "zsic_mid_ragged": (synth.config(5).resized(m=300, n=1100), "f64", 0.001),
     # n % 4 != 0: rows of L are not 16-byte aligned (generic update kernel)
     "tiny_unaligned": (synth.config(1).resized(m=40, n=130, ntok=1000), "f32", None),
     # n % 4 == 0 but n % 64 != 0: 16-byte rows with a ragged last panel and
