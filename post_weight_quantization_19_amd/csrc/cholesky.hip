@@ -35,13 +35,21 @@ namespace pwq {
 namespace {
 
 constexpr int NB = 64;   // panel width
-// Panels per trailing update.  fp64 trailing tiles are bound by their
-// read-modify-write, so it pays to apply several panels at once.  fp32 tiles
-// are too once the trailing triangle is large (n = 14336: 20.8 ms with one
-// panel per pass, 17.2 with two, 16.3 with four, 16.8 with eight); on small
-// matrices the wider K only lengthens the panel role (n = 4096: 1.58 ms with
-// one or two, 1.78 with four).
-template <typename T> int lazy_panels(int n) { return sizeof(T) == 8 ? 8 : (n >= 8192 ? 4 : 1); }
+// Panels per trailing update.  Applying several pending panels at once pays
+// the trailing tiles' read-modify-write once per pass, but every panel in
+// between applies the pending ones to itself, which lengthens the serial
+// panel role; the balance moves with n.  Measured (register trailing tiles):
+//   fp32  n = 14336: 19.5 / 15.8 / 14.4 / 15.0 ms with 1 / 2 / 4 / 8;
+//         n = 8192: 4.92 / 4.56 / 4.62 / 5.22;  n = 4096: 1.51 / 1.50 / 1.64
+//   fp64  n = 28672: 195 / 184 / 180 / 179 / 182 ms with 4 / 6 / 8 / 12 / 16;
+//         n = 16384: 48.3 / 42.1 / 41.3 / 41.4 with 2 / 4 / 6 / 8;
+//         n = 12288: 29.8 / 23.3 / 21.3 with 1 / 2 / 4;
+//         n = 8192: 9.98 / 8.78 / 8.86 / 9.94 with 1 / 2 / 4 / 8;
+//         n = 4096: 2.45 / 2.57 / 2.90 / 3.54 with 1 / 2 / 4 / 8.
+template <typename T> int lazy_panels(int n) {
+  if (sizeof(T) == 8) return n <= 4096 ? 1 : (n <= 8192 ? 2 : (n <= 12288 ? 4 : 8));
+  return n >= 8192 ? 4 : 1;
+}
 
 // lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;
 // fixed-order fp64 reduction.
