@@ -773,29 +773,6 @@ __device__ __forceinline__ void trailing_tile_f64_reg(double* __restrict__ A, in
 // 64 rows r0 .. r0+63, columns kc .. kc+63 of fp32 A into LDS (row pitch
 // NB + 1), for 16-byte aligned rows: four 16-byte loads per thread from rows
 // clamped into the matrix, rows past n stored as zeros.
-template <typename T>
-__device__ __forceinline__ void rows_to_lds_vec(T* __restrict__ dst, const T* __restrict__ A,
-                                                int n, int r0, int kc, int tid) {
-  if constexpr (sizeof(T) == 4) {
-    constexpr int LD = NB + 1;
-    float4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i, r = e >> 4, c4 = (e & 15) * 4;
-      v[i] = *(const float4*)(A + (int64_t)min(r0 + r, n - 1) * n + kc + c4);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i, r = e >> 4, c4 = (e & 15) * 4;
-      const bool ok = r0 + r < n;
-      dst[r * LD + c4 + 0] = ok ? v[i].x : 0.0f;
-      dst[r * LD + c4 + 1] = ok ? v[i].y : 0.0f;
-      dst[r * LD + c4 + 2] = ok ? v[i].z : 0.0f;
-      dst[r * LD + c4 + 3] = ok ? v[i].w : 0.0f;
-    }
-  }
-}
-
 // One step with look-ahead, given the finished panel at k0 (columns
 // k0..k0+63 of every row >= k0 hold L).  The trailing update is applied
 // lazily, several panels at a time: panels kfrom/64 .. k0/64 (npan of them)
@@ -853,26 +830,104 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1) void chol_step(T* __re
   Mfma64<T> u0, u1;
   u0.zero();
   u1.zero();
-  // fp32 rows of 16-byte multiples: the pending-panel rows come in with
-  // 16-byte loads from rows clamped into the matrix (rows past n are zeroed
-  // after the load)
-  const bool vec = sizeof(T) == 4 && n % 4 == 0 && ((uintptr_t)A & 15) == 0;
-  for (int pc = 0; pc < npan; ++pc) {
+  bool npan_done = false;   // the pending panels were applied by a vector path below
+  if constexpr (sizeof(T) == 8) {
+    if (n % 2 == 0 && ((uintptr_t)A & 15) == 0) {
+      // fp64 rows of 16-byte multiples: the pending-panel rows come in as
+      // 16-byte pairs from rows clamped into the matrix (rows past n are
+      // zeroed on the way into LDS), and the next chunk's loads are in
+      // flight while the current chunk's MFMAs run
+      double2 qv[8], sv[8];
+      auto vload = [&](int kc) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = tid + 256 * i, r = e >> 5, c2 = (e & 31) * 2;
+          qv[i] = *(const double2*)(A + (int64_t)min(p1 + r, n - 1) * n + kc + c2);
+          if (b > 0)
+            sv[i] = *(const double2*)(A + (int64_t)min(p1 + NB * b + r, n - 1) * n + kc + c2);
+        }
+      };
+      auto vstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = tid + 256 * i, r = e >> 5, c2 = (e & 31) * 2;
+          const bool okq = p1 + r < n;
+          Q[r * LD + c2] = okq ? qv[i].x : 0.0;
+          Q[r * LD + c2 + 1] = okq ? qv[i].y : 0.0;
+          if (b > 0) {
+            const bool oks = p1 + NB * b + r < n;
+            S[r * LD + c2] = oks ? sv[i].x : 0.0;
+            S[r * LD + c2 + 1] = oks ? sv[i].y : 0.0;
+          }
+        }
+      };
+      vload(kfrom);
+      for (int pc = 0; pc < npan; ++pc) {
+        if (pc > 0) __syncthreads();   // the previous chunk's LDS reads are done
+        vstore();
+        __syncthreads();
+        if (pc + 1 < npan) vload(kfrom + (pc + 1) * NB);
+        u0.add(Q, Q);
+        if (b > 0) u1.add(S, Q);
+      }
+      npan_done = true;
+    }
+  } else {
+    if (n % 4 == 0 && ((uintptr_t)A & 15) == 0) {
+      // fp32 rows of 16-byte multiples: the same with 16-byte loads, the
+      // next chunk's loads in flight under the current chunk's MFMAs
+      float4 qv[4], sv[4];
+      auto vload = [&](int kc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = tid + 256 * i, r = e >> 4, c4 = (e & 15) * 4;
+          qv[i] = *(const float4*)(A + (int64_t)min(p1 + r, n - 1) * n + kc + c4);
+          if (b > 0)
+            sv[i] = *(const float4*)(A + (int64_t)min(p1 + NB * b + r, n - 1) * n + kc + c4);
+        }
+      };
+      auto vstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = tid + 256 * i, r = e >> 4, c4 = (e & 15) * 4;
+          const bool okq = p1 + r < n;
+          Q[r * LD + c4 + 0] = okq ? qv[i].x : 0.0f;
+          Q[r * LD + c4 + 1] = okq ? qv[i].y : 0.0f;
+          Q[r * LD + c4 + 2] = okq ? qv[i].z : 0.0f;
+          Q[r * LD + c4 + 3] = okq ? qv[i].w : 0.0f;
+          if (b > 0) {
+            const bool oks = p1 + NB * b + r < n;
+            S[r * LD + c4 + 0] = oks ? sv[i].x : 0.0f;
+            S[r * LD + c4 + 1] = oks ? sv[i].y : 0.0f;
+            S[r * LD + c4 + 2] = oks ? sv[i].z : 0.0f;
+            S[r * LD + c4 + 3] = oks ? sv[i].w : 0.0f;
+          }
+        }
+      };
+      vload(kfrom);
+      for (int pc = 0; pc < npan; ++pc) {
+        if (pc > 0) __syncthreads();   // the previous chunk's LDS reads are done
+        vstore();
+        __syncthreads();
+        if (pc + 1 < npan) vload(kfrom + (pc + 1) * NB);
+        u0.add(Q, Q);
+        if (b > 0) u1.add(S, Q);
+      }
+      npan_done = true;
+    }
+  }
+  // rows that are not 16-byte aligned: element loads, chunk by chunk
+  for (int pc = 0; pc < npan && !npan_done; ++pc) {
     const int kc = kfrom + pc * NB;
     if (pc > 0) __syncthreads();   // the previous chunk's LDS reads are done
-    if (vec) {
-      rows_to_lds_vec(Q, A, n, p1, kc, tid);
-      if (b > 0) rows_to_lds_vec(S, A, n, p1 + NB * b, kc, tid);
-    } else {
-      tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
-        return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + kc + k] : (T)0;
+    tile_to_lds<T, 64, NB, 256, LD>(Q, tid, [&](int r, int k) {
+      return (p1 + r < n) ? A[(int64_t)(p1 + r) * n + kc + k] : (T)0;
+    });
+    if (b > 0)
+      tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
+        const int row = p1 + NB * b + r;
+        return (row < n) ? A[(int64_t)row * n + kc + k] : (T)0;
       });
-      if (b > 0)
-        tile_to_lds<T, 64, NB, 256, LD>(S, tid, [&](int r, int k) {
-          const int row = p1 + NB * b + r;
-          return (row < n) ? A[(int64_t)row * n + kc + k] : (T)0;
-        });
-    }
     __syncthreads();
     u0.add(Q, Q);
     if (b > 0) u1.add(S, Q);
