@@ -39,7 +39,8 @@ constexpr int NB = 64;   // panel width
 // the trailing tiles' read-modify-write once per pass, but every panel in
 // between applies the pending ones to itself, which lengthens the serial
 // panel role; the balance moves with n.  Measured (register trailing tiles):
-//   fp32  n = 14336: 19.5 / 15.8 / 14.4 / 15.0 ms with 1 / 2 / 4 / 8;
+//   fp32  n = 28672: 84.6 / 81.1 ms with 4 / 8;  n = 20480: 34.6 / 34.0;
+//         n = 14336: 19.5 / 15.8 / 14.4 / 15.0 ms with 1 / 2 / 4 / 8;
 //         n = 8192: 4.92 / 4.56 / 4.62 / 5.22;  n = 4096: 1.51 / 1.50 / 1.64
 //   fp64  n = 28672: 195 / 184 / 180 / 179 / 182 ms with 4 / 6 / 8 / 12 / 16;
 //         n = 16384: 48.3 / 42.1 / 41.3 / 41.4 with 2 / 4 / 6 / 8;
@@ -48,7 +49,7 @@ constexpr int NB = 64;   // panel width
 //         n = 4096: 2.45 / 2.57 / 2.90 / 3.54 with 1 / 2 / 4 / 8.
 template <typename T> int lazy_panels(int n) {
   if (sizeof(T) == 8) return n <= 4096 ? 1 : (n <= 8192 ? 2 : (n <= 12288 ? 4 : 8));
-  return n >= 8192 ? 4 : 1;
+  return n >= 20480 ? 8 : (n >= 8192 ? 4 : 1);
 }
 
 // lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;

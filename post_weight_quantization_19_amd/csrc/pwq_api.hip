@@ -356,6 +356,7 @@ pwq_status pwq_grid_steps(const void* W, int32_t wdtype, int64_t m, int64_t n, i
 
 size_t pwq_sweep_workspace_size(int64_t m, int64_t n, int32_t block, int32_t prec) {
   if (m < 0 || n <= 0 || !valid_block(block)) return 0;
+  if (prec != PWQ_F32 && prec != PWQ_F64) return 0;
   Carver c(nullptr);
   c.take(sizeof(DevFlags));
   SweepWs w;

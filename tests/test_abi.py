@@ -148,6 +148,7 @@ def test_workspace_sizes_grow_with_the_problem():
     c = L.pwq_quant_layer_workspace_size(2048, 1024, 8192, 1, 0, 128, 2)
     assert 0 < a < b < c
     assert L.pwq_sweep_workspace_size(64, 128, 100, 0) == 0
+    assert L.pwq_sweep_workspace_size(64, 128, 128, 7) == 0       # no such precision
     assert L.pwq_quant_layer_workspace_size(64, 0, 0, 0, 0, 128, 0) == 0
 
 

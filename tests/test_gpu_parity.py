@@ -121,17 +121,21 @@ def test_cholesky_stage(layers, prec, tol):
     assert rel_fro(Lg, Lo) <= tol
 
 
-@pytest.mark.parametrize("n", [8200, 8256])
+@pytest.mark.parametrize("n", [8200, 8256, 20544])
 def test_cholesky_large_fp32(n):
     """From n = 8192 the fp32 factor applies four pending panels per pass
-    over the trailing triangle; a ragged last panel (8200) and an aligned
-    size (8256), against the oracle's fp64 factor of the same float32 input."""
+    over the trailing triangle, from n = 20480 eight; a ragged last panel
+    (8200), an aligned size (8256) and a size whose last 128-column tile is
+    ragged (20544), against the oracle's fp64 factor of the same float32
+    input."""
     rng = np.random.default_rng(n)
-    A = rng.standard_normal((n, n + 512)).astype(np.float32)
-    H = A @ A.T
+    A = torch.from_numpy(rng.standard_normal((n, n + 512), dtype=np.float32)).cuda()
+    Hg = A @ A.T
     del A
+    torch.cuda.synchronize()
+    H = Hg.cpu().numpy()
     print(f"[cholesky] fp32 n={n}", flush=True)
-    L, _, res = P.damp_cholesky(torch.from_numpy(H).cuda(), damp=0.01, prec="f32")
+    L, _, res = P.damp_cholesky(Hg, damp=0.01, prec="f32")
     torch.cuda.synchronize()
     r = P.read_result(res)
     Hd, _, lam, _ = O.fix_dead_and_damp(H.astype(np.float64), np.zeros((1, n)), 0.01)
