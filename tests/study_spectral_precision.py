@@ -19,11 +19,10 @@ selectable precisions:
   fp32 factor                 the Cholesky factor of the damped H in fp32
   fp32 factor and updates     both, fp64 target
 
-The fp32 factor here is LAPACK's (numpy).  The library's own fp32 factor
-(right-looking, the trailing values rounded to fp32 after every pass) was
-measured about 100 times less accurate on these Hessians (relative
-Frobenius error 2e-6 to 4e-6 at n = 1100 to 4096, against 2.5e-8), so the
-fp32-factor rows are a lower bound for it.
+The fp32 factor is LAPACK's spotrf (through scipy).  numpy's float32
+Cholesky cannot stand in for it: it factors in fp64 and rounds the result
+(bitwise the fp64 factor rounded), about 300 times more accurate than an
+fp32 factor of these Hessians.
 
 For each it prints the share of codes equal to the fp64 sweep's, the
 mismatches that are not within 1e-5 of a rounding tie, and the drift
@@ -35,6 +34,7 @@ import os
 import sys
 
 import numpy as np
+import scipy.linalg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -97,7 +97,9 @@ def main(m=128, n=2048):
     bits = float(np.mean(O.column_entropy_bits(Z64.astype(np.int64))))
     print(f"m={m} n={n} c={c:.4g} mean bits {bits:.3f} max |code| {np.abs(Z64).max():.0f}")
 
-    L32 = np.linalg.cholesky(Hd.astype(np.float32)).astype(np.float64)
+    L32 = scipy.linalg.cholesky(Hd.astype(np.float32), lower=True,
+                                check_finite=False).astype(np.float64)
+    assert L32.dtype == np.float64 and np.all(np.triu(L32, 1) == 0)
     print(f"fp32 factor: relative Frobenius difference {np.linalg.norm(L32 - L) / np.linalg.norm(L):.2e}")
     cases = [("fp32 updates, fp64 target", L, np.float32, np.float64),
              ("fp32 updates and target", L, np.float32, np.float32),
