@@ -113,6 +113,22 @@ __global__ __launch_bounds__(256) void copy_damped(const float* __restrict__ H,
   A[(int64_t)i * n + j] = v;
 }
 
+// In place, for a Hessian already in the working copy (natural order):
+// A[i][i] = H'_ii + lambda as copy_damped forms it, 0 above the diagonal,
+// the lower triangle as it is.  One workgroup per matrix row.
+__global__ __launch_bounds__(256) void damp_in_place(float* __restrict__ A, int n,
+                                                    const double* __restrict__ lam_p,
+                                                    const DevFlags* flags) {
+  if (flags->info != 0) return;
+  const int i = blockIdx.x;
+  float* a = A + (int64_t)i * n;
+  if (threadIdx.x == 0) {
+    const float h = a[i];
+    a[i] = (float)((h == 0.0f ? 1.0 : (double)h) + *lam_p);
+  }
+  for (int j = i + 1 + (int)threadIdx.x; j < n; j += 256) a[j] = 0.0f;
+}
+
 __device__ __forceinline__ float readlane_t(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -977,6 +993,16 @@ hipError_t factor_impl(T* A, int n, T* dbuf, DevFlags* flags, pwq_result* res,
 }
 
 }  // namespace
+
+hipError_t launch_damp_cholesky_in_place(float* A, int64_t n, double damp, int32_t* dead,
+                                         pwq_result* res, DevFlags* flags, double* lam,
+                                         void* dscratch, hipStream_t st) {
+  damp_prep<<<1, 256, 0, st>>>(A, (int)n, damp, dead, res, flags, lam);
+  damp_in_place<<<(unsigned)n, 256, 0, st>>>(A, (int)n, lam, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return factor_impl<float>(A, (int)n, (float*)dscratch, flags, res, st);
+}
 
 hipError_t launch_damp_lambda(const float* H, int64_t n, double damp, int32_t* dead,
                               pwq_result* res, DevFlags* flags, double* lam, hipStream_t st) {

@@ -479,8 +479,13 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
   Carver c(ws);
   carve_layer(c, m, n, ntok, has_x, need_h, need_l, xdtype, xal, block, prec, mp, &w);
   hipStream_t st = (hipStream_t)stream;
-  float* Hm = has_x ? (H_out ? H_out : w.H) : (float*)H;
   void* Lm = L_out ? L_out : w.L;
+  // fp32, natural order, H not asked for: the Hessian is accumulated
+  // straight into the factor's working copy, which is damped and factored
+  // in place (no n x n copy)
+  const bool in_place = has_x && !H_out && prec == PWQ_F32 &&
+                        order_kind == PWQ_ORDER_BACK_TO_FRONT;
+  float* Hm = has_x ? (H_out ? H_out : (in_place ? (float*)Lm : w.H)) : (float*)H;
 
   hipError_t e = launch_init_flags(w.flags, result, 1, st);
   if (e == hipSuccess && has_x) {
@@ -502,7 +507,10 @@ pwq_status pwq_quant_layer(const void* W, int32_t wdtype, int64_t m, int64_t n, 
     e = launch_order(order_kind, Hm, n, perm, w.perm, w.seen, result, w.flags, st);
     colmap = order_kind == PWQ_ORDER_PERM ? perm : w.perm;
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess && in_place)
+    e = launch_damp_cholesky_in_place((float*)Lm, n, damp, w.dead, result, w.flags, w.lam,
+                                      w.dscratch, st);
+  else if (e == hipSuccess)
     e = launch_damp_cholesky(Hm, n, damp, prec, colmap, Lm, w.dead, result, w.flags, w.lam,
                              w.dscratch, st);
   const bool colsp = grid->kind == PWQ_GRID_COLSPACING;

@@ -51,6 +51,11 @@ constexpr size_t kCholScratchBytes = 2 * 64 * 64 * sizeof(double);
 hipError_t launch_damp_cholesky(const float* H, int64_t n, double damp, int32_t prec,
                                 const int32_t* perm, void* L, int32_t* dead, pwq_result* res,
                                 DevFlags* flags, double* lam, void* dscratch, hipStream_t st);
+// The same for fp32 in natural order with H already in the working copy A
+// (both triangles or the lower one; the upper is overwritten with zeros).
+hipError_t launch_damp_cholesky_in_place(float* A, int64_t n, double damp, int32_t* dead,
+                                         pwq_result* res, DevFlags* flags, double* lam,
+                                         void* dscratch, hipStream_t st);
 
 // OA-EM codebook initialisation (all float64).  Workspace: Hb ng g g,
 // R m n, Q ng K, S ng K g doubles, cnt ng K int32, part

@@ -215,6 +215,27 @@ def test_quant_layer(layers, case):
     print(case, stats, flush=True)
 
 
+@pytest.mark.parametrize("case,want_l", [("qproj_small", True), ("downproj_small_ragged", True),
+                                         ("tiny_unaligned", False), ("tiny_ragged_aligned", True)])
+def test_hessian_into_factor_copy(layers, case, want_l):
+    """Without an H output (fp32, natural order) the Hessian is accumulated
+    into the factor's working copy and damped there; codes, steps, factor
+    and result must be bitwise those of the run that keeps H."""
+    cfg, prec, c = CASES[case]
+    lay = layers[case]
+    W, X, _ = upload(lay)
+    kw = dict(grid=_grid(cfg, c), damp=cfg.damp, block=cfg.block, prec=prec)
+    a = P.quant_layer(W, X=X, want_H=True, want_L=want_l, **kw)
+    b = P.quant_layer(W, X=X, want_H=False, want_L=want_l, **kw)
+    torch.cuda.synchronize()
+    assert "H" not in b or b["H"] is None
+    for k in ("codes", "scales", "result") + (("L",) if want_l else ()):
+        assert torch.equal(a[k], b[k]), k
+    if prec == "f32" and cfg.grid_kind == "asym":
+        assert torch.equal(a["zeros"], b["zeros"])
+    assert P.read_result(b["result"])["info"] == 0
+
+
 def test_deterministic(layers):
     lay = layers["qproj_small"]
     a = _run(lay, "f32", None)
