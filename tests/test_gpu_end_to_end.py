@@ -4,7 +4,7 @@ compared with the fp64 oracle run on ITS OWN Hessian 2 X X^T of the same X
 (not on the GPU's H), every row and every column:
 
   * >= 99.9% of codes identical;
-  * every GPU code, judged through the oracle's own fp64 factor and steps,
+  * every GPU code, checked through the oracle's own fp64 factor and steps,
     is a nearest rounding of its running target: |G| <= 1/2 + 1e-5;
   * loss, damped loss and bound within 1e-3 of the oracle's.
 

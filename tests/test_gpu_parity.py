@@ -2,7 +2,7 @@
 the oracle finishes in seconds that still span several tiles, panels and
 blocks plus ragged tails.
 
-Codes are judged stage-fed: the oracle is run on the GPU's own fp32 Hessian
+Codes are checked stage-fed: the oracle is run on the GPU's own fp32 Hessian
 (widened to fp64), so the comparison isolates the factor and the sweep; the
 Hessian itself is compared with the oracle's fp64 Hessian of the same X.
 """
