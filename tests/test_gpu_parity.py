@@ -286,6 +286,14 @@ def test_dead_feature(layers):
     Z = codes - np.repeat(zeros, cfg.group, axis=1)
     assert np.all(Z[:, 37] == 0)
     check_codes(codes, ref, zeros, label="dead")
+    # without an H output the Hessian is damped in the factor's working copy:
+    # the erased input's diagonal is handled the same way, bitwise
+    W, X, _ = upload(lay)
+    b = P.quant_layer(W, X=X, grid=_grid(cfg), damp=cfg.damp, block=cfg.block, prec="f32",
+                      want_L=True)
+    torch.cuda.synchronize()
+    for k in ("codes", "scales", "zeros", "result", "L"):
+        assert torch.equal(out[k], b[k]), k
 
 
 @pytest.mark.parametrize("block", [32, 64, 128, 256])
