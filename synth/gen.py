@@ -93,7 +93,8 @@ def make_activations(cfg: LayerConfig, ss_std: np.random.SeedSequence,
     else:
         chan = np.ones(n)
     if cfg.outliers:
-        idx = ro.choice(n, size=cfg.outliers, replace=False)
+        # (layers narrower than the outlier count: every channel)
+        idx = ro.choice(n, size=min(cfg.outliers, n), replace=False)
         chan[idx] *= cfg.outlier_scale
     chan = chan.reshape(n, 1)
     nchunks = (ntok + CHUNK_TOKENS - 1) // CHUNK_TOKENS

@@ -35,11 +35,13 @@ def lattice_ints(codes, zeros, n):
     return Z
 
 
-def check_codes(codes_gpu, ref, zeros_gpu=None, label=""):
+def check_codes(codes_gpu, ref, zeros_gpu=None, label="", min_identical=MIN_IDENTICAL):
     """Compare GPU codes with an oracle result dict ``ref`` (from
     oracle.quant_layer, or the same keys for a row sample: codes, pi, Sp, W0
     and L).  Returns a dict of statistics; raises AssertionError on
-    failure."""
+    failure.  ``min_identical`` may be lowered for layers of a few hundred
+    codes, where a couple of exact ties already exceed 0.1%; the
+    nearest-rounding check is the same for every layer."""
     codes_gpu = np.asarray(codes_gpu, np.int64)
     ref_codes = ref["codes"]
     same = float(np.mean(codes_gpu == ref_codes))
@@ -55,7 +57,7 @@ def check_codes(codes_gpu, ref, zeros_gpu=None, label=""):
     gmax = float(np.max(np.abs(G))) if G.size else 0.0
     stats = {"identical": same, "max_abs_G": gmax,
              "mismatches": int(np.sum(codes_gpu != ref_codes))}
-    assert same >= MIN_IDENTICAL, f"{label}: only {same:.6f} of codes identical {stats}"
+    assert same >= min_identical, f"{label}: only {same:.6f} of codes identical {stats}"
     assert gmax <= 0.5 + TOL_TIE, f"{label}: a code is not a nearest rounding {stats}"
     return stats
 
