@@ -23,7 +23,8 @@ events around each of their launches in the timed steps, and the Cholesky
 (n^3/3 flop, stage time).  Each carries the published peak and the
 achievable one measured on the device by the peak probe
 (post_weight_quantization_19_amd/peak_probe, dense MFMA from registers and a
-1 GiB copy), run in its own process first.
+1 GiB copy), run in its own process first; the SYRK's line also carries the
+bf16 rate the device sustains over a long launch on random operands.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -71,6 +72,11 @@ def parse():
     ap.add_argument("--cpu-token-fraction", type=int, default=0,
                     help="oracle Hessian is timed on 1/k of the tokens, scaled by k "
                          "(0: the smallest k that keeps the sample near 2e12 flop)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="context for the Hessian's roofline: time the vendor library's "
+                         "bf16 GEMM (torch.mm, hipBLASLt) computing the whole X^T X of the "
+                         "layer's token-major X beside this library's Hessian on the same X, "
+                         "in one process; prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (the reference kernel "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -264,6 +270,74 @@ def stage_roofline(achieved, peak, achievable, unit, bound, work, how):
             "work_per_step": work, "timed_by": how}
 
 
+def library_gemm_bench(args):
+    """The vendor library's bf16 GEMM (torch.mm, which hipBLASLt serves)
+    computing the whole product X^T X (2 n^2 N flop, fp32 output) of the
+    layer's token-major X, and this library's Hessian (n(n+1)N flop, the
+    lower triangle, mirrored) on the same X in the same process, launches
+    alternating.  Context for the Hessian's roofline, not a stage of the
+    quantizer.  Prints one JSON line of its own."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_19_amd as P
+    import synth
+
+    cfg = synth.config(args.config)
+    n, N = cfg.n, cfg.ntok
+    if cfg.ntok == 0 or cfg.xdtype != "bf16":
+        print(f"bench.py --library-gemm: config {args.config} has no bf16 X", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] generating X of {cfg.name} n={n} ntok={N}", file=sys.stderr, flush=True)
+    lay = synth.make_layer(cfg, keep_x_f32=False)
+    dev = torch.device("cuda:0")
+    X = torch.from_numpy(lay.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = X.t().contiguous()              # token-major [N, n]
+    del lay
+    H = torch.empty((n, n), dtype=torch.float32, device=dev)
+    G = torch.empty((n, n), dtype=torch.float32, device=dev)
+
+    def lib_gemm():
+        torch.mm(X.t(), X, out_dtype=torch.float32, out=G)
+
+    def ours():
+        P.hessian_accum(X, H, x_layout="tokens")
+
+    for _ in range(max(1, args.warmup)):
+        lib_gemm()
+        ours()
+    torch.cuda.synchronize()
+    t_lib, t_ours = [], []
+    for _ in range(args.steps):
+        for f, ts in ((lib_gemm, t_lib), (ours, t_ours)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+    # both compute X^T X: the library's fp32 product and half of this
+    # library's H agree to fp32 rounding of differently ordered sums
+    rel = (torch.linalg.norm(2.0 * G - H) / torch.linalg.norm(H)).item()
+    ml, mo = float(np.median(t_lib)), float(np.median(t_ours))
+    fl_lib, fl_ours = 2.0 * n * n * N, float(n) * (n + 1) * N
+    line = {
+        "metric": "bf16 X^T X: vendor-library GEMM against this library's Hessian",
+        "value": ml / mo, "unit": "x (library GEMM time / Hessian time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "library_gemm": {"call": "torch.mm(X.t(), X, out_dtype=torch.float32)",
+                         "ms_median": ml, "ms_min": min(t_lib), "flop": fl_lib,
+                         "tflops": fl_lib / ml / 1e9},
+        "hessian": {"call": "pwq_hessian_accum (token-major X)", "ms_median": mo,
+                    "ms_min": min(t_ours), "flop": fl_ours, "tflops": fl_ours / mo / 1e9},
+        "rel_fro_2G_vs_H": rel,
+        "dtype": "bf16 products, f32 accumulate", "data": "synthetic (seeded)",
+        "config": {"workload": f"{cfg.name}: X {N}x{n} bf16 token-major", "n": n, "ntok": N},
+    }
+    print(json.dumps(line))
+
+
 def ssqr_bench(args):
     """The overflow-tolerant layer (SSQR): one call = the Hessian once, then
     iters + 2 (or 3) quantizations of the bisection of the step multiplier,
@@ -426,6 +500,9 @@ def main():
     if args.oaem and args.gpus == 1:
         oaem_bench(args)
         return
+    if args.library_gemm and args.gpus == 1:
+        library_gemm_bench(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the "
               "quantizer's rows are independent, and a multi-GPU run would shard them "
@@ -585,6 +662,13 @@ def main():
             roofline["achieved"], PEAK_BF16_TFLOPS, pk.get("mfma_bf16_tflops"), "TFLOP/s",
             "mfma", roofline["flops_per_launch"], "library HIP events around each launch")
         roofline["achievable"] = pk.get("mfma_bf16_tflops")
+        # the rate the device holds over a long launch of random-operand bf16
+        # MFMAs (its power limit lowers the clock); the SYRK runs as long
+        sus = pk.get("mfma_bf16_sustained_random_tflops")
+        roofline["achievable_sustained"] = sus
+        roofline["frac_of_sustained"] = (roofline["achieved"] / sus) if sus else None
+        stages["hessian_tiles"]["achievable_sustained"] = sus
+        stages["hessian_tiles"]["frac_of_sustained"] = roofline["frac_of_sustained"]
 
     line = {
         "metric": METRIC,

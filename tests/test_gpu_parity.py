@@ -121,13 +121,14 @@ def test_cholesky_stage(layers, prec, tol):
     assert rel_fro(Lg, Lo) <= tol
 
 
-@pytest.mark.parametrize("n", [8200, 8256, 20544])
+@pytest.mark.parametrize("n", [8198, 8200, 8256, 20544])
 def test_cholesky_large_fp32(n):
     """From n = 8192 the fp32 factor applies four pending panels per pass
     over the trailing triangle, from n = 20480 eight; a ragged last panel
-    (8200), an aligned size (8256) and a size whose last 128-column tile is
-    ragged (20544), against the oracle's fp64 factor of the same float32
-    input."""
+    (8200), rows that are not 16-byte multiples
+    (8198, the trailing tiles go through LDS), an aligned size (8256) and a
+    size whose last 128-column tile is ragged (20544), against the oracle's
+    fp64 factor of the same float32 input."""
     rng = np.random.default_rng(n)
     A = torch.from_numpy(rng.standard_normal((n, n + 512), dtype=np.float32)).cuda()
     Hg = A @ A.T
