@@ -1,6 +1,7 @@
-"""bench.py's refusals that need no GPU: more than one GPU, and the fp32
-tiny layer (a parity-test size, not a timed layer).  Both exit with status
-2 and a message before any device work."""
+"""bench.py's refusals that need no GPU: more than one GPU, the fp32 tiny
+layer (a parity-test size, not a timed layer), and the library-GEMM
+comparison on the layer given by its Hessian (no X).  Each exits with
+status 2 and a message before any device work."""
 import os
 import subprocess
 import sys
@@ -24,4 +25,11 @@ def test_tiny_fp32_layer_is_not_a_bench_line():
     r = _bench("--config", "1")
     assert r.returncode == 2
     assert "parity-test size" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_library_gemm_needs_activations():
+    r = _bench("--config", "5", "--library-gemm")
+    assert r.returncode == 2
+    assert "has no bf16 X" in r.stderr
     assert r.stdout.strip() == ""
