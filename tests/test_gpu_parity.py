@@ -90,6 +90,23 @@ def test_hessian_large_tiles(n, ntok):
     assert rel_fro(to_np(H2), 2 * Hg) <= 1e-6
 
 
+@pytest.mark.parametrize("n,ntok", [(2048, 20480), (8192, 4096)])
+def test_hessian_large_tiles_run_to_run(n, ntok):
+    """The 256x256-tile SYRK sums split tiles in a fixed order with no
+    float atomics, so repeated calls give the same H bit for bit, in both X
+    layouts (the first case splits every tile over the token axis; the
+    second computes whole rounds of tiles over all tokens and splits the
+    remainder, the plan of the large layers)."""
+    cfg = synth.config(2).resized(m=16, n=n, ntok=ntok)
+    lay = synth.make_layer(cfg)
+    _, X, _ = upload(lay)
+    Xt = X.t().contiguous()
+    ref = P.hessian_accum(X)
+    for _ in range(2):
+        assert torch.equal(P.hessian_accum(X), ref)
+        assert torch.equal(P.hessian_accum(Xt, x_layout="tokens"), ref)
+
+
 def test_hessian_accumulate_and_empty(layers):
     lay = layers["qproj_small"]
     _, X, _ = upload(lay)
