@@ -561,12 +561,19 @@ def main():
     # library launches it on.
     timer = P.HessianTileTimer(args.steps if has_x else 0)
     torch.cuda.synchronize()
+    # one HIP event between consecutive steps on the library's stream (events
+    # only: no synchronisation inside the timed region) for the per-step
+    # median and minimum
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with timer:
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        step_ev[0].record()
+        for i in range(args.steps):
             step()
+            step_ev[i + 1].record()
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     roofline = None
     if has_x:
         tiles_ms = timer.durations_ms()
@@ -678,6 +685,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": dt * 1e3,
+        "step_ms": {"median": float(np.median(step_ms)), "min": min(step_ms),
+                    "max": max(step_ms)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
