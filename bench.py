@@ -670,8 +670,9 @@ def main():
             "mfma", roofline["flops_per_launch"], "library HIP events around each launch")
         roofline["achievable"] = pk.get("mfma_bf16_tflops")
         # the rate the device holds over a long launch of random-operand bf16
-        # MFMAs (its power limit lowers the clock); the SYRK runs as long
-        sus = pk.get("mfma_bf16_sustained_random_tflops")
+        # MFMAs of the form the SYRK issues (16x16x32; the power limit lowers
+        # the clock); the SYRK runs as long
+        sus = pk.get("mfma_bf16_16x16x32_sustained_random_tflops")
         roofline["achievable_sustained"] = sus
         roofline["frac_of_sustained"] = (roofline["achieved"] / sus) if sus else None
         stages["hessian_tiles"]["achievable_sustained"] = sus

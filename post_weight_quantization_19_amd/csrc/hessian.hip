@@ -11,9 +11,10 @@
 // Design (gfx950): the product is a symmetric rank-N update, so only the
 // lower-triangular output tiles are computed.  bf16 X on layers of >= 1024
 // channels (16-byte aligned rows) takes syrk_tiles256: 256x256 tiles, X
-// streamed HBM -> LDS by asynchronous copies through a ten-slot ring, MFMA
-// operands read from LDS one stage ahead of the v_mfma_f32_32x32x16_bf16
-// that use them (bf16 products are exact in fp32).  Each XCD owns a
+// streamed HBM -> LDS in 32-token stages by asynchronous copies through a
+// five-slot ring, MFMA operands read from LDS one stage ahead of the
+// v_mfma_f32_16x16x32_bf16 that use them (bf16 products are exact in
+// fp32).  Each XCD owns a
 // contiguous range of tiles; it computes whole rounds of them in one pass
 // over the token axis and splits the remainder over the token axis so its
 // 32 CUs finish together.  fp32 X, small or unaligned layers take
@@ -262,10 +263,16 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
 }
 
 // Large-tile kernel for bf16 X: 256x256 output tiles, 8 waves of 64x128
-// (2x4 v_mfma_f32_32x32x16_bf16 accumulators), two waves per SIMD.
+// (4x8 v_mfma_f32_16x16x32_bf16 accumulators), two waves per SIMD.  A
+// long launch of this kernel runs at the chip's power limit: the clock and
+// the share of cycles the MFMA pipe is busy trade against each other, and
+// the rate follows from the bytes moved per flop, which the 256x256 tile
+// fixes.  The 16x16x32 form (a quarter of the accumulator data per
+// instruction of the 32x32x16 form) and copies addressed from a scalar
+// base (no 64-bit per-lane pointers to spill) come out a little ahead.
 //
-// Stages of 16 tokens (one MFMA K step) stream HBM -> LDS through a ring of
-// NSLOT slots of 16 KB (the A and B panels, 8 KB each; 160 KB in all) with
+// Stages of 32 tokens (one MFMA K step) stream HBM -> LDS through a ring of
+// NSLOT slots of 32 KB (the A and B panels, 16 KB each; 160 KB in all) with
 // AHEAD stages in flight.  The copies are global_load_lds_dwordx4 issued
 // from inline asm: the compiler then does not see an asynchronous LDS
 // writer, so it neither drains the copy queue before LDS reads nor reorders
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
 // The ring is safe because the slot refilled after barrier s + 1 held stage
 // s - 2, which every wave finished reading before it arrived there.
 //
-// Token-major X (TM): a panel stage is 16 token rows of 512 B (256
+// Token-major X (TM): a panel stage is 32 token rows of 512 B (256
 // channels); the MFMA operand (8 consecutive tokens of one channel per
 // lane) comes from two ds_read_b64_tr_b16 (within each 16-lane group, lane i
 // receives element i % 4 of the 8 bytes addressed by lane 4 j + i / 4 as
@@ -284,39 +291,53 @@ __global__ __launch_bounds__(NT) void syrk_tiles(
 // channels f0 + 4 a .. f0 + 4 a + 3 gives lane i tokens t0 .. t0 + 3 of
 // channel f0 + i).  The 16-byte chunks of a token row are XOR-swizzled by
 // 4 (row % 4) so the four rows a group reads fall in distinct banks.
-// Channel-major X: a panel stage is 256 channel rows of 32 B (16 tokens);
-// the operand is one ds_read_b128 of 8 tokens; the two chunks of a row are
-// swapped on rows with bit 3 set, so 16 consecutive rows at one logical
-// chunk cover all banks.  Both layouts feed the same values to the same
-// MFMAs in the same order: H is bitwise the same.
+// Channel-major X: a panel stage is 256 channel rows of 64 B (32 tokens);
+// the operand is one ds_read_b128 of 8 tokens; the four chunks of a row are
+// XOR-swizzled by bits 2-3 of the row, so 16 consecutive rows at one
+// logical chunk cover all banks.  Both layouts feed the same values to the
+// same MFMAs in the same order: H is bitwise the same.
+//
+// A 16x16x32 operand holds row (or column) l % 16 and the 8 tokens
+// 8 (l / 16) .. 8 (l / 16) + 7 of the stage in lane l, for A and B alike,
+// so the instruction sums exactly the stage's 32 token products of each
+// output.  Result layout: lane l, register r -> row 4 (l / 16) + r,
+// column l % 16 of the 16x16 block.
 constexpr int BL = 256;        // tile edge
-constexpr int BKS = 16;        // tokens per stage
+constexpr int BKS = 32;        // tokens per stage
 constexpr int PANEL = BL * BKS * 2;   // bytes of one panel stage
-constexpr int NSLOT = 10;      // LDS ring slots of two panels
-constexpr int AHEAD = 8;       // stages in flight (<= NSLOT - 2)
-constexpr int NWL = 8;         // waves per workgroup
+constexpr int NSLOT = 5;       // LDS ring slots of two panels
+constexpr int AHEAD = 3;       // stages in flight (<= NSLOT - 2)
+constexpr int TRIP = 2 * NSLOT;   // stages per steady-state trip (operand sets alternate)
+constexpr int NWL = 8;         // waves per workgroup, (NWL / 2) x 2 over the tile
 constexpr int NTL = 64 * NWL;  // threads
+constexpr int WR = 2 * BL / NWL;   // rows of a wave's sub-tile (columns: 128)
+constexpr int FA = WR / 16;    // A operand fragments per stage and wave
+constexpr int NFR = FA + 8;    // operand fragments per stage and wave (FA A, 8 B)
+constexpr int NCPY = PANEL / (NTL * 16);   // 16-byte copies per lane and panel stage
 static_assert(NSLOT * 2 * PANEL <= 160 * 1024, "ring fits the LDS");
 static_assert(AHEAD <= NSLOT - 2, "refilled slot is two stages old");
-static_assert(PANEL == NWL * 1024, "one 1 KB copy per wave and panel");
+static_assert(NCPY * NTL * 16 == PANEL, "whole copies per panel stage");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ int tm_swz(int r) { return 4 * (r & 3); }
+__device__ __forceinline__ int cm_swz(int r) { return (r >> 2) & 3; }
 
-// Copy 16 bytes per lane from global memory into LDS at lds + 16 lane
-// (lds wave-uniform).  M0 holds the LDS base for the copy and is restored.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+// Copy 16 bytes per lane from global memory at sbase + voff into LDS at
+// lds + 16 lane: a wave-uniform base in scalar registers plus a 32-bit
+// per-lane byte offset, so no 64-bit per-lane address is kept (lds
+// wave-uniform).  M0 holds the LDS base for the copy and is restored.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
   uint32_t keep;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(keep)
-      : "v"(src), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 
@@ -332,7 +353,7 @@ __device__ __forceinline__ void stage_barrier(int later) {
     default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
 }
-static_assert(AHEAD - 1 <= 7 && 2 * 7 <= 63, "stage_barrier covers every count");
+static_assert(AHEAD - 1 <= 7 && 2 * NCPY * 7 <= 63, "stage_barrier covers every count");
 
 __device__ __forceinline__ bf16x8_t tr_operand(uint32_t a) {
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)a);
@@ -359,104 +380,130 @@ __host__ __device__ __forceinline__ void xcd_tiles(int64_t T, int x, int mode, i
 template <bool TM, bool DIAG>
 __device__ __forceinline__ void syrk256_tile(const uint16_t* __restrict__ X, int n, int64_t ldx,
                                              int r0, int c0, int64_t kbeg, int64_t kend,
-                                             lds_char* Ls, f32x16_t (&acc)[2][4]) {
-  constexpr int P = DIAG ? 1 : 2;           // copies per wave and stage
+                                             lds_char* Ls, f32x4_t (&acc)[FA][8]) {
+  constexpr int NP = DIAG ? 1 : 2;          // panels copied per stage
+  constexpr int P = NCPY * NP;              // copies per wave and stage
   constexpr uint32_t BOFF = DIAG ? 0 : PANEL;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;   // rows 64 wm, columns 128 wn of the tile
+  const int wm = wave >> 1, wn = wave & 1;   // rows WR wm, columns 128 wn of the tile
   // waves entirely above the diagonal of a diagonal tile only copy
-  const bool skip = DIAG && (64 * wm + 63 < 128 * wn);
+  const bool skip = DIAG && (WR * wm + WR - 1 < 128 * wn);
   const int nfull = (int)((kend - kbeg) / BKS);
   const int nstage = (int)((kend - kbeg + BKS - 1) / BKS);
   const uint32_t lbase = (uint32_t)(uintptr_t)Ls;
 
-  // copy sources: lane l of wave w fills LDS unit u = 64 w + l of a panel
+  // copy sources: copy h of lane l of wave w fills LDS unit
+  // u = NTL h + 64 w + l of a panel stage, from a wave-uniform base plus a
+  // per-lane byte offset (below 2^32: the host routes layers whose offsets
+  // would not fit to the 128-tile kernel).  Token-major: copy h covers
+  // token rows (NTL / 32) h + u / 32 with the same swizzle (it depends on
+  // the row mod 4), so one offset per panel and a uniform row step serve
+  // all of them.  Channel-major: rows (NTL / 4) h + u / 4, each clamped
+  // into the matrix.
   const int u = 64 * wave + lane;
-  const uint16_t* ga;
-  const uint16_t* gb;
-  int64_t kstep;
+  constexpr int NPTR = TM ? 1 : NCPY;
+  const uint16_t* ga[1];
+  const uint16_t* gb[1];
+  uint32_t oa_[NPTR], ob_[NPTR];   // byte offsets from the panel bases
+  int64_t kstep, hstep;
   if constexpr (TM) {
     // token row u / 32, physical chunk u % 32 holding logical chunk
     // c = (u % 32) ^ tm_swz(row) of 8 channels; channels past n read
     // channels n - 8 .. n - 1 (only outputs past n, never stored, use them)
     const int t = u >> 5, c = (u & 31) ^ tm_swz(u >> 5);
-    ga = X + (kbeg + t) * ldx + min(r0 + 8 * c, n - 8);
-    gb = X + (kbeg + t) * ldx + min(c0 + 8 * c, n - 8);
+    ga[0] = gb[0] = X + kbeg * ldx;
+    oa_[0] = (uint32_t)(2 * ((int64_t)t * ldx + min(r0 + 8 * c, n - 8)));
+    ob_[0] = (uint32_t)(2 * ((int64_t)t * ldx + min(c0 + 8 * c, n - 8)));
     kstep = (int64_t)BKS * ldx;
+    hstep = (int64_t)(NTL / 32) * ldx;
   } else {
-    // channel row u / 2, physical chunk u % 2 holding logical chunk
-    // (u % 2) ^ bit 3 of the row (8 tokens); rows past n read row n - 1
-    const int r = u >> 1, c = (u & 1) ^ ((r >> 3) & 1);
-    ga = X + (int64_t)min(r0 + r, n - 1) * ldx + kbeg + 8 * c;
-    gb = X + (int64_t)min(c0 + r, n - 1) * ldx + kbeg + 8 * c;
-    kstep = BKS;
-  }
-  auto issue = [&](int stage) {
-    const uint32_t dst = lbase + (uint32_t)(stage % NSLOT) * (2 * PANEL) + 1024u * wave;
-    dma16(ga + stage * kstep, dst);
-    if constexpr (!DIAG) dma16(gb + stage * kstep, dst + PANEL);
-  };
-  // operand addresses within a slot: A fragments t < 2 (rows 64 wm + 32 t),
-  // B fragments t >= 2 (columns 128 wn + 32 (t - 2))
-  uint32_t off[6];
+    // uniform panel bases; per-lane offsets within 256 rows of X
+    ga[0] = X + (int64_t)r0 * ldx + kbeg;
+    gb[0] = X + (int64_t)c0 * ldx + kbeg;
 #pragma unroll
-  for (int t = 0; t < 6; ++t) {
-    const int f0 = t < 2 ? wm * 64 + 32 * t : wn * 128 + 32 * (t - 2);
-    const uint32_t pb = t < 2 ? 0u : BOFF;
+    for (int h = 0; h < NCPY; ++h) {
+      // channel row uh / 4, physical chunk uh % 4 holding logical chunk
+      // (uh % 4) ^ cm_swz(row) (8 tokens); rows past n read row n - 1
+      const int uh = u + NTL * h;
+      const int r = uh >> 2, c = (uh & 3) ^ cm_swz(r);
+      oa_[h] = (uint32_t)(2 * ((min(r0 + r, n - 1) - r0) * ldx + 8 * c));
+      ob_[h] = (uint32_t)(2 * ((min(c0 + r, n - 1) - c0) * ldx + 8 * c));
+    }
+    kstep = BKS;
+    hstep = 0;
+  }
+  auto copy_stage = [&](int64_t ofs, uint32_t dst) {
+#pragma unroll
+    for (int h = 0; h < NCPY; ++h)
+      dma16s(oa_[TM ? 0 : h], ga[0] + ofs + h * hstep, dst + 1024u * NWL * h);
+    if constexpr (!DIAG) {
+#pragma unroll
+      for (int h = 0; h < NCPY; ++h)
+        dma16s(ob_[TM ? 0 : h], gb[0] + ofs + h * hstep, dst + PANEL + 1024u * NWL * h);
+    }
+  };
+  auto issue = [&](int stage) {
+    copy_stage(stage * kstep, lbase + (uint32_t)(stage % NSLOT) * (2 * PANEL) + 1024u * wave);
+  };
+  // operand addresses within a slot: A fragments t < FA (rows WR wm + 16 t),
+  // B fragments t >= FA (columns 128 wn + 16 (t - FA))
+  uint32_t off[NFR];
+#pragma unroll
+  for (int t = 0; t < NFR; ++t) {
+    const int f0 = t < FA ? wm * WR + 16 * t : wn * 128 + 16 * (t - FA);
+    const uint32_t pb = t < FA ? 0u : BOFF;
     if constexpr (TM) {
       const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
-      const int f = f0 + 16 * (g & 1) + 4 * a;
-      off[t] = pb + (uint32_t)((8 * (g >> 1) + j) * 512 + (((f >> 3) ^ tm_swz(j)) << 4) +
-                               2 * (f & 7));
+      const int f = f0 + 4 * a, row = 8 * g + j;
+      off[t] = pb + (uint32_t)(row * 512 + (((f >> 3) ^ tm_swz(row)) << 4) + 2 * (f & 7));
     } else {
-      const int row = f0 + (lane & 31), c = (lane >> 5) ^ ((row >> 3) & 1);
-      off[t] = pb + (uint32_t)(row * 32 + 16 * c);
+      const int row = f0 + (lane & 15), c = (lane >> 4) ^ cm_swz(row);
+      off[t] = pb + (uint32_t)(row * 64 + 16 * c);
     }
   }
-  auto read = [&](int slot, bf16x8_t (&o)[6]) {
-    const uint32_t sb = lbase + (uint32_t)slot * (2 * PANEL);
+  // The slot base is made opaque per read pass: slot offsets past 64 KB do
+  // not fit the LDS instructions' offset field, and the compiler would
+  // otherwise keep a precomputed address per fragment and slot live.
+  auto read = [&](int slot, bf16x8_t (&o)[NFR]) {
+    uint32_t sb = lbase + (uint32_t)slot * (2 * PANEL);
+    asm volatile("" : "+v"(sb));
 #pragma unroll
-    for (int t = 0; t < 6; ++t) {
+    for (int t = 0; t < NFR; ++t) {
       if constexpr (TM)
         o[t] = tr_operand(sb + off[t]);
       else
         o[t] = *(const bf16x8_t*)(Ls + (sb - lbase) + off[t]);
     }
   };
-  auto mfma = [&](const bf16x8_t (&o)[6]) {
+  auto mfma = [&](const bf16x8_t (&o)[NFR]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[i], o[2 + j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < FA; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o[i], o[FA + j], acc[i][j], 0, 0, 0);
   };
-  // Interleave of one stage's work: MFMA, two LDS reads, MFMA, two reads,
-  // ... (6 x), then the last two MFMAs.  Measured against "all reads, then
-  // all MFMAs": the LDS reads and the matrix pipe then run side by side
-  // (about 520 instead of 700 cycles per stage with both waves of a SIMD).
+  // Interleave of one stage's work: one MFMA, one LDS read, ... while the
+  // reads last, then the remaining MFMAs, so the LDS reads and the matrix
+  // pipe run side by side.
   auto interleave = [&]() {
+    constexpr int NRD = TM ? 2 * NFR : NFR;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8 * FA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+      if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
   };
-  // one stage in the steady state, its ring slot K = s % NSLOT known at
-  // compile time (the LDS offsets fold into the instructions): wait for
-  // stage s + 1 and meet, refill the slot of stage s - 2 with stage
-  // s + AHEAD from the running copy sources, read stage s + 1, multiply
-  // stage s
-  const uint16_t* pa = ga + AHEAD * kstep;
-  const uint16_t* pb = gb + AHEAD * kstep;
-  auto step = [&](auto KK, bf16x8_t (&cur)[6], bf16x8_t (&nxt)[6]) {
+  // one stage in the steady state, its ring slot K % NSLOT known at compile
+  // time (the LDS offsets fold into the instructions): wait for stage
+  // s + 1 and meet, refill the slot of stage s - 2 with stage s + AHEAD
+  // from the running copy offset, read stage s + 1, multiply stage s
+  int64_t pofs = AHEAD * kstep;
+  auto step = [&](auto KK, bf16x8_t (&cur)[NFR], bf16x8_t (&nxt)[NFR]) {
     constexpr int K = decltype(KK)::value;
     stage_barrier<P>(AHEAD - 2);
-    const uint32_t dst = lbase + (uint32_t)((K + AHEAD) % NSLOT) * (2 * PANEL) + 1024u * wave;
-    dma16(pa, dst);
-    if constexpr (!DIAG) dma16(pb, dst + PANEL);
-    pa += kstep;
-    pb += kstep;
+    copy_stage(pofs, lbase + (uint32_t)((K + AHEAD) % NSLOT) * (2 * PANEL) + 1024u * wave);
+    pofs += kstep;
     if (!skip) {
       read((K + 1) % NSLOT, nxt);
       mfma(cur);
@@ -464,7 +511,7 @@ __device__ __forceinline__ void syrk256_tile(const uint16_t* __restrict__ X, int
     }
   };
   // the same near the end of the range, where fewer copies are in flight
-  auto step_tail = [&](int s, bf16x8_t (&cur)[6], bf16x8_t (&nxt)[6]) {
+  auto step_tail = [&](int s, bf16x8_t (&cur)[NFR], bf16x8_t (&nxt)[NFR]) {
     if (s + 1 < nfull) {
       stage_barrier<P>(min(nfull, s + AHEAD) - (s + 2));
       if (s + AHEAD < nfull) issue(s + AHEAD);
@@ -475,7 +522,7 @@ __device__ __forceinline__ void syrk256_tile(const uint16_t* __restrict__ X, int
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  bf16x8_t oa[6], ob[6];
+  bf16x8_t oa[NFR], ob[NFR];
   if (nfull > 0) {
     const int first = min(nfull, AHEAD);
     for (int s = 0; s < first; ++s) issue(s);
@@ -483,10 +530,11 @@ __device__ __forceinline__ void syrk256_tile(const uint16_t* __restrict__ X, int
     if (!skip) read(0, oa);
   }
   int s = 0;
-  // steady state: NSLOT stages per trip, every one issuing its copy
-  static_assert(NSLOT % 2 == 0, "operand sets alternate within a trip");
-  for (; s + NSLOT + AHEAD <= nfull; s += NSLOT) {
-    static_for_up<NSLOT>([&](auto KK) {
+  // steady state: TRIP stages per trip (two turns of the ring, so the
+  // operand sets alternate within it), every one issuing its copy
+  static_assert(TRIP % 2 == 0 && TRIP % NSLOT == 0, "trip = whole turns, even length");
+  for (; s + TRIP + AHEAD <= nfull; s += TRIP) {
+    static_for_up<TRIP>([&](auto KK) {
       constexpr int K = decltype(KK)::value;
       if constexpr (K % 2 == 0)
         step(KK, oa, ob);
@@ -506,21 +554,25 @@ __device__ __forceinline__ void syrk256_tile(const uint16_t* __restrict__ X, int
     const uint32_t sl = (uint32_t)(nfull % NSLOT) * (2 * PANEL);
     const int64_t k0 = kbeg + (int64_t)nfull * BKS;
 #pragma unroll
-    for (int pnl = 0; pnl < (DIAG ? 1 : 2); ++pnl) {
+    for (int pnl = 0; pnl < NP; ++pnl) {
       const int base = pnl ? c0 : r0;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if constexpr (TM) {
-        const int t = u >> 5, c = (u & 31) ^ tm_swz(u >> 5);
-        if (k0 + t < kend) v = *(const uint4*)(X + (k0 + t) * ldx + min(base + 8 * c, n - 8));
-      } else {
-        const int r = u >> 1, c = (u & 1) ^ ((r >> 3) & 1);
-        const uint16_t* src = X + (int64_t)min(base + r, n - 1) * ldx + k0 + 8 * c;
-        uint16_t tmp[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmp[e] = (k0 + 8 * c + e < kend) ? src[e] : (uint16_t)0;
-        __builtin_memcpy(&v, tmp, sizeof(v));
+      for (int h = 0; h < NCPY; ++h) {
+        const int uh = u + NTL * h;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if constexpr (TM) {
+          const int t = uh >> 5, c = (uh & 31) ^ tm_swz(uh >> 5);
+          if (k0 + t < kend) v = *(const uint4*)(X + (k0 + t) * ldx + min(base + 8 * c, n - 8));
+        } else {
+          const int r = uh >> 2, c = (uh & 3) ^ cm_swz(r);
+          const uint16_t* src = X + (int64_t)min(base + r, n - 1) * ldx + k0 + 8 * c;
+          uint16_t tmp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tmp[e] = (k0 + 8 * c + e < kend) ? src[e] : (uint16_t)0;
+          __builtin_memcpy(&v, tmp, sizeof(v));
+        }
+        *(uint4*)(Ls + sl + pnl * PANEL + 16 * uh) = v;
       }
-      *(uint4*)(Ls + sl + pnl * PANEL + 16 * u) = v;
     }
     __syncthreads();
     if (!skip) {
@@ -567,13 +619,13 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
   int ti, tj;
   tile_coords(tile, nt, ti, tj);
   const int r0 = ti * BL, c0 = tj * BL;
-  f32x16_t acc[2][4];
+  f32x4_t acc[FA][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
   if (ti == tj)
     syrk256_tile<TM, true>(X, n, ldx, r0, c0, kbeg, kend, Ls, acc);
   else
@@ -581,29 +633,29 @@ __global__ __launch_bounds__(NTL, 1) void syrk_tiles256(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // 32x32 result layout: lane l, register r -> row 8(r/4) + 4(l/32) + r%4, col l%32
+  // 16x16 result layout: lane l, register r -> row 4 (l / 16) + r, col l % 16
   if (pslot >= 0) {
     float* Pt = partial + (int64_t)pslot * (BL * BL);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FA; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int col = wn * 128 + j * 32 + (lane & 31);
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * WR + i * 16 + 4 * (lane >> 4) + r;
+          const int col = wn * 128 + j * 16 + (lane & 15);
           Pt[row * BL + col] = acc[i][j][r];
         }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int gc = c0 + wn * 128 + j * 32 + (lane & 31);
+      for (int r = 0; r < 4; ++r) {
+        const int gr = r0 + wm * WR + i * 16 + 4 * (lane >> 4) + r;
+        const int gc = c0 + wn * 128 + j * 16 + (lane & 15);
         if (gr < n && gc <= gr) {
           float v = 2.0f * acc[i][j][r];
           if (accumulate) v += H[(int64_t)gr * n + gc];
@@ -736,7 +788,12 @@ bool syrk_aligned(const void* X, int64_t n, int64_t ldx, int32_t xdtype) {
   // token-major rows are read in 16-byte pieces of channels, so n must fill
   // whole pieces as well
   const bool tm = (xdtype & kXTokenMajor) != 0;
-  return ((uintptr_t)X % 16 == 0) && ((ldx * es) % 16 == 0) && (!tm || (n * es) % 16 == 0);
+  // the 256-tile kernel addresses its copies by 32-bit byte offsets within
+  // NTL / 32 token rows (token-major) or 256 channel rows (channel-major)
+  // of X; a larger row stride takes the 128-tile kernel
+  const int64_t span = (tm ? NTL / 32 : BL) * ldx * es;
+  return ((uintptr_t)X % 16 == 0) && ((ldx * es) % 16 == 0) && (!tm || (n * es) % 16 == 0) &&
+         span < ((int64_t)1 << 32);
 }
 
 void syrk_plan(int64_t n, int64_t ntok, int32_t xdtype, bool aligned, SyrkPlan* p) {
