@@ -51,6 +51,16 @@ template <typename T> int lazy_panels(int n) {
   if (sizeof(T) == 8) return n <= 4096 ? 1 : (n <= 8192 ? 2 : (n <= 12288 ? 4 : 8));
   return n >= 20480 ? 8 : (n >= 8192 ? 4 : 1);
 }
+// Panels per trailing update at the step with rem columns still to
+// factor.  fp32 below n = 20480: the count follows rem, so the large early
+// passes gather more panels and the chain near the end applies fewer
+// (against the size rule, same process, alternating: n = 4096 1.43 vs
+// 1.47 ms, 8192 4.31 vs 4.47, 14336 14.08 vs 14.27; at 20480 it was 1%
+// slower and at 28672 even, so larger factors keep the size rule).
+template <typename T> int lazy_panels_at(int n, int rem) {
+  if (sizeof(T) == 8 || n >= 20480) return lazy_panels<T>(n);
+  return rem >= 6144 ? 4 : (rem >= 2048 ? 2 : 1);
+}
 
 // lambda = damp * mean(diag H'), H'_kk = 1 where H_kk == 0.  One workgroup;
 // fixed-order fp64 reduction.
@@ -979,8 +989,8 @@ hipError_t factor_impl(T* A, int n, T* dbuf, DevFlags* flags, pwq_result* res,
     const int np = (n - p1 + NB - 1) / NB;
     const int base2 = k0 + 2 * NB;
     const int nt = base2 < n ? (n - base2 + 127) / 128 : 0;
-    // the trailing triangle takes the pending panels lazy_panels<T>(n) at a time
-    const bool trail = nt > 0 && (k0 - kfrom) / NB + 1 >= lazy_panels<T>(n);
+    // the trailing triangle takes the pending panels lazy_panels_at<T> at a time
+    const bool trail = nt > 0 && (k0 - kfrom) / NB + 1 >= lazy_panels_at<T>(n, n - k0);
     const int ntrail = trail ? nt * (nt + 1) / 2 : 0;
     chol_step<T><<<np + ntrail + 1, 256, 0, st>>>(A, n, k0, kfrom, np, ntrail, dbuf, flags,
                                                   res);
