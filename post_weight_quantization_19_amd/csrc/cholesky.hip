@@ -52,13 +52,18 @@ template <typename T> int lazy_panels(int n) {
   return n >= 20480 ? 8 : (n >= 8192 ? 4 : 1);
 }
 // Panels per trailing update at the step with rem columns still to
-// factor.  fp32 below n = 20480: the count follows rem, so the large early
-// passes gather more panels and the chain near the end applies fewer
-// (against the size rule, same process, alternating: n = 4096 1.43 vs
-// 1.47 ms, 8192 4.31 vs 4.47, 14336 14.08 vs 14.27; at 20480 it was 1%
-// slower and at 28672 even, so larger factors keep the size rule).
+// factor.  The count follows rem, so the large early passes gather more
+// panels and the chain near the end applies fewer.  Against the size rule,
+// same process, alternating: fp32 n = 4096 1.43 vs 1.47 ms, 8192 4.31 vs
+// 4.47, 14336 14.08 vs 14.27 (at 20480 it was 1% slower and at 28672 even,
+// so larger fp32 factors keep the size rule); fp64 n = 8192 8.50 vs 8.73,
+// 16384 39.8 vs 40.3, 28672 176.3 vs 176.6 (n <= 4096 keeps one panel).
 template <typename T> int lazy_panels_at(int n, int rem) {
-  if (sizeof(T) == 8 || n >= 20480) return lazy_panels<T>(n);
+  if (sizeof(T) == 8) {
+    if (n <= 4096) return lazy_panels<T>(n);
+    return rem >= 12288 ? 8 : (rem >= 6144 ? 4 : (rem >= 2048 ? 2 : 1));
+  }
+  if (n >= 20480) return lazy_panels<T>(n);
   return rem >= 6144 ? 4 : (rem >= 2048 ? 2 : 1);
 }
 
