@@ -140,9 +140,10 @@ def test_cholesky_stage(layers, prec, tol):
 
 @pytest.mark.parametrize("n", [8198, 8200, 8256, 20544])
 def test_cholesky_large_fp32(n):
-    """From n = 8192 the fp32 factor applies four pending panels per pass
-    over the trailing triangle, from n = 20480 eight; a ragged last panel
-    (8200), rows that are not 16-byte multiples
+    """Below n = 20480 the fp32 factor applies 4, 2 and then 1 pending
+    panel per pass over the trailing triangle as the columns still to
+    factor fall past 6144 and 2048, from n = 20480 eight; a ragged last
+    panel (8200), rows that are not 16-byte multiples
     (8198, the trailing tiles go through LDS), an aligned size (8256) and a
     size whose last 128-column tile is ragged (20544), against the oracle's
     fp64 factor of the same float32 input."""
@@ -163,6 +164,31 @@ def test_cholesky_large_fp32(n):
     Lg = to_np(L)
     assert np.all(np.triu(Lg, 1) == 0)
     assert rel_fro(Lg, Lo) <= TOL_L
+
+
+@pytest.mark.parametrize("n", [6200])
+def test_cholesky_mid_fp64(n):
+    """fp64 factors above n = 4096 apply 8, 4, 2 and then 1 pending panel
+    per trailing pass as the columns still to factor fall past 12288, 6144
+    and 2048; a size that crosses the last two with a ragged last panel,
+    against the oracle's fp64 factor of the same float32 input."""
+    rng = np.random.default_rng(n)
+    A = torch.from_numpy(rng.standard_normal((n, n + 256), dtype=np.float32)).cuda()
+    Hg = A @ A.T
+    del A
+    torch.cuda.synchronize()
+    H = Hg.cpu().numpy()
+    print(f"[cholesky] fp64 n={n}", flush=True)
+    L, _, res = P.damp_cholesky(Hg, damp=0.01, prec="f64")
+    torch.cuda.synchronize()
+    r = P.read_result(res)
+    Hd, _, lam, _ = O.fix_dead_and_damp(H.astype(np.float64), np.zeros((1, n)), 0.01)
+    Lo, info = O.cholesky_lower(Hd)
+    assert info == 0 and r["info"] == 0
+    Lg = to_np(L)
+    assert Lg.dtype == np.float64
+    assert np.all(np.triu(Lg, 1) == 0)
+    assert rel_fro(Lg, Lo) <= 1e-10
 
 
 def test_cholesky_reports_failing_minor():
